@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for the row-normalization workloads.
+
+This module only draws numbers: it holds none of the normalization
+arithmetic, and both the HIP path's tests and the CPU oracle read the bytes
+it produces.
+
+Recipe (per workload): numpy ``Generator(PCG64)`` streams, one child of
+``SeedSequence(seed).spawn(5)`` per tensor, in the fixed order
+[x, residual, dy, gamma, beta].  Each tensor is a binary64 standard-normal
+draw z of its shape, mapped to ``mu + sigma * z`` (or the row-split mixture
+for the cancellation workload), then rounded to the storage type: binary32
+by numpy's round-to-nearest-even cast, bfloat16 by torch's CPU cast of that
+binary32 value (round-to-nearest-even).  bfloat16 arrays are carried as
+uint16 bit patterns, binary32 as float32.
+
+Workloads (sizes and distributions as the normalization pages' benchmark
+shapes and test lists describe them):
+
+  ln_f32_64x1000       LayerNorm fwd+bwd, fp32, N=64, H=1000; x, dy ~ N(0,1),
+                       gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1), eps 1e-5
+  fwd_bf16_8192x1024   LayerNorm and RMSNorm fwd, bf16, N=8192, H=1024;
+                       rows [0, N/2) x ~ N(0,1), rows [N/2, N)
+                       x = 50 + N(0, 0.01); gamma = 1 + N(0, 0.1); no beta;
+                       eps 1e-5
+  fused_bf16_32768x4096  fused add+RMSNorm fwd, bf16, (B=16, T=2048) -> N=32768,
+                       H=4096; x, residual ~ N(0,1); gamma = 1 + N(0, 0.05);
+                       eps 1e-6
+  bwd_bf16_32768x1024, bwd_bf16_16384x2048  (tall-narrow)
+  bwd_bf16_512x16384,  bwd_bf16_2048x16384  (wide)
+                       LayerNorm and RMSNorm fwd+bwd, bf16; x, dy ~ N(0,1),
+                       gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1), eps 1e-5
+"""
+from dataclasses import dataclass
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+ORDER = ("x", "residual", "dy", "gamma", "beta")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    N: int
+    H: int
+    dtype: str                 # "bf16" or "f32"
+    eps: float
+    x: Tuple[float, float]     # (mu, sigma) of x
+    gamma: Tuple[float, float]
+    beta: Optional[Tuple[float, float]]
+    residual: Optional[Tuple[float, float]] = None
+    dy: Optional[Tuple[float, float]] = (0.0, 1.0)
+    half_shifted: Optional[Tuple[float, float]] = None  # rows [N/2, N)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [
+        Workload("ln_f32_64x1000", 1001, 64, 1000, "f32", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        Workload("fwd_bf16_8192x1024", 1002, 8192, 1024, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=None, dy=None,
+                 half_shifted=(50.0, 0.01)),
+        Workload("fused_bf16_32768x4096", 1003, 32768, 4096, "bf16", 1e-6,
+                 x=(0.0, 1.0), gamma=(1.0, 0.05), beta=None,
+                 residual=(0.0, 1.0), dy=None),
+        Workload("bwd_bf16_32768x1024", 1004, 32768, 1024, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        Workload("bwd_bf16_16384x2048", 1004, 16384, 2048, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        Workload("bwd_bf16_512x16384", 1005, 512, 16384, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        Workload("bwd_bf16_2048x16384", 1005, 2048, 16384, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+    ]
+}
+
+
+def to_storage(a64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a binary64 draw to the storage type (see module docstring)."""
+    a32 = np.asarray(a64, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return a32
+    if dtype == "bf16":
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(a32)).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _streams(seed: int):
+    kids = np.random.SeedSequence(seed).spawn(len(ORDER))
+    return {name: np.random.Generator(np.random.PCG64(k))
+            for name, k in zip(ORDER, kids)}
+
+
+def generate(w: Workload, N: Optional[int] = None, H: Optional[int] = None,
+             seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Storage-typed arrays for workload ``w`` (optionally at another shape
+    or seed, same distributions).  Keys present: x, gamma, and whichever of
+    residual, dy, beta the workload has."""
+    N = w.N if N is None else N
+    H = w.H if H is None else H
+    rng = _streams(w.seed if seed is None else seed)
+    out = {}
+    z = rng["x"].standard_normal((N, H))
+    xv = w.x[0] + w.x[1] * z
+    if w.half_shifted is not None:
+        lo = N // 2
+        xv[lo:] = w.half_shifted[0] + w.half_shifted[1] * z[lo:]
+    out["x"] = to_storage(xv, w.dtype)
+    if w.residual is not None:
+        mu, sd = w.residual
+        out["residual"] = to_storage(
+            mu + sd * rng["residual"].standard_normal((N, H)), w.dtype)
+    if w.dy is not None:
+        mu, sd = w.dy
+        out["dy"] = to_storage(mu + sd * rng["dy"].standard_normal((N, H)),
+                               w.dtype)
+    mu, sd = w.gamma
+    out["gamma"] = to_storage(mu + sd * rng["gamma"].standard_normal(H),
+                              w.dtype)
+    if w.beta is not None:
+        mu, sd = w.beta
+        out["beta"] = to_storage(mu + sd * rng["beta"].standard_normal(H),
+                                 w.dtype)
+    return out
+
+
+def custom(seed: int, N: int, H: int, dtype: str, x=(0.0, 1.0),
+           gamma=(1.0, 0.1), beta=(0.0, 0.1), residual=(0.0, 1.0),
+           dy=(0.0, 1.0), half_shifted=None) -> Dict[str, np.ndarray]:
+    """Arrays for an ad-hoc shape (edge cases, ragged tails)."""
+    w = Workload("custom", seed, N, H, dtype, 1e-5, x=x, gamma=gamma,
+                 beta=beta, residual=residual, dy=dy,
+                 half_shifted=half_shifted)
+    return generate(w)
