@@ -1,0 +1,166 @@
+/*
+ * rownorm.h - row-wise LayerNorm / RMSNorm / fused residual-add + RMSNorm,
+ * forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI of librownorm.so.  Every tensor argument is a DEVICE pointer
+ * owned by the caller; the library allocates nothing, keeps no buffers, and
+ * never synchronizes.  Every compute entry point only validates its
+ * arguments and enqueues kernels on `stream` (0 = the null stream of the
+ * current device), then returns.  The current HIP device must be the device
+ * that owns the pointers and the stream.
+ *
+ * Shapes.  A tensor argument "[N, H]" is N rows of H elements, row-major,
+ * with a row stride ld (in ELEMENTS, ld >= H) and contiguous elements within
+ * a row.  Normalization is over the last dimension (the H elements of one
+ * row); rows are independent.  Callers with (B, T, H) inputs pass N = B*T.
+ * gamma, beta, dgamma, dbeta are vectors of H elements shared by all rows
+ * (no row offset is ever applied to them).
+ *
+ * Types.  One `dtype` (rn_dtype) covers every activation and parameter
+ * tensor of a call: x, residual, h, y, dy, dx, gamma, beta, dgamma, dbeta.
+ * mean and rstd are always float32 vectors of N elements.  All arithmetic
+ * runs in float32 after the load; results are rounded to `dtype` (round to
+ * nearest even) at the store.
+ *
+ * eps.  Added INSIDE the square root: rstd = 1 / sqrt(var + eps).  It must be
+ * finite and > 0.
+ *
+ * Status.  Every function returns RN_OK (0) or a negative RN_E* code.  All
+ * argument checks run before anything is enqueued: a non-zero return means
+ * nothing was launched.  RN_EHIP means a HIP call failed after the checks
+ * (e.g. the launch itself); rn_status_str() names every code.
+ *
+ * Pages these operations follow (cited by title and section):
+ *  "Write Triton Layernorm Kernel": Required reasoning process (row per
+ *      program, mean over H, variance, rstd with eps inside the root,
+ *      affine, saved mean/rstd); Kernel design rules; Correctness
+ *      requirements.
+ *  "Write Cuda Layernorm Kernel": Required reasoning process (two-pass and
+ *      Welford statistics, the parallel merge, RMSNorm, the backward
+ *      formulas); Kernel design rules.
+ *  "Write Triton Fused Add Rmsnorm Kernel": Required reasoning process
+ *      (fp32 add, write-back of h in the same pass, RMSNorm of h, in-place
+ *      aliasing rules); Correctness requirements.
+ *  "Rewrite Triton normalization backward kernel_1 (#499)": Summary
+ *      (per-row grad_input, parameter gradients through a bounded set of
+ *      fp32 partial rows reduced by a second kernel, program count a small
+ *      multiple of the compute-unit count).
+ */
+#ifndef ROWNORM_H
+#define ROWNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RN_F32 = 0, RN_BF16 = 1 } rn_dtype;
+
+enum {
+    RN_OK = 0,
+    RN_EINVAL = -1,        /* bad size, stride, eps, NULL or misaligned ptr */
+    RN_EDTYPE = -2,        /* unknown dtype                                 */
+    RN_EOVERLAP = -3,      /* an output overlaps an input or another output */
+    RN_EWORKSPACE = -4,    /* backward workspace missing or too small       */
+    RN_EHIP = -5,          /* a HIP runtime call failed                     */
+    RN_EUNSUPPORTED = -6   /* H above the largest row this build supports   */
+};
+
+/* LayerNorm forward ("Write Triton Layernorm Kernel", Required reasoning
+ * process, steps 1-10; "Write Cuda Layernorm Kernel", steps 2, 5, 6, 7).
+ * Per row:  mean = sum(x)/H,  var = sum((x - mean)^2)/H,
+ *           rstd = 1/sqrt(var + eps),
+ *           y = (x - mean) * rstd * gamma + beta.
+ *   x     [N, H] in, row stride ldx          gamma [H] in
+ *   beta  [H] in, or NULL for no bias        y     [N, H] out, stride ldy
+ *   mean, rstd  [N] float32 out, each may be NULL (not written)
+ * y may not overlap any input; mean/rstd may not overlap anything. */
+int ln_fwd(const void *x, int64_t ldx, const void *gamma, const void *beta,
+           void *y, int64_t ldy, float *mean, float *rstd,
+           int64_t N, int64_t H, int dtype, float eps, hipStream_t stream);
+
+/* RMSNorm forward ("Write Cuda Layernorm Kernel", Required reasoning
+ * process, step 5 and Kernel design rules).  No mean subtraction, no bias:
+ *   rstd = 1/sqrt(sum(x^2)/H + eps),  y = x * rstd * gamma.
+ *   x [N, H] in; gamma [H] in; y [N, H] out; rstd [N] float32 out or NULL. */
+int rms_fwd(const void *x, int64_t ldx, const void *gamma, void *y,
+            int64_t ldy, float *rstd, int64_t N, int64_t H, int dtype,
+            float eps, hipStream_t stream);
+
+/* Fused residual add + RMSNorm forward ("Write Triton Fused Add Rmsnorm
+ * Kernel", Required reasoning process, steps 1-9):
+ *   h = x + residual (in float32), stored rounded to dtype in the same pass;
+ *   y = h * rstd * gamma with rstd = 1/sqrt(sum(h^2)/H + eps), computed from
+ *   the UNROUNDED float32 h.
+ *   x, residual [N, H] in (strides ldx, ldr); gamma [H] in;
+ *   y [N, H] out (ldy); h [N, H] out (ldh); rstd [N] float32 out or NULL.
+ * In-place residual update is allowed: h may be EXACTLY x (same pointer and
+ * ldh == ldx) or exactly residual; each element is read before it is
+ * written.  Any other overlap is RN_EOVERLAP. */
+int fused_add_rms_fwd(const void *x, int64_t ldx, const void *residual,
+                      int64_t ldr, const void *gamma, void *y, int64_t ldy,
+                      void *h, int64_t ldh, float *rstd, int64_t N, int64_t H,
+                      int dtype, float eps, hipStream_t stream);
+
+/* LayerNorm backward ("Write Cuda Layernorm Kernel", Required reasoning
+ * process, step 8; "Rewrite Triton normalization backward kernel_1 (#499)",
+ * Summary).  With x_hat = (x - mean) * rstd and g = dy * gamma, per row:
+ *   c1 = sum(g)/H,  c2 = sum(g * x_hat)/H,
+ *   dx = rstd * (g - c1 - x_hat * c2);
+ * and over all rows: dgamma = sum(dy * x_hat), dbeta = sum(dy).
+ *   dy, x  [N, H] in;  gamma [H] in;
+ *   mean, rstd [N] float32 in: the statistics saved by ln_fwd (required;
+ *     eps is already inside rstd, so `eps` is only validated);
+ *   dx [N, H] out;  dgamma, dbeta [H] out (required);
+ *   workspace: device scratch of at least rn_bwd_workspace_bytes(N, H,
+ *     dtype, 1) bytes, 256-byte aligned, owned by the caller; it holds the
+ *     float32 partial rows between the two kernels and must not be touched
+ *     until the call's work on `stream` is done.  NULL is fine when that size
+ *     is 0.
+ * The partial-row count is fixed by (N, H, dtype, device), so results are
+ * bitwise reproducible run to run.  N = 0 writes dgamma = dbeta = 0. */
+int ln_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
+           const void *gamma, const float *mean, const float *rstd, void *dx,
+           int64_t lddx, void *dgamma, void *dbeta, void *workspace,
+           size_t workspace_bytes, int64_t N, int64_t H, int dtype, float eps,
+           hipStream_t stream);
+
+/* RMSNorm backward.  The pages ask for it but print no formula; it is the
+ * derivative of rms_fwd: with x_hat = x * rstd and g = dy * gamma,
+ *   c2 = sum(g * x_hat)/H,   dx = rstd * (g - x_hat * c2),
+ *   dgamma = sum over rows of dy * x_hat.
+ * Arguments as in ln_bwd (no mean, no dbeta). */
+int rms_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
+            const void *gamma, const float *rstd, void *dx, int64_t lddx,
+            void *dgamma, void *workspace, size_t workspace_bytes, int64_t N,
+            int64_t H, int dtype, float eps, hipStream_t stream);
+
+/* Bytes of backward workspace needed on the CURRENT device for (N, H,
+ * dtype, LayerNorm or RMSNorm).  It grows with H and the device's
+ * compute-unit count, and with N only up to a small multiple of the CU
+ * count.  Returns RN_OK and sets *bytes, or an error code. */
+int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype, int is_layernorm,
+                           size_t *bytes);
+
+/* Largest H supported for `dtype` (rows are held in registers): for rows
+ * whose size, stride or base address is not a multiple of 16 bytes a
+ * narrower element-wise path runs, with a lower limit, given by
+ * `vectorizable` = 0. */
+int64_t rn_max_hidden(int dtype, int vectorizable);
+
+const char *rn_status_str(int status);
+
+/* Benchmark helper, not part of the normalization: copies `bytes` bytes
+ * between two device buffers with 16-byte loads/stores (used as the
+ * streaming-copy ceiling, as a cache flush, and as the known-size kernel
+ * that calibrates hardware byte counters).  Buffers must not overlap. */
+int rn_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWNORM_H */

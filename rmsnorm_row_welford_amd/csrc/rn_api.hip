@@ -1,0 +1,336 @@
+// C-ABI entry points of librownorm.so: argument validation, overlap checks,
+// plan inputs (vectorizability, CU count) and kernel launches.  All checks
+// run before anything is enqueued.
+#include <math.h>
+#include <mutex>
+#include <stdint.h>
+
+#include "../../include/rownorm.h"
+#include "rn_internal.h"
+
+using namespace rn;
+
+namespace {
+
+// ------------------------------------------------------- device properties --
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+
+// Compute-unit count of the current device, cached per device.
+int current_cus(int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return RN_EHIP;
+    std::call_once(g_once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount,
+                                  dev) != hipSuccess)
+            n = 0;
+        g_cus[dev] = n;
+    });
+    if (g_cus[dev] <= 0) return RN_EHIP;
+    *cus = g_cus[dev];
+    return RN_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == RN_F32 ? 4 : 2; }
+
+bool dtype_ok(int dtype) { return dtype == RN_F32 || dtype == RN_BF16; }
+
+// Byte range [lo, hi) touched by an [N, H] tensor with row stride ld.
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+    bool empty() const { return hi <= lo; }
+};
+
+Span span2d(const void *p, int64_t N, int64_t H, int64_t ld, size_t e) {
+    Span s;
+    if (!p || N <= 0 || H <= 0) return s;
+    s.lo = (uintptr_t)p;
+    s.hi = s.lo + (size_t)((N - 1) * ld + H) * e;
+    return s;
+}
+Span span1d(const void *p, int64_t n, size_t e) { return span2d(p, 1, n, n, e); }
+
+bool overlaps(const Span &a, const Span &b) {
+    if (a.empty() || b.empty()) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Sizes: H in [1, max], N >= 0, strides >= H, and the addressed extent must
+// stay far from int64 overflow.
+int check_shape(int64_t N, int64_t H) {
+    if (N < 0 || H <= 0) return RN_EINVAL;
+    if (H > kMaxHidden) return RN_EUNSUPPORTED;
+    return RN_OK;
+}
+int check_ld(int64_t ld, int64_t N, int64_t H) {
+    if (ld < H) return RN_EINVAL;
+    // (N-1)*ld + H elements must fit comfortably in 2^60 bytes
+    if (N > 0 && ld > ((int64_t)1 << 58) / (N > 0 ? N : 1)) return RN_EINVAL;
+    return RN_OK;
+}
+int check_eps(float eps) {
+    if (!(eps > 0.0f) || !isfinite(eps)) return RN_EINVAL;
+    return RN_OK;
+}
+
+// The 16-byte vector path needs H, every row stride and every row/vector
+// base address to be multiples of 16 bytes.
+struct VecCheck {
+    size_t e;
+    int64_t H;
+    bool ok;
+    VecCheck(size_t e_, int64_t H_) : e(e_), H(H_), ok((H_ * (int64_t)e_) % 16 == 0) {}
+    void ptr(const void *p) { if (p && !aligned(p, 16)) ok = false; }
+    void ld(int64_t l) { if ((l * (int64_t)e) % 16 != 0) ok = false; }
+};
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RN_OK : RN_EHIP; }
+
+}  // namespace
+
+#define RN_TRY(expr)                 \
+    do {                             \
+        int rn_st_ = (expr);         \
+        if (rn_st_ != RN_OK) return rn_st_; \
+    } while (0)
+
+// ------------------------------------------------------------------ forward --
+static int fwd_common(int op, const void *x, int64_t ldx, const void *res,
+                      int64_t ldr, const void *gamma, const void *beta, void *y,
+                      int64_t ldy, void *h, int64_t ldh, float *mean,
+                      float *rstd, int64_t N, int64_t H, int dtype, float eps,
+                      hipStream_t stream) {
+    if (!dtype_ok(dtype)) return RN_EDTYPE;
+    RN_TRY(check_shape(N, H));
+    RN_TRY(check_eps(eps));
+    const size_t e = elem_size(dtype);
+    // Row tensors may be NULL only when there are no rows.
+    if (!gamma || (N > 0 && (!x || !y))) return RN_EINVAL;
+    if (op == OP_FUSED && N > 0 && (!res || !h)) return RN_EINVAL;
+    RN_TRY(check_ld(ldx, N, H));
+    RN_TRY(check_ld(ldy, N, H));
+    if (op == OP_FUSED) {
+        RN_TRY(check_ld(ldr, N, H));
+        RN_TRY(check_ld(ldh, N, H));
+    }
+    const void *ptrs[] = {x, res, gamma, beta, y, h};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, e)) return RN_EINVAL;
+    if ((mean && !aligned(mean, 4)) || (rstd && !aligned(rstd, 4)))
+        return RN_EINVAL;
+
+    // Overlaps.  Inputs: x, res, gamma, beta.  Outputs: y, h, mean, rstd.
+    // h may be exactly x or exactly res (in-place residual update).
+    const Span sx = span2d(x, N, H, ldx, e), sr = span2d(res, N, H, ldr, e);
+    const Span sg = span1d(gamma, H, e), sb = span1d(beta, H, e);
+    const Span sy = span2d(y, N, H, ldy, e), sh = span2d(h, N, H, ldh, e);
+    const Span sm = span1d(mean, N, 4), ss = span1d(rstd, N, 4);
+    const Span ins[] = {sx, sr, sg, sb};
+    const Span outs[] = {sy, sh, sm, ss};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j) {
+            if (i == 1 && ((j == 0 && h == x && ldh == ldx) ||
+                           (j == 1 && h == res && ldh == ldr)))
+                continue;   // the documented in-place forms
+            if (overlaps(outs[i], ins[j])) return RN_EOVERLAP;
+        }
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return RN_EOVERLAP;
+    }
+    if (op == OP_FUSED && h == x && h == res) return RN_EOVERLAP;
+
+    VecCheck vc(e, H);
+    for (const void *p : ptrs) vc.ptr(p);
+    vc.ld(ldx);
+    vc.ld(ldy);
+    if (op == OP_FUSED) {
+        vc.ld(ldr);
+        vc.ld(ldh);
+    }
+    if (!vc.ok && H > kMaxHiddenScalar) return RN_EUNSUPPORTED;
+
+    if (N == 0) return RN_OK;
+    int cus = 0;
+    RN_TRY(current_cus(&cus));
+
+    FwdArgs a{};
+    a.x = x; a.res = res; a.gamma = gamma; a.beta = beta;
+    a.y = y; a.h = h; a.mean = mean; a.rstd = rstd;
+    a.ldx = ldx; a.ldr = ldr; a.ldy = ldy; a.ldh = ldh;
+    a.N = N; a.H = (int)H; a.eps = eps; a.inv_H = 1.0f / (float)H;
+    hipError_t err = dtype == RN_F32 ? launch_fwd_f32(op, a, vc.ok, cus, stream)
+                                     : launch_fwd_bf16(op, a, vc.ok, cus, stream);
+    return hip_status(err);
+}
+
+extern "C" int ln_fwd(const void *x, int64_t ldx, const void *gamma,
+                      const void *beta, void *y, int64_t ldy, float *mean,
+                      float *rstd, int64_t N, int64_t H, int dtype, float eps,
+                      hipStream_t stream) {
+    return fwd_common(OP_LN, x, ldx, nullptr, 0, gamma, beta, y, ldy, nullptr,
+                      0, mean, rstd, N, H, dtype, eps, stream);
+}
+
+extern "C" int rms_fwd(const void *x, int64_t ldx, const void *gamma, void *y,
+                       int64_t ldy, float *rstd, int64_t N, int64_t H,
+                       int dtype, float eps, hipStream_t stream) {
+    return fwd_common(OP_RMS, x, ldx, nullptr, 0, gamma, nullptr, y, ldy,
+                      nullptr, 0, nullptr, rstd, N, H, dtype, eps, stream);
+}
+
+extern "C" int fused_add_rms_fwd(const void *x, int64_t ldx,
+                                 const void *residual, int64_t ldr,
+                                 const void *gamma, void *y, int64_t ldy,
+                                 void *h, int64_t ldh, float *rstd, int64_t N,
+                                 int64_t H, int dtype, float eps,
+                                 hipStream_t stream) {
+    return fwd_common(OP_FUSED, x, ldx, residual, ldr, gamma, nullptr, y, ldy,
+                      h, ldh, nullptr, rstd, N, H, dtype, eps, stream);
+}
+
+// ----------------------------------------------------------------- backward --
+static bool bwd_vec_ok(size_t e, int64_t H, const void *const *ptrs, int np,
+                       const int64_t *lds, int nl) {
+    VecCheck vc(e, H);
+    for (int i = 0; i < np; ++i) vc.ptr(ptrs[i]);
+    for (int i = 0; i < nl; ++i) vc.ld(lds[i]);
+    return vc.ok;
+}
+
+static int partial_rows(int dtype, int64_t N, int64_t H, bool vec, int cus) {
+    return dtype == RN_F32 ? bwd_partials_f32(N, (int)H, vec, cus)
+                           : bwd_partials_bf16(N, (int)H, vec, cus);
+}
+
+extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
+                                      int is_layernorm, size_t *bytes) {
+    if (!bytes) return RN_EINVAL;
+    if (!dtype_ok(dtype)) return RN_EDTYPE;
+    RN_TRY(check_shape(N, H));
+    if (N == 0) {
+        *bytes = 0;
+        return RN_OK;
+    }
+    int cus = 0;
+    RN_TRY(current_cus(&cus));
+    // The vector and element-wise plans may differ; size for the larger.
+    int P = partial_rows(dtype, N, H, true, cus);
+    const int P2 = partial_rows(dtype, N, H, false, cus);
+    if (P2 > P) P = P2;
+    if (P < 0) return RN_EUNSUPPORTED;
+    *bytes = (size_t)P * (size_t)H * sizeof(float) * (is_layernorm ? 2 : 1);
+    return RN_OK;
+}
+
+static int bwd_common(bool ln, const void *dy, int64_t lddy, const void *x,
+                      int64_t ldx, const void *gamma, const float *mean,
+                      const float *rstd, void *dx, int64_t lddx, void *dgamma,
+                      void *dbeta, void *workspace, size_t workspace_bytes,
+                      int64_t N, int64_t H, int dtype, float eps,
+                      hipStream_t stream) {
+    if (!dtype_ok(dtype)) return RN_EDTYPE;
+    RN_TRY(check_shape(N, H));
+    RN_TRY(check_eps(eps));
+    const size_t e = elem_size(dtype);
+    // Row tensors and saved statistics may be NULL only when there are no
+    // rows; the parameter gradients are always written.
+    if (!gamma || !dgamma || (ln && !dbeta)) return RN_EINVAL;
+    if (N > 0 && (!dy || !x || !rstd || !dx || (ln && !mean))) return RN_EINVAL;
+    RN_TRY(check_ld(lddy, N, H));
+    RN_TRY(check_ld(ldx, N, H));
+    RN_TRY(check_ld(lddx, N, H));
+    const void *ptrs[] = {dy, x, gamma, dx, dgamma, ln ? dbeta : nullptr};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, e)) return RN_EINVAL;
+    if (!aligned(rstd, 4) || (mean && !aligned(mean, 4))) return RN_EINVAL;
+    if (workspace && !aligned(workspace, 256)) return RN_EINVAL;
+
+    const Span sdy = span2d(dy, N, H, lddy, e), sx = span2d(x, N, H, ldx, e);
+    const Span sg = span1d(gamma, H, e);
+    const Span sm = span1d(ln ? mean : nullptr, N, 4), ss = span1d(rstd, N, 4);
+    const Span sdx = span2d(dx, N, H, lddx, e);
+    const Span sdg = span1d(dgamma, H, e), sdb = span1d(ln ? dbeta : nullptr, H, e);
+    const Span sw = span1d(workspace, (int64_t)workspace_bytes, 1);
+    const Span ins[] = {sdy, sx, sg, sm, ss};
+    const Span outs[] = {sdx, sdg, sdb, sw};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span &in : ins)
+            if (overlaps(outs[i], in)) return RN_EOVERLAP;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return RN_EOVERLAP;
+    }
+
+    const int64_t lds[] = {lddy, ldx, lddx};
+    const bool vec = bwd_vec_ok(e, H, ptrs, 6, lds, 3);
+    if (!vec && H > kMaxHiddenScalar) return RN_EUNSUPPORTED;
+    int cus = 0;
+    RN_TRY(current_cus(&cus));
+    const int P = N == 0 ? 0 : partial_rows(dtype, N, H, vec, cus);
+    if (P < 0) return RN_EUNSUPPORTED;
+    const size_t need = (size_t)P * (size_t)H * sizeof(float) * (ln ? 2 : 1);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return RN_EWORKSPACE;
+
+    BwdArgs a{};
+    a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd;
+    a.dx = dx; a.part = (float *)workspace;
+    a.lddy = lddy; a.ldx = ldx; a.lddx = lddx;
+    a.N = N; a.H = (int)H; a.inv_H = 1.0f / (float)H;
+    hipError_t err =
+        dtype == RN_F32
+            ? launch_bwd_f32(ln, a, vec, cus, P, dgamma, dbeta, stream)
+            : launch_bwd_bf16(ln, a, vec, cus, P, dgamma, dbeta, stream);
+    return hip_status(err);
+}
+
+extern "C" int ln_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
+                      const void *gamma, const float *mean, const float *rstd,
+                      void *dx, int64_t lddx, void *dgamma, void *dbeta,
+                      void *workspace, size_t workspace_bytes, int64_t N,
+                      int64_t H, int dtype, float eps, hipStream_t stream) {
+    return bwd_common(true, dy, lddy, x, ldx, gamma, mean, rstd, dx, lddx,
+                      dgamma, dbeta, workspace, workspace_bytes, N, H, dtype,
+                      eps, stream);
+}
+
+extern "C" int rms_bwd(const void *dy, int64_t lddy, const void *x,
+                       int64_t ldx, const void *gamma, const float *rstd,
+                       void *dx, int64_t lddx, void *dgamma, void *workspace,
+                       size_t workspace_bytes, int64_t N, int64_t H, int dtype,
+                       float eps, hipStream_t stream) {
+    return bwd_common(false, dy, lddy, x, ldx, gamma, nullptr, rstd, dx, lddx,
+                      dgamma, nullptr, workspace, workspace_bytes, N, H, dtype,
+                      eps, stream);
+}
+
+// ------------------------------------------------------------------- misc --
+extern "C" int64_t rn_max_hidden(int dtype, int vectorizable) {
+    if (!dtype_ok(dtype)) return 0;
+    return vectorizable ? kMaxHidden : kMaxHiddenScalar;
+}
+
+extern "C" const char *rn_status_str(int status) {
+    switch (status) {
+    case RN_OK: return "ok";
+    case RN_EINVAL: return "invalid argument (size, stride, eps, NULL or misaligned pointer)";
+    case RN_EDTYPE: return "unknown dtype";
+    case RN_EOVERLAP: return "an output overlaps an input or another output";
+    case RN_EWORKSPACE: return "backward workspace missing or too small";
+    case RN_EHIP: return "HIP runtime error";
+    case RN_EUNSUPPORTED: return "row length above the supported maximum";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int rn_copy(const void *src, void *dst, size_t bytes,
+                       hipStream_t stream) {
+    if (bytes == 0) return RN_OK;
+    if (!src || !dst) return RN_EINVAL;
+    const Span a = span1d(src, (int64_t)bytes, 1), b = span1d(dst, (int64_t)bytes, 1);
+    if (overlaps(a, b)) return RN_EOVERLAP;
+    return hip_status(launch_copy(src, dst, bytes, stream));
+}

@@ -1,0 +1,198 @@
+// Device primitives for the gfx950 row-normalization kernels: vector
+// load/store of row chunks with float32 conversion, bfloat16 rounding, and
+// wave64 reductions built from DPP row permutations and ds_swizzle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rn {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 values travel as their 16-bit patterns.
+typedef uint16_t bf16_bits;
+
+// Elements per 16-byte chunk.
+template <class T> struct Vec16;
+template <> struct Vec16<float> { static constexpr int N = 4; };
+template <> struct Vec16<bf16_bits> { static constexpr int N = 8; };
+
+// ------------------------------------------------------------------ codec --
+__device__ __forceinline__ float bf16_lo(unsigned u) {
+    return __uint_as_float(u << 16);
+}
+__device__ __forceinline__ float bf16_hi(unsigned u) {
+    return __uint_as_float(u & 0xffff0000u);
+}
+// Two float32 -> two bfloat16 (round to nearest even, NaN stays NaN) in one
+// v_cvt_pk_bf16_f32; `a` lands in the low half.
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16_bits to_bf16(float a) {
+    return __builtin_bit_cast(bf16_bits, (__bf16)a);
+}
+
+// ------------------------------------------------------------ chunk I/O --
+// Load VEC consecutive elements at p (aligned to VEC elements) as float32.
+// NT selects the non-temporal hint for data read exactly once.
+template <int VEC, bool NT>
+__device__ __forceinline__ void load_chunk(const float *p, float *o) {
+    if constexpr (VEC == 4) {
+        f32x4 v = NT ? __builtin_nontemporal_load((const f32x4 *)p)
+                     : *(const f32x4 *)p;
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else {
+        static_assert(VEC == 1, "fp32 chunks are 4 or 1 elements");
+        o[0] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
+}
+template <int VEC, bool NT>
+__device__ __forceinline__ void load_chunk(const bf16_bits *p, float *o) {
+    if constexpr (VEC == 8) {
+        u32x4 v = NT ? __builtin_nontemporal_load((const u32x4 *)p)
+                     : *(const u32x4 *)p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[2 * k] = bf16_lo(v[k]);
+            o[2 * k + 1] = bf16_hi(v[k]);
+        }
+    } else {
+        static_assert(VEC == 1, "bf16 chunks are 8 or 1 elements");
+        unsigned u = NT ? __builtin_nontemporal_load(p) : *p;
+        o[0] = __uint_as_float(u << 16);
+    }
+}
+
+template <int VEC, bool NT>
+__device__ __forceinline__ void store_chunk(float *p, const float *v) {
+    if constexpr (VEC == 4) {
+        f32x4 w = {v[0], v[1], v[2], v[3]};
+        if (NT) __builtin_nontemporal_store(w, (f32x4 *)p);
+        else *(f32x4 *)p = w;
+    } else {
+        static_assert(VEC == 1, "fp32 chunks are 4 or 1 elements");
+        if (NT) __builtin_nontemporal_store(v[0], p);
+        else *p = v[0];
+    }
+}
+template <int VEC, bool NT>
+__device__ __forceinline__ void store_chunk(bf16_bits *p, const float *v) {
+    if constexpr (VEC == 8) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+        if (NT) __builtin_nontemporal_store(w, (u32x4 *)p);
+        else *(u32x4 *)p = w;
+    } else {
+        static_assert(VEC == 1, "bf16 chunks are 8 or 1 elements");
+        bf16_bits b = to_bf16(v[0]);
+        if (NT) __builtin_nontemporal_store(b, p);
+        else *p = b;
+    }
+}
+
+// One chunk kept in its storage form (bfloat16 stays packed two per
+// register) and widened to float32 on use; used for gamma/beta, which are
+// held in registers for a whole persistent loop.
+template <class T, int VEC> struct RawChunk;
+template <> struct RawChunk<bf16_bits, 8> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const bf16_bits *p) { v = *(const u32x4 *)p; }
+    __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float get(int k) const {
+        return (k & 1) ? bf16_hi(v[k >> 1]) : bf16_lo(v[k >> 1]);
+    }
+};
+template <> struct RawChunk<bf16_bits, 1> {
+    unsigned v;
+    __device__ __forceinline__ void load(const bf16_bits *p) { v = *p; }
+    __device__ __forceinline__ void zero() { v = 0u; }
+    __device__ __forceinline__ float get(int) const { return __uint_as_float(v << 16); }
+};
+template <> struct RawChunk<float, 4> {
+    f32x4 v;
+    __device__ __forceinline__ void load(const float *p) { v = *(const f32x4 *)p; }
+    __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ float get(int k) const { return v[k]; }
+};
+template <> struct RawChunk<float, 1> {
+    float v;
+    __device__ __forceinline__ void load(const float *p) { v = *p; }
+    __device__ __forceinline__ void zero() { v = 0.f; }
+    __device__ __forceinline__ float get(int) const { return v; }
+};
+
+// Store one float32 as the storage type.
+__device__ __forceinline__ void store_one(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_one(bf16_bits *p, float v) { *p = to_bf16(v); }
+
+// ------------------------------------------------------ wave reductions --
+// DPP controls (GFX9 encoding).
+enum : int {
+    DPP_QUAD_XOR1 = 0xB1,   // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,   // quad_perm [2,3,0,1]
+    DPP_ROW_HALF_MIRROR = 0x141,
+    DPP_ROW_MIRROR = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                           0xF, 0xF, false));
+}
+
+// Lane i reads lane i ^ 16 within each half of the wave (ds_swizzle
+// bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10).
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the same bits.
+// Each step pairs lanes symmetrically (a+b and b+a round identically), so
+// after the four DPP steps all 16 lanes of a DPP row hold the row's sum,
+// after the swizzle all 32 lanes of a half hold the half's sum, and the two
+// halves are added once from scalar registers.  Must be called with all 64
+// lanes active.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<DPP_QUAD_XOR1>(v);
+    v += dpp<DPP_QUAD_XOR2>(v);
+    v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp<DPP_ROW_MIRROR>(v);
+    v += swizzle_xor16(v);
+    return lane_value(v, 0) + lane_value(v, 32);
+}
+
+// Two independent sums, interleaved for latency.
+__device__ __forceinline__ void wave_sum2(float &a, float &b) {
+    a += dpp<DPP_QUAD_XOR1>(a);
+    b += dpp<DPP_QUAD_XOR1>(b);
+    a += dpp<DPP_QUAD_XOR2>(a);
+    b += dpp<DPP_QUAD_XOR2>(b);
+    a += dpp<DPP_ROW_HALF_MIRROR>(a);
+    b += dpp<DPP_ROW_HALF_MIRROR>(b);
+    a += dpp<DPP_ROW_MIRROR>(a);
+    b += dpp<DPP_ROW_MIRROR>(b);
+    a += swizzle_xor16(a);
+    b += swizzle_xor16(b);
+    a = lane_value(a, 0) + lane_value(a, 32);
+    b = lane_value(b, 0) + lane_value(b, 32);
+}
+
+__device__ __forceinline__ int wave_id_uniform() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+}  // namespace rn

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI entry points (rn_api.hip) and the
+// kernel translation units (one per direction and storage type).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rn {
+
+enum FwdOp : int { OP_LN = 0, OP_RMS = 1, OP_FUSED = 2 };
+
+// Arguments of one forward call, already validated.  Pointers that a given
+// op does not use are NULL.  x and h may be the same buffer (fused op), so
+// none of these pointers is restrict.
+struct FwdArgs {
+    const void *x;
+    const void *res;
+    const void *gamma;
+    const void *beta;
+    void *y;
+    void *h;
+    float *mean;
+    float *rstd;
+    int64_t ldx, ldr, ldy, ldh;
+    int64_t N;
+    int H;
+    float eps;
+    float inv_H;
+};
+
+// Arguments of one backward call.  `part` is the float32 partial-row
+// workspace: rows [0, P) hold dgamma partials, rows [P, 2P) dbeta (LN).
+struct BwdArgs {
+    const void *dy;
+    const void *x;
+    const void *gamma;
+    const float *mean;
+    const float *rstd;
+    void *dx;
+    float *part;
+    int64_t lddy, ldx, lddx;
+    int64_t N;
+    int H;
+    float inv_H;
+};
+
+// Largest H each path supports: 16-byte vector path, element-wise path.
+constexpr int kMaxHidden = 16384;
+constexpr int kMaxHiddenScalar = 8192;
+
+// Forward: picks the kernel for (op, H, vec) and launches it.  Returns a
+// hipError_t.
+hipError_t launch_fwd_f32(int op, const FwdArgs &a, bool vec, int cus,
+                          hipStream_t s);
+hipError_t launch_fwd_bf16(int op, const FwdArgs &a, bool vec, int cus,
+                           hipStream_t s);
+
+// Backward kernel 1 grid (the number of partial rows P) for a shape.
+int bwd_partials_f32(int64_t N, int H, bool vec, int cus);
+int bwd_partials_bf16(int64_t N, int H, bool vec, int cus);
+
+// Backward: kernel 1 (dx + partial rows) then kernel 2 (partial rows ->
+// dgamma [, dbeta]).  `P` must equal bwd_partials_*(N, H, vec, cus).
+hipError_t launch_bwd_f32(bool ln, const BwdArgs &a, bool vec, int cus, int P,
+                          void *dgamma, void *dbeta, hipStream_t s);
+hipError_t launch_bwd_bf16(bool ln, const BwdArgs &a, bool vec, int cus, int P,
+                           void *dgamma, void *dbeta, hipStream_t s);
+
+hipError_t launch_copy(const void *src, void *dst, size_t bytes,
+                       hipStream_t s);
+
+}  // namespace rn

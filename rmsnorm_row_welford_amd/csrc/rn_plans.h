@@ -1,0 +1,99 @@
+// Plan tables: which team shape serves a row of H elements.
+//
+// Forward rows live in registers (E = VEC*CPL floats per lane plus gamma and
+// beta), backward rows need x_hat, g and two accumulators per element, so
+// the backward keeps E <= 16 and widens the team instead.  Rows whose H,
+// strides or base addresses are not multiples of 16 bytes take the
+// element-wise (VEC = 1) plans.
+#pragma once
+
+#include "rn_kernels.h"
+
+namespace rn {
+
+// Walk a list of plans and run `f.template operator()<P>()` on the first
+// plan whose span covers H.
+template <class... Ps> struct PlanList {};
+
+template <class F>
+hipError_t pick_plan(PlanList<>, int, F &&) {
+    return hipErrorInvalidValue;
+}
+template <class P, class... Ps, class F>
+hipError_t pick_plan(PlanList<P, Ps...>, int H, F &&f) {
+    if (H <= P::SPAN) return f.template operator()<P>();
+    return pick_plan(PlanList<Ps...>{}, H, f);
+}
+
+template <class F>
+int pick_plan_int(PlanList<>, int, F &&) { return -1; }
+template <class P, class... Ps, class F>
+int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
+    if (H <= P::SPAN) return f.template operator()<P>();
+    return pick_plan_int(PlanList<Ps...>{}, H, f);
+}
+
+// ------------------------------------------------------------- forward --
+using FwdPlansBf16 = PlanList<Plan<8, 1, 1, 4>,     //   512
+                              Plan<8, 2, 1, 4>,     //  1024
+                              Plan<8, 4, 1, 4>,     //  2048
+                              Plan<8, 2, 4, 1>,     //  4096
+                              Plan<8, 2, 8, 1>,     //  8192
+                              Plan<8, 2, 16, 1>>;   // 16384
+using FwdPlansF32 = PlanList<Plan<4, 1, 1, 4>,      //   256
+                             Plan<4, 2, 1, 4>,      //   512
+                             Plan<4, 4, 1, 4>,      //  1024
+                             Plan<4, 4, 2, 2>,      //  2048
+                             Plan<4, 4, 4, 1>,      //  4096
+                             Plan<4, 4, 8, 1>,      //  8192
+                             Plan<4, 4, 16, 1>>;    // 16384
+using FwdPlansScalar = PlanList<Plan<1, 1, 1, 4>,   //    64
+                                Plan<1, 4, 1, 4>,   //   256
+                                Plan<1, 4, 4, 1>,   //  1024
+                                Plan<1, 4, 16, 1>,  //  4096
+                                Plan<1, 8, 16, 1>>; //  8192
+
+// ------------------------------------------------------------ backward --
+using BwdPlansBf16 = PlanList<Plan<8, 1, 1, 8>,     //   512
+                              Plan<8, 2, 1, 8>,     //  1024
+                              Plan<8, 2, 2, 4>,     //  2048
+                              Plan<8, 2, 4, 2>,     //  4096
+                              Plan<8, 2, 8, 1>,     //  8192
+                              Plan<8, 2, 16, 1>>;   // 16384
+using BwdPlansF32 = PlanList<Plan<4, 1, 1, 8>,      //   256
+                             Plan<4, 2, 1, 8>,      //   512
+                             Plan<4, 4, 1, 8>,      //  1024
+                             Plan<4, 4, 2, 4>,      //  2048
+                             Plan<4, 4, 4, 2>,      //  4096
+                             Plan<4, 4, 8, 1>,      //  8192
+                             Plan<4, 4, 16, 1>>;    // 16384
+using BwdPlansScalar = PlanList<Plan<1, 1, 1, 8>,   //    64
+                                Plan<1, 4, 1, 8>,   //   256
+                                Plan<1, 4, 4, 2>,   //  1024
+                                Plan<1, 4, 16, 1>,  //  4096
+                                Plan<1, 8, 16, 1>>; //  8192
+
+template <class T, class VecPlans>
+hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
+                        hipStream_t s) {
+    auto f = [&]<class P>() { return launch_fwd_op<T, P>(op, a, cus, s); };
+    return vec ? pick_plan(VecPlans{}, a.H, f)
+               : pick_plan(FwdPlansScalar{}, a.H, f);
+}
+
+template <class VecPlans>
+int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
+    auto f = [&]<class P>() { return bwd_grid<P>(N, cus); };
+    return vec ? pick_plan_int(VecPlans{}, H, f)
+               : pick_plan_int(BwdPlansScalar{}, H, f);
+}
+
+template <class T, class VecPlans>
+hipError_t launch_bwd_t(bool ln, const BwdArgs &a, bool vec, int P,
+                        void *dg, void *db, hipStream_t s) {
+    auto f = [&]<class Pl>() { return launch_bwd_plan<T, Pl>(ln, a, P, dg, db, s); };
+    return vec ? pick_plan(VecPlans{}, a.H, f)
+               : pick_plan(BwdPlansScalar{}, a.H, f);
+}
+
+}  // namespace rn

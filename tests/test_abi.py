@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: librownorm.so loads, exports every function
+include/rownorm.h declares, and rejects bad arguments before anything is
+enqueued (all of these return before the library's first HIP call, so no
+compute call is made here).  Pointers below are fake, suitably aligned
+addresses that are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rmsnorm_row_welford_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rownorm.h")
+
+OK, EINVAL, EDTYPE, EOVERLAP, EWORKSPACE, EHIP, EUNSUP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rn.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return rn.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char|void)\s*\*?\s*"
+                       r"(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("ln_fwd", "rms_fwd", "fused_add_rms_fwd", "ln_bwd", "rms_bwd",
+                 "rn_bwd_workspace_bytes", "rn_status_str"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names == sorted(rn.SIGNATURES), "binding and header disagree"
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_status_strings(L):
+    for code in (OK, EINVAL, EDTYPE, EOVERLAP, EWORKSPACE, EHIP, EUNSUP):
+        s = L.rn_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert L.rn_status_str(12345).decode() == "unknown status"
+
+
+def test_max_hidden(L):
+    assert L.rn_max_hidden(BF16, 1) == 16384
+    assert L.rn_max_hidden(F32, 1) == 16384
+    assert L.rn_max_hidden(BF16, 0) == 8192
+    assert L.rn_max_hidden(9, 1) == 0
+
+
+A = 1 << 30          # fake device addresses, far apart, 256-byte aligned
+X, Y, G, B, M, R, H_, DY, DX, DG, DB, W, RES = (A * k for k in range(1, 14))
+S = None             # stream: never reached
+
+
+def ln_fwd(L, x=X, ldx=1024, g=G, b=B, y=Y, ldy=1024, m=M, r=R, N=8,
+           H=1024, dt=BF16, eps=1e-5):
+    return L.ln_fwd(x, ldx, g, b, y, ldy, m, r, N, H, dt, eps, S)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(eps=0.0), EINVAL), (dict(eps=-1e-5), EINVAL),
+    (dict(eps=float("nan")), EINVAL), (dict(eps=float("inf")), EINVAL),
+    (dict(dt=7), EDTYPE), (dict(H=0), EINVAL), (dict(N=-1), EINVAL),
+    (dict(H=16385, ldx=16385, ldy=16385), EUNSUP),
+    (dict(ldx=1000), EINVAL), (dict(ldy=1023), EINVAL),
+    (dict(x=None), EINVAL), (dict(g=None), EINVAL), (dict(y=None), EINVAL),
+    (dict(x=X + 1), EINVAL),                 # bf16 pointer not 2-aligned
+    (dict(m=M + 2), EINVAL),                 # float pointer not 4-aligned
+    (dict(y=X + 512), EOVERLAP),             # y inside x
+    (dict(y=G - 8), EOVERLAP),               # y runs into gamma
+    (dict(m=R), EOVERLAP),                   # mean == rstd
+    (dict(r=Y + 100), EOVERLAP),             # rstd inside y
+    (dict(N=0), OK),                         # no rows: nothing to do
+    (dict(N=0, b=None, m=None, r=None), OK),
+    (dict(N=0, x=None, y=None), OK),         # torch gives NULL for 0 rows
+    (dict(N=0, g=None), EINVAL),             # gamma is always required
+    # odd H cannot use 16-byte rows; the element-wise path stops at 8192
+    (dict(H=8193, ldx=8193, ldy=8193), EUNSUP),
+])
+def test_ln_fwd_argument_errors(L, kw, want):
+    assert ln_fwd(L, **kw) == want
+
+
+def test_rms_fwd_argument_errors(L):
+    assert L.rms_fwd(X, 64, G, Y, 64, R, 4, 64, BF16, 0.0, S) == EINVAL
+    assert L.rms_fwd(X, 64, G, X, 64, R, 4, 64, BF16, 1e-6, S) == EOVERLAP
+    assert L.rms_fwd(X, 64, G, Y, 64, None, 0, 64, F32, 1e-6, S) == OK
+    assert L.rms_fwd(X, 64, G, Y, 64, None, 4, 64, 3, 1e-6, S) == EDTYPE
+
+
+def fused(L, x=X, ldx=4096, res=RES, ldr=4096, g=G, y=Y, ldy=4096, h=H_,
+          ldh=4096, r=R, N=0, H=4096, dt=BF16, eps=1e-6):
+    return L.fused_add_rms_fwd(x, ldx, res, ldr, g, y, ldy, h, ldh, r, N, H,
+                               dt, eps, S)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), OK),
+    (dict(h=X), OK),                 # in place over x
+    (dict(h=RES), OK),               # in place over the residual
+    (dict(h=X, ldh=4104), EOVERLAP),  # same base, different stride
+    (dict(h=X + 64), EOVERLAP),      # partial overlap
+    (dict(res=X, h=X), EOVERLAP),    # x == residual == h
+    (dict(y=X), EOVERLAP),
+    (dict(y=H_), EOVERLAP),          # y == h
+    (dict(res=None), EINVAL), (dict(h=None), EINVAL),
+    (dict(ldr=4000), EINVAL), (dict(ldh=100), EINVAL),
+])
+def test_fused_argument_errors(L, kw, want):
+    kw.setdefault("N", 16)
+    if want == OK:
+        kw["N"] = 0     # valid: N = 0 returns before touching the device
+    assert fused(L, **kw) == want
+
+
+def ln_bwd(L, dy=DY, lddy=1024, x=X, ldx=1024, g=G, m=M, r=R, dx=DX,
+           lddx=1024, dg=DG, db=DB, w=W, wb=1 << 24, N=8, H=1024, dt=BF16,
+           eps=1e-5):
+    return L.ln_bwd(dy, lddy, x, ldx, g, m, r, dx, lddx, dg, db, w, wb, N, H,
+                    dt, eps, S)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(m=None), EINVAL), (dict(r=None), EINVAL), (dict(db=None), EINVAL),
+    (dict(dg=None), EINVAL), (dict(dx=None), EINVAL),
+    (dict(w=W + 16), EINVAL),              # workspace not 256-aligned
+    (dict(dx=DY), EOVERLAP), (dict(dx=X + 2048), EOVERLAP),
+    (dict(dg=DB), EOVERLAP), (dict(w=X), EOVERLAP),
+    (dict(dg=G), EOVERLAP),
+    (dict(eps=0.0), EINVAL), (dict(dt=5), EDTYPE),
+    (dict(H=16385, lddy=16385, ldx=16385, lddx=16385), EUNSUP),
+    (dict(lddx=1000), EINVAL),
+])
+def test_ln_bwd_argument_errors(L, kw, want):
+    assert ln_bwd(L, **kw) == want
+
+
+def test_rms_bwd_argument_errors(L):
+    a = (DY, 256, X, 256, G, R, DX, 256, DG, W, 1 << 20)
+    assert L.rms_bwd(*a, 4, 256, BF16, -1.0, S) == EINVAL
+    b = (DY, 256, X, 256, G, None, DX, 256, DG, W, 1 << 20)
+    assert L.rms_bwd(*b, 4, 256, BF16, 1e-5, S) == EINVAL
+    c = (DY, 256, X, 256, G, R, X, 256, DG, W, 1 << 20)
+    assert L.rms_bwd(*c, 4, 256, BF16, 1e-5, S) == EOVERLAP
+
+
+def test_workspace_query_without_device(L):
+    out = ctypes.c_size_t(123)
+    assert L.rn_bwd_workspace_bytes(0, 1024, BF16, 1, ctypes.byref(out)) == OK
+    assert out.value == 0
+    assert L.rn_bwd_workspace_bytes(10, 1024, 9, 1, ctypes.byref(out)) == EDTYPE
+    assert L.rn_bwd_workspace_bytes(10, 0, BF16, 1, ctypes.byref(out)) == EINVAL
+    assert L.rn_bwd_workspace_bytes(10, 1024, BF16, 1, None) == EINVAL
+
+
+def test_copy_argument_errors(L):
+    assert L.rn_copy(X, Y, 0, S) == OK
+    assert L.rn_copy(None, Y, 16, S) == EINVAL
+    assert L.rn_copy(X, X + 8, 64, S) == EOVERLAP

@@ -1,0 +1,340 @@
+"""HIP path vs the binary64 oracle, element by element, on the same seeded
+inputs (rmsnorm_row_welford_amd.synth), through the C ABI.
+
+Full-size workloads run on the GPU exactly as the benchmark launches them;
+the oracle then checks sampled rows (and, for the backward, dgamma/dbeta
+over all rows).  Smaller shapes are checked in full.  Bars: tests/tolerance.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tolerance as tol
+import rmsnorm_row_welford_amd as rn
+from rmsnorm_row_welford_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def sample_rows(N, k=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, N // 2, N - 1} | set(rng.choice(N, size=min(k, N), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+def dec(orc, arr, k, dtype):
+    return orc.decode(arr[k], dtype)
+
+
+# ----------------------------------------------------------------- helpers --
+def check_ln_fwd(orc, arr, dtype, eps, rows=None, use_beta=True):
+    x = to_dev(arr["x"])
+    g = to_dev(arr["gamma"])
+    b = to_dev(arr["beta"]) if (use_beta and "beta" in arr) else None
+    y, mean, rstd = rn.ln_fwd(x, g, b, eps)
+    torch.cuda.synchronize()
+    rows = np.arange(arr["x"].shape[0]) if rows is None else rows
+    xd = orc.decode(arr["x"][rows], dtype)
+    e = oracle.eps_at_boundary(eps)
+    bd = dec(orc, arr, "beta", dtype) if b is not None else None
+    y_o, m_o, r_o = orc.ln_fwd(xd, dec(orc, arr, "gamma", dtype), bd, e)
+    var_o = 1.0 / (r_o * r_o) - e
+    stats = tol.check_out(host(y)[rows], y_o, dtype, orc, "LN y")
+    tol.check_mean(host(mean)[rows], m_o, var_o, e, "LN mean")
+    tol.check_rstd(host(rstd)[rows], r_o, "LN rstd")
+    return y, mean, rstd, stats
+
+
+def check_rms_fwd(orc, arr, dtype, eps, rows=None):
+    x = to_dev(arr["x"])
+    g = to_dev(arr["gamma"])
+    y, rstd = rn.rms_fwd(x, g, eps)
+    torch.cuda.synchronize()
+    rows = np.arange(arr["x"].shape[0]) if rows is None else rows
+    xd = orc.decode(arr["x"][rows], dtype)
+    y_o, r_o = orc.rms_fwd(xd, dec(orc, arr, "gamma", dtype),
+                           oracle.eps_at_boundary(eps))
+    stats = tol.check_out(host(y)[rows], y_o, dtype, orc, "RMS y")
+    tol.check_rstd(host(rstd)[rows], r_o, "RMS rstd")
+    return y, rstd, stats
+
+
+def check_bwd(orc, arr, dtype, eps, layernorm, rows=None):
+    """GPU forward (for the saved stats), GPU backward, oracle backward."""
+    x = to_dev(arr["x"])
+    dy = to_dev(arr["dy"])
+    g = to_dev(arr["gamma"])
+    N = arr["x"].shape[0]
+    e = oracle.eps_at_boundary(eps)
+    xd = orc.decode(arr["x"], dtype)
+    dyd = orc.decode(arr["dy"], dtype)
+    gd = orc.decode(arr["gamma"], dtype)
+    rows = np.arange(N) if rows is None else rows
+    if layernorm:
+        _, mean, rstd = rn.ln_fwd(x, g, None, eps)
+        dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, eps)
+        torch.cuda.synchronize()
+        dx_o, dg_o, db_o, _, _ = orc.ln_bwd(dyd, xd, gd, e)
+    else:
+        _, rstd = rn.rms_fwd(x, g, eps)
+        dx, dg = rn.rms_bwd(dy, x, g, rstd, eps)
+        torch.cuda.synchronize()
+        dx_o, dg_o, _ = orc.rms_bwd(dyd, xd, gd, e)
+    stats = tol.check_out(host(dx)[rows], dx_o[rows], dtype, orc, "dx")
+    rr = tol.check_param(orc.decode(host(dg), dtype), dg_o, "dgamma")
+    if layernorm:
+        tol.check_param(orc.decode(host(db), dtype), db_o, "dbeta")
+    return stats, rr
+
+
+# ------------------------------------------------------- the workloads --
+def test_ln_f32_64x1000_fwd_bwd(orc):
+    w = synth.WORKLOADS["ln_f32_64x1000"]
+    arr = synth.generate(w)
+    check_ln_fwd(orc, arr, "f32", w.eps)
+    check_bwd(orc, arr, "f32", w.eps, layernorm=True)
+
+
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_fwd_bf16_8192x1024(orc, op):
+    w = synth.WORKLOADS["fwd_bf16_8192x1024"]
+    arr = synth.generate(w)
+    if op == "ln":
+        y, mean, rstd, _ = check_ln_fwd(orc, arr, "bf16", w.eps, use_beta=False)
+        # rows [N/2, N) are exactly 50.0 after rounding: zero variance,
+        # y = beta = 0, mean = 50, rstd = 1/sqrt(eps) (in float32)
+        lo = w.N // 2
+        assert np.all(host(y)[lo:] == 0)
+        assert np.all(host(mean)[lo:] == 50.0)
+        want = np.float32(1.0) / np.sqrt(np.float32(w.eps))
+        assert np.allclose(host(rstd)[lo:], want, rtol=1e-6)
+    else:
+        check_rms_fwd(orc, arr, "bf16", w.eps)
+
+
+def test_fused_bf16_32768x4096(orc):
+    w = synth.WORKLOADS["fused_bf16_32768x4096"]
+    arr = synth.generate(w)
+    x = to_dev(arr["x"])
+    r = to_dev(arr["residual"])
+    g = to_dev(arr["gamma"])
+    y, h, rstd = rn.fused_add_rms_fwd(x, r, g, w.eps)
+    torch.cuda.synchronize()
+    # h: every element, bit-exact
+    h_exact = orc.decode(arr["x"], "bf16") + orc.decode(arr["residual"], "bf16")
+    assert np.array_equal(host(h), orc.bf16_encode(h_exact)), "h not RNE(x + r)"
+    rows = sample_rows(w.N)
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(
+        orc.decode(arr["x"][rows], "bf16"), orc.decode(arr["residual"][rows], "bf16"),
+        orc.decode(arr["gamma"], "bf16"), oracle.eps_at_boundary(w.eps))
+    tol.check_bf16(host(y)[rows], y_o, orc, "fused y")
+    tol.check_rstd(host(rstd)[rows], r_o, "fused rstd")
+
+
+BWD = ["bwd_bf16_32768x1024", "bwd_bf16_16384x2048", "bwd_bf16_512x16384",
+       "bwd_bf16_2048x16384"]
+
+
+@pytest.mark.parametrize("name", BWD)
+@pytest.mark.parametrize("op", ["ln", "rms"])
+def test_bwd_workloads(orc, name, op):
+    w = synth.WORKLOADS[name]
+    arr = synth.generate(w)
+    rows = sample_rows(w.N)
+    if op == "ln":
+        check_ln_fwd(orc, arr, "bf16", w.eps, rows=rows)
+    else:
+        check_rms_fwd(orc, arr, "bf16", w.eps, rows=rows)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=(op == "ln"), rows=rows)
+
+
+# ------------------------------------------------------------ edge cases --
+# The LayerNorm page's validation list (64 ... 2049) plus tiny rows, ragged
+# tails, element-wise-path shapes and the largest rows.
+SHAPES = [64, 128, 512, 768, 1024, 2049, 1, 2, 3, 1000, 3000, 4095, 4096,
+          8192, 12288, 16384]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H", SHAPES)
+def test_shapes_all_ops(orc, dtype, H):
+    N = 67 if H <= 4096 else 19
+    arr = synth.custom(100 + H, N, H, dtype)
+    check_ln_fwd(orc, arr, dtype, 1e-5)
+    check_rms_fwd(orc, arr, dtype, 1e-5)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
+    x, r, g = (to_dev(arr[k]) for k in ("x", "residual", "gamma"))
+    y, h, rstd = rn.fused_add_rms_fwd(x, r, g, 1e-6)
+    torch.cuda.synchronize()
+    xd, rd = orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype)
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(xd, rd, orc.decode(arr["gamma"], dtype),
+                                          oracle.eps_at_boundary(1e-6))
+    assert np.array_equal(host(h), orc.encode(h_o, dtype))
+    tol.check_out(host(y), y_o, dtype, orc, "fused y")
+    tol.check_rstd(host(rstd), r_o, "fused rstd")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_variance_rows(orc, dtype):
+    # fp32 rows with |mean|/sigma = 50 and constant rows
+    N, H = 40, 1024
+    arr = synth.custom(5, N, H, dtype, x=(0.0, 1.0), half_shifted=(2.0, 0.04))
+    check_ln_fwd(orc, arr, dtype, 1e-5)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
+    c = arr["x"].copy()
+    c[:] = c[0, 0]      # every row constant
+    arr2 = dict(arr, x=c)
+    y, mean, rstd, _ = check_ln_fwd(orc, arr2, dtype, 1e-5)
+    assert np.all(orc.decode(host(y), dtype) == orc.decode(arr["beta"], dtype)[None, :])
+
+
+@pytest.mark.parametrize("pad", [24, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_rows_and_canaries(orc, dtype, pad):
+    """Row strides > H (pad 24 keeps 16-byte rows, pad 3 forces the
+    element-wise path): the padding between rows and a guard row after the
+    last row stay untouched, and results match the oracle."""
+    N, H = 33, 1024
+    arr = synth.custom(11, N, H, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    SENT = -7.0
+
+    def buf(a=None):
+        t = torch.full((N + 1, H + pad), SENT, dtype=tdt, device=DEV)
+        if a is not None:
+            t[:N, :H] = to_dev(a)
+        return t
+
+    def view(t):
+        return t.as_strided((N, H), (H + pad, 1))
+
+    X, DY, R = buf(arr["x"]), buf(arr["dy"]), buf(arr["residual"])
+    Y, DX, HH, Y2 = buf(), buf(), buf(), buf()
+    g, b = to_dev(arr["gamma"]), to_dev(arr["beta"])
+    _, mean, rstd = rn.ln_fwd(view(X), g, b, 1e-5, y=view(Y))
+    rn.ln_bwd(view(DY), view(X), g, mean, rstd, 1e-5, dx=view(DX))
+    rn.fused_add_rms_fwd(view(X), view(R), g, 1e-6, y=view(Y2), h=view(HH))
+    torch.cuda.synchronize()
+    for t, name in ((Y, "y"), (DX, "dx"), (HH, "h"), (Y2, "fused y")):
+        hb = t.float().cpu().numpy()
+        assert np.all(hb[:N, H:] == SENT), f"{name}: row padding written"
+        assert np.all(hb[N, :] == SENT), f"{name}: guard row written"
+    e = oracle.eps_at_boundary(1e-5)
+    xd = orc.decode(arr["x"], dtype)
+    gd, bd = orc.decode(arr["gamma"], dtype), orc.decode(arr["beta"], dtype)
+    y_o, _, _ = orc.ln_fwd(xd, gd, bd, e)
+    tol.check_out(host(Y[:N, :H].contiguous()), y_o, dtype, orc, "strided LN y")
+    dx_o, _, _, _, _ = orc.ln_bwd(orc.decode(arr["dy"], dtype), xd, gd, e)
+    tol.check_out(host(DX[:N, :H].contiguous()), dx_o, dtype, orc, "strided dx")
+    h_o = xd + orc.decode(arr["residual"], dtype)
+    assert np.array_equal(host(HH[:N, :H].contiguous()), orc.encode(h_o, dtype))
+
+
+@pytest.mark.parametrize("alias", ["x", "residual"])
+def test_fused_in_place(orc, alias):
+    N, H = 129, 4096
+    arr = synth.custom(12, N, H, "bf16")
+    x, r, g = (to_dev(arr[k]) for k in ("x", "residual", "gamma"))
+    target = x if alias == "x" else r
+    y, h, _ = rn.fused_add_rms_fwd(x, r, g, 1e-6, h=target)
+    torch.cuda.synchronize()
+    assert h.data_ptr() == target.data_ptr()
+    xd, rd = orc.decode(arr["x"], "bf16"), orc.decode(arr["residual"], "bf16")
+    y_o, h_o, _ = orc.fused_add_rms_fwd(xd, rd, orc.decode(arr["gamma"], "bf16"),
+                                        oracle.eps_at_boundary(1e-6))
+    assert np.array_equal(host(target), orc.bf16_encode(h_o))
+    tol.check_bf16(host(y), y_o, orc, "in-place fused y")
+
+
+@pytest.mark.parametrize("H", [1024, 16384])
+def test_bitwise_deterministic(H):
+    N = 4099
+    arr = synth.custom(13, N, H, "bf16")
+    x, dy, g, b = (to_dev(arr[k]) for k in ("x", "dy", "gamma", "beta"))
+    outs = []
+    for _ in range(2):
+        y, mean, rstd = rn.ln_fwd(x, g, b, 1e-5)
+        dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5)
+        _, rs2 = rn.rms_fwd(x, g, 1e-5)
+        dx2, dg2 = rn.rms_bwd(dy, x, g, rs2, 1e-5)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (y, mean, rstd, dx, dg, db, dx2, dg2)])
+    for a, b_ in zip(*outs):
+        assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("N", [0, 1, 2, 7, 255, 513])
+def test_row_counts(orc, N):
+    """N = 0 (no rows: dgamma = dbeta = 0), N below the partial-row count,
+    and N just above it."""
+    H = 1024
+    if N == 0:
+        x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+        g = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+        y, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+        dg = torch.full((H,), 3.0, dtype=torch.bfloat16, device=DEV)
+        db = torch.full((H,), 3.0, dtype=torch.bfloat16, device=DEV)
+        rn.ln_bwd(x, x, g, mean, rstd, 1e-5, dgamma=dg, dbeta=db)
+        torch.cuda.synchronize()
+        assert torch.all(dg == 0) and torch.all(db == 0)
+        return
+    arr = synth.custom(14 + N, N, H, "bf16")
+    check_ln_fwd(orc, arr, "bf16", 1e-5)
+    check_bwd(orc, arr, "bf16", 1e-5, layernorm=True)
+    check_bwd(orc, arr, "bf16", 1e-5, layernorm=False)
+
+
+def test_many_short_rows(orc):
+    """Persistent loops with many iterations per workgroup."""
+    N, H = 200003, 64
+    arr = synth.custom(15, N, H, "bf16")
+    rows = sample_rows(N, k=300)
+    check_ln_fwd(orc, arr, "bf16", 1e-5, rows=rows)
+    check_rms_fwd(orc, arr, "bf16", 1e-5, rows=rows)
+    check_bwd(orc, arr, "bf16", 1e-5, layernorm=True, rows=rows)
+
+
+def test_unsupported_sizes():
+    g = torch.ones(16385, dtype=torch.bfloat16, device=DEV)
+    x = torch.ones((2, 16385), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(rn.RowNormError) as ei:
+        rn.rms_fwd(x, g, 1e-5)
+    assert ei.value.status == -6
+    # odd H above the element-wise limit
+    x = torch.ones((2, 8193), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(rn.RowNormError) as ei:
+        rn.rms_fwd(x, g[:8193], 1e-5)
+    assert ei.value.status == -6
+
+
+def test_workspace_errors():
+    H = 1024
+    x = torch.ones((64, H), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    _, rstd = rn.rms_fwd(x, g, 1e-5)
+    need = rn.workspace_bytes(64, H, torch.bfloat16, False)
+    assert need > 0
+    small = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(rn.RowNormError) as ei:
+        rn.rms_bwd(x, x, g, rstd, 1e-5, workspace=small)
+    assert ei.value.status == -4
+    # the workspace does not grow with N past the partial-row cap
+    assert rn.workspace_bytes(10 ** 6, H, torch.bfloat16, True) == \
+        rn.workspace_bytes(10 ** 7, H, torch.bfloat16, True)

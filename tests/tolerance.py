@@ -1,0 +1,96 @@
+"""Parity bars between the HIP path and the binary64 oracle.
+
+bf16 outputs: the GPU value must be within 1 bf16 ulp of the correctly
+  rounded oracle value (distance measured on the ordered integer image of the
+  bit patterns, +0 == -0), or, for values produced by cancellation, within an
+  absolute floor of 2^-16 times the row's RMS of the oracle output.  The
+  float32 pipeline's own error is a few float32 ulps of the row scale
+  (about 2^-22 * scale); a bf16 ulp at |v| is 2^-8..2^-7 * |v|, so only
+  outputs far below the row scale can need the floor.
+fp32 outputs: |gpu - oracle| <= 1e-5 * max(|oracle|, row RMS of oracle).
+mean (fp32): |gpu - oracle| <= 1e-5 * max(|mean|, sqrt(var + eps)).
+rstd (fp32): relative 1e-5.
+dgamma/dbeta: relative RMS error ||gpu - oracle|| / ||oracle|| <= 5e-3.
+h of the fused op: bit-exact to RNE(x + residual).
+"""
+import numpy as np
+
+BF16_FLOOR = 2.0 ** -16
+F32_REL = 1e-5
+PARAM_REL_RMS = 5e-3
+
+
+def ordered(bits_u16: np.ndarray) -> np.ndarray:
+    """Map bfloat16 bit patterns to integers ordered like their values."""
+    b = bits_u16.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def row_rms(v: np.ndarray) -> np.ndarray:
+    v = np.atleast_2d(v)
+    return np.sqrt(np.mean(v * v, axis=1, keepdims=True))
+
+
+def check_bf16(gpu_bits, oracle_vals, orc, what):
+    """gpu_bits: uint16 [N, H]; oracle_vals: float64 [N, H] (unrounded)."""
+    gpu_bits = np.atleast_2d(gpu_bits)
+    oracle_vals = np.atleast_2d(oracle_vals)
+    want = orc.bf16_encode(oracle_vals)
+    ulp = np.abs(ordered(gpu_bits) - ordered(want))
+    gv = orc.bf16_decode(gpu_bits)
+    floor = BF16_FLOOR * row_rms(oracle_vals)
+    ok = (ulp <= 1) | (np.abs(gv - oracle_vals) <= floor)
+    bad = np.argwhere(~ok)
+    if bad.size:
+        i, j = bad[0]
+        raise AssertionError(
+            f"{what}: {len(bad)} of {ok.size} elements off; first at "
+            f"[{i},{j}] gpu={gv[i, j]!r} oracle={oracle_vals[i, j]!r} "
+            f"ulp={ulp[i, j]}")
+    return {"max_ulp": int(ulp.max()) if ulp.size else 0,
+            "floored": int(np.sum((ulp > 1) & ok))}
+
+
+def check_f32(gpu, oracle_vals, what, rel=F32_REL):
+    gpu = np.atleast_2d(np.asarray(gpu, dtype=np.float64))
+    oracle_vals = np.atleast_2d(oracle_vals)
+    scale = np.maximum(np.abs(oracle_vals), row_rms(oracle_vals))
+    err = np.abs(gpu - oracle_vals)
+    ok = err <= rel * scale
+    bad = np.argwhere(~ok)
+    if bad.size:
+        i, j = bad[0]
+        raise AssertionError(
+            f"{what}: {len(bad)} of {ok.size} off; first at [{i},{j}] "
+            f"gpu={gpu[i, j]!r} oracle={oracle_vals[i, j]!r}")
+    return float(np.max(err / np.maximum(scale, 1e-300))) if err.size else 0.0
+
+
+def check_out(gpu_host, oracle_vals, dtype, orc, what):
+    if dtype == "bf16":
+        return check_bf16(gpu_host, oracle_vals, orc, what)
+    return check_f32(gpu_host, oracle_vals, what)
+
+
+def check_mean(gpu, mean_o, var_o, eps, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    scale = np.maximum(np.abs(mean_o), np.sqrt(var_o + eps))
+    err = np.abs(gpu - mean_o)
+    assert np.all(err <= F32_REL * scale), \
+        f"{what}: max scaled err {np.max(err / scale):.3e}"
+
+
+def check_rstd(gpu, rstd_o, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    rel = np.abs(gpu - rstd_o) / np.abs(rstd_o)
+    assert np.all(rel <= F32_REL), f"{what}: max rel err {rel.max():.3e}"
+
+
+def check_param(gpu_vals, oracle_vals, what):
+    gpu_vals = np.asarray(gpu_vals, dtype=np.float64)
+    num = np.linalg.norm(gpu_vals - oracle_vals)
+    den = np.linalg.norm(oracle_vals)
+    rr = num / den if den > 0 else num
+    assert rr <= PARAM_REL_RMS, f"{what}: rel-rms {rr:.3e}"
+    return rr
