@@ -25,6 +25,8 @@ shapes and test lists describe them):
   fused_bf16_32768x4096  fused add+RMSNorm fwd, bf16, (B=16, T=2048) -> N=32768,
                        H=4096; x, residual ~ N(0,1); gamma = 1 + N(0, 0.05);
                        eps 1e-6
+  step_bf16_32768x1024  the benchmark step: x, residual, dy ~ N(0,1),
+                       gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1), eps 1e-5
   bwd_bf16_32768x1024, bwd_bf16_16384x2048  (tall-narrow)
   bwd_bf16_512x16384,  bwd_bf16_2048x16384  (wide)
                        LayerNorm and RMSNorm fwd+bwd, bf16; x, dy ~ N(0,1),
@@ -66,6 +68,11 @@ WORKLOADS: Dict[str, Workload] = {
                  residual=(0.0, 1.0), dy=None),
         Workload("bwd_bf16_32768x1024", 1004, 32768, 1024, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        # one full training-style pass at the headline shape: LN and RMS
+        # forward, fused add+RMSNorm forward, LN and RMS backward
+        Workload("step_bf16_32768x1024", 1004, 32768, 1024, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1),
+                 residual=(0.0, 1.0)),
         Workload("bwd_bf16_16384x2048", 1004, 16384, 2048, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         Workload("bwd_bf16_512x16384", 1005, 512, 16384, "bf16", 1e-5,

@@ -3,11 +3,15 @@
 bf16 outputs: the GPU value must be within 1 bf16 ulp of the correctly
   rounded oracle value (distance measured on the ordered integer image of the
   bit patterns, +0 == -0), or, for values produced by cancellation, within an
-  absolute floor of 2^-16 times the row's RMS of the oracle output.  The
-  float32 pipeline's own error is a few float32 ulps of the row scale
-  (about 2^-22 * scale); a bf16 ulp at |v| is 2^-8..2^-7 * |v|, so only
-  outputs far below the row scale can need the floor.
-fp32 outputs: |gpu - oracle| <= 1e-5 * max(|oracle|, row RMS of oracle).
+  absolute floor of 2^-16 times the row's scale.  The float32 pipeline's own
+  error is a few float32 ulps of the scale of the terms that cancel (about
+  2^-22 * scale); a bf16 ulp at |v| is 2^-8..2^-7 * |v|, so only outputs far
+  below that scale can need the floor.  The row scale is the RMS of the
+  oracle output, or for dx the larger of that and rstd * RMS(dy * gamma):
+  dx = rstd * (g - c1 - x_hat * c2) is a difference of terms of size
+  rstd * |g|, and for short rows it can cancel almost completely (H = 1
+  RMSNorm: dx = rstd * g * eps / (x^2 + eps)).
+fp32 outputs: |gpu - oracle| <= 1e-5 * max(|oracle|, row scale).
 mean (fp32): |gpu - oracle| <= 1e-5 * max(|mean|, sqrt(var + eps)).
 rstd (fp32): relative 1e-5.
 dgamma/dbeta: relative RMS error ||gpu - oracle|| / ||oracle|| <= 5e-3.
@@ -32,14 +36,22 @@ def row_rms(v: np.ndarray) -> np.ndarray:
     return np.sqrt(np.mean(v * v, axis=1, keepdims=True))
 
 
-def check_bf16(gpu_bits, oracle_vals, orc, what):
-    """gpu_bits: uint16 [N, H]; oracle_vals: float64 [N, H] (unrounded)."""
+def _scale(oracle_vals, term_scale):
+    s = row_rms(oracle_vals)
+    if term_scale is not None:
+        s = np.maximum(s, np.asarray(term_scale, dtype=np.float64).reshape(-1, 1))
+    return s
+
+
+def check_bf16(gpu_bits, oracle_vals, orc, what, term_scale=None):
+    """gpu_bits: uint16 [N, H]; oracle_vals: float64 [N, H] (unrounded);
+    term_scale: optional per-row scale of the terms that cancel."""
     gpu_bits = np.atleast_2d(gpu_bits)
     oracle_vals = np.atleast_2d(oracle_vals)
     want = orc.bf16_encode(oracle_vals)
     ulp = np.abs(ordered(gpu_bits) - ordered(want))
     gv = orc.bf16_decode(gpu_bits)
-    floor = BF16_FLOOR * row_rms(oracle_vals)
+    floor = BF16_FLOOR * _scale(oracle_vals, term_scale)
     ok = (ulp <= 1) | (np.abs(gv - oracle_vals) <= floor)
     bad = np.argwhere(~ok)
     if bad.size:
@@ -52,10 +64,10 @@ def check_bf16(gpu_bits, oracle_vals, orc, what):
             "floored": int(np.sum((ulp > 1) & ok))}
 
 
-def check_f32(gpu, oracle_vals, what, rel=F32_REL):
+def check_f32(gpu, oracle_vals, what, rel=F32_REL, term_scale=None):
     gpu = np.atleast_2d(np.asarray(gpu, dtype=np.float64))
     oracle_vals = np.atleast_2d(oracle_vals)
-    scale = np.maximum(np.abs(oracle_vals), row_rms(oracle_vals))
+    scale = np.maximum(np.abs(oracle_vals), _scale(oracle_vals, term_scale))
     err = np.abs(gpu - oracle_vals)
     ok = err <= rel * scale
     bad = np.argwhere(~ok)
@@ -67,10 +79,16 @@ def check_f32(gpu, oracle_vals, what, rel=F32_REL):
     return float(np.max(err / np.maximum(scale, 1e-300))) if err.size else 0.0
 
 
-def check_out(gpu_host, oracle_vals, dtype, orc, what):
+def check_out(gpu_host, oracle_vals, dtype, orc, what, term_scale=None):
     if dtype == "bf16":
-        return check_bf16(gpu_host, oracle_vals, orc, what)
-    return check_f32(gpu_host, oracle_vals, what)
+        return check_bf16(gpu_host, oracle_vals, orc, what, term_scale)
+    return check_f32(gpu_host, oracle_vals, what, term_scale=term_scale)
+
+
+def dx_term_scale(dy, gamma, rstd):
+    """Per-row scale of the terms dx is the difference of: rstd*RMS(dy*gamma)."""
+    g = np.atleast_2d(dy) * np.asarray(gamma)[None, :]
+    return np.asarray(rstd) * np.sqrt(np.mean(g * g, axis=1))
 
 
 def check_mean(gpu, mean_o, var_o, eps, what):
