@@ -6,17 +6,24 @@ at the headline shape (bf16, N=32768 rows, H=1024):
     -> LayerNorm bwd (dx, dgamma, dbeta)  ->  RMSNorm bwd (dx, dgamma)
 
 Inputs are synthetic (rmsnorm_row_welford_amd.synth, workload
-step_bf16_32768x1024) and resident in HBM before timing.  By default every
-op runs cold: a read-only sweep of a 512 MiB buffer (twice the 256 MB
-Infinity Cache, far above the 8 x 4 MB of L2) precedes it, and HIP events on
-the launch stream bracket the op alone.  The step time is the sum of the
-five op times; value = the step's algorithmic HBM bytes / step time.
+step_bf16_32768x1024) and resident in HBM before timing.
 
-Prints ONE JSON line on stdout (diagnostics go to stderr).  One GPU only.
+Cold data without cache sweeps: the step's tensors exist in M = 6 copies
+("sets", about 3.4 GiB) and consecutive ops use consecutive sets, so every
+launch reads data last touched about 1 GiB of traffic earlier, far beyond
+the 256 MB Infinity Cache and 32 MB of L2.  The K timed steps run back to
+back between two HIP events on the launch stream (ms_per_step = elapsed/K).
+The per-op table times K launches of one op back to back over the rotating
+sets the same way.  --sweep adds the isolated protocol (a 512 MiB read sweep
+before each op, events around the op alone), which also pays each op's
+launch latency.
+
+value = the step's algorithmic HBM bytes / ms_per_step.  Prints ONE JSON line
+on stdout (diagnostics go to stderr).  One GPU only.
 """
 import argparse
-import hashlib
 import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_GBS = 8000.0          # MI355X HBM3E, published
 WORKLOAD = "step_bf16_32768x1024"
 FUSED_EPS = 1e-6
+OPS = ("ln_fwd", "rms_fwd", "fused_add_rms_fwd", "ln_bwd", "rms_bwd")
 
 
 def log(*a):
@@ -39,11 +47,11 @@ def log(*a):
 def alg_bytes(N, H, e):
     """Algorithmic HBM bytes of each op: every tensor read or written once."""
     return {
-        "ln_fwd": 2 * N * H * e + 2 * H * e + 8 * N,       # x,y,gamma,beta,mean,rstd
-        "rms_fwd": 2 * N * H * e + H * e + 4 * N,          # x,y,gamma,rstd
-        "fused_add_rms_fwd": 4 * N * H * e + H * e + 4 * N,  # x,r,h,y,gamma,rstd
-        "ln_bwd": 3 * N * H * e + 3 * H * e + 8 * N,       # dy,x,dx,gamma,dg,db,stats
-        "rms_bwd": 3 * N * H * e + 2 * H * e + 4 * N,      # dy,x,dx,gamma,dg,rstd
+        "ln_fwd": 2 * N * H * e + 2 * H * e + 8 * N,          # x,y,gamma,beta,mean,rstd
+        "rms_fwd": 2 * N * H * e + H * e + 4 * N,             # x,y,gamma,rstd
+        "fused_add_rms_fwd": 4 * N * H * e + H * e + 4 * N,   # x,r,h,y,gamma,rstd
+        "ln_bwd": 3 * N * H * e + 3 * H * e + 8 * N,          # dy,x,dx,gamma,dg,db,stats
+        "rms_bwd": 3 * N * H * e + 2 * H * e + 4 * N,         # dy,x,dx,gamma,dg,rstd
     }
 
 
@@ -69,6 +77,138 @@ def counters_traffic(op, shape_tag):
     return d.get("traffic_bytes_per_launch")
 
 
+class Sets:
+    """M copies of the step's tensors on the GPU, and the five ops bound to
+    one copy each."""
+
+    def __init__(self, rn, arr, eps, M, dev):
+        import torch
+        self.rn, self.eps, self.M = rn, eps, M
+        bf = torch.bfloat16
+        N, H = arr["x"].shape
+
+        def to_dev(a):
+            return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
+
+        x0, r0, dy0 = to_dev(arr["x"]), to_dev(arr["residual"]), to_dev(arr["dy"])
+        self.g, self.b = to_dev(arr["gamma"]), to_dev(arr["beta"])
+        ws_ln = rn.workspace_bytes(N, H, bf, True)
+        ws_rms = rn.workspace_bytes(N, H, bf, False)
+        self.s = []
+        for _ in range(M):
+            t = {"x": x0.clone(), "r": r0.clone(), "dy": dy0.clone()}
+            for k in ("y", "y2", "y3", "h", "dx", "dx2"):
+                t[k] = torch.empty((N, H), dtype=bf, device=dev)
+            for k in ("mean", "rstd", "rstd2", "rstd3"):
+                t[k] = torch.empty(N, dtype=torch.float32, device=dev)
+            for k in ("dg", "db", "dg2"):
+                t[k] = torch.empty(H, dtype=bf, device=dev)
+            t["ws_ln"] = torch.empty(ws_ln, dtype=torch.uint8, device=dev)
+            t["ws_rms"] = torch.empty(ws_rms, dtype=torch.uint8, device=dev)
+            self.s.append(t)
+        del x0, r0, dy0
+        for i in range(M):       # saved statistics for the backward ops
+            self.run("ln_fwd", i)
+            self.run("rms_fwd", i)
+
+    def run(self, op, i):
+        rn, t, g, b, eps = self.rn, self.s[i % self.M], self.g, self.b, self.eps
+        if op == "ln_fwd":
+            rn.ln_fwd(t["x"], g, b, eps, y=t["y"], mean=t["mean"], rstd=t["rstd"])
+        elif op == "rms_fwd":
+            rn.rms_fwd(t["x"], g, eps, y=t["y2"], rstd=t["rstd2"])
+        elif op == "fused_add_rms_fwd":
+            rn.fused_add_rms_fwd(t["x"], t["r"], g, FUSED_EPS, y=t["y3"], h=t["h"],
+                                 rstd=t["rstd3"])
+        elif op == "ln_bwd":
+            rn.ln_bwd(t["dy"], t["x"], g, t["mean"], t["rstd"], eps, dx=t["dx"],
+                      dgamma=t["dg"], dbeta=t["db"], workspace=t["ws_ln"])
+        elif op == "rms_bwd":
+            rn.rms_bwd(t["dy"], t["x"], g, t["rstd2"], eps, dx=t["dx2"],
+                       dgamma=t["dg2"], workspace=t["ws_rms"])
+        else:
+            raise ValueError(op)
+
+
+def time_steps(sets, ops, K, W):
+    """ms per step: K steps back to back, consecutive ops on consecutive sets."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n = len(ops)
+    for s in range(W):
+        for j, op in enumerate(ops):
+            sets.run(op, s * n + j)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for s in range(K):
+        for j, op in enumerate(ops):
+            sets.run(op, (W + s) * n + j)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / K, wall * 1e3 / K
+
+
+def time_op(sets, op, K, reps=3):
+    """us per launch of one op: K launches back to back over rotating sets,
+    median over `reps` timed groups."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(sets.M):
+        sets.run(op, i)
+    out = []
+    for r in range(reps):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            sets.run(op, i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / K)
+    return float(np.median(out)), out
+
+
+def time_op_swept(sets, op, K, sweep):
+    """Isolated protocol: read sweep of 512 MiB, then events around one op."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(K + 2):
+        sweep.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sets.run(op, i)
+        e1.record(stream)
+        if i >= 2:
+            ms.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ms])) * 1e3
+
+
+def copy_ceiling(rn, dev, nbytes=1 << 30, reps=5):
+    """Streaming copy bandwidth over rotating buffers (read + write bytes)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(4)]
+    rn.copy(bufs[0], bufs[1])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        rn.copy(bufs[(2 * i) % 4], bufs[(2 * i + 1) % 4])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del bufs
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def cpu_baseline(arr, eps, budget_s=20.0):
     """The oracle as it stands, on the host cores, on a bounded row sample of
     the same workload; GB/s over the sample's algorithmic bytes."""
@@ -77,8 +217,7 @@ def cpu_baseline(arr, eps, budget_s=20.0):
     N, H = arr["x"].shape
     e = oracle.eps_at_boundary(eps)
     ef = oracle.eps_at_boundary(FUSED_EPS)
-    rows = N
-    # time one pass on a small sample first, then size the sample to budget
+
     def one_pass(n):
         t0 = time.perf_counter()
         x = orc.decode(arr["x"][:n], "bf16")
@@ -91,28 +230,30 @@ def cpu_baseline(arr, eps, budget_s=20.0):
         y, s = orc.rms_fwd(x, g, e)
         orc.encode(y, "bf16")
         y, h, s = orc.fused_add_rms_fwd(x, r, g, ef)
-        orc.encode(y, "bf16"); orc.encode(h, "bf16")
+        orc.encode(y, "bf16")
+        orc.encode(h, "bf16")
         dx, dg, db, _, _ = orc.ln_bwd(dy, x, g, e)
-        orc.encode(dx, "bf16"); orc.encode(dg, "bf16"); orc.encode(db, "bf16")
+        orc.encode(dx, "bf16")
+        orc.encode(dg, "bf16")
+        orc.encode(db, "bf16")
         dx, dg, _ = orc.rms_bwd(dy, x, g, e)
-        orc.encode(dx, "bf16"); orc.encode(dg, "bf16")
+        orc.encode(dx, "bf16")
+        orc.encode(dg, "bf16")
         return time.perf_counter() - t0
+
     probe_rows = min(N, 1024)
-    t_probe = one_pass(probe_rows)
-    per_row = t_probe / probe_rows
+    per_row = one_pass(probe_rows) / probe_rows
     rows = int(min(N, max(probe_rows, budget_s / 3.0 / max(per_row, 1e-9))))
-    times = [one_pass(rows) for _ in range(3)]
-    t = float(np.median(times))
+    t = float(np.median([one_pass(rows) for _ in range(3)]))
     nbytes = sum(alg_bytes(rows, H, 2).values())
     return {
         "value": nbytes / t / 1e9,
         "unit": "GB/s",
         "cores": orc.num_threads(),
         "kind": "oracle",
-        "sample": f"{rows} of {N} rows x H={H}, the full five-op step (bf16 "
+        "sample": f"{rows} of {N} rows x H={H}: the full five-op step (bf16 "
                   f"decode/encode included), median of 3 passes, "
                   f"{t * 1e3:.1f} ms per pass",
-        "ms_per_step_sample": t * 1e3,
     }
 
 
@@ -121,16 +262,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--warm-cache", action="store_true",
-                    help="no cache sweep between ops (back-to-back timing)")
+    ap.add_argument("--sets", type=int, default=6)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time each op isolated after a cache sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None,
-                    help="comma list of ops to run (profiling)")
+    ap.add_argument("--only", default=None, help="comma list of ops")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the path has no "
-              "multi-GPU component); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the row-normalization path has no "
+              "multi-GPU part in this build; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -148,114 +289,44 @@ def main():
     t0 = time.time()
     arr = synth.generate(w)
     log(f"inputs generated in {time.time() - t0:.1f}s")
-
-    def to_dev(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x, r, dy = to_dev(arr["x"]), to_dev(arr["residual"]), to_dev(arr["dy"])
-    g, b = to_dev(arr["gamma"]), to_dev(arr["beta"])
-    bf = torch.bfloat16
-    y = torch.empty((N, H), dtype=bf, device=dev)
-    y2 = torch.empty_like(y)
-    y3 = torch.empty_like(y)
-    hh = torch.empty_like(y)
-    dx = torch.empty_like(y)
-    dx2 = torch.empty_like(y)
-    mean = torch.empty(N, dtype=torch.float32, device=dev)
-    rstd = torch.empty_like(mean)
-    rstd2 = torch.empty_like(mean)
-    rstd3 = torch.empty_like(mean)
-    dg = torch.empty(H, dtype=bf, device=dev)
-    db = torch.empty_like(dg)
-    dg2 = torch.empty_like(dg)
-    ws_ln = torch.empty(rn.workspace_bytes(N, H, bf, True), dtype=torch.uint8, device=dev)
-    ws_rms = torch.empty(rn.workspace_bytes(N, H, bf, False), dtype=torch.uint8, device=dev)
-    sweep = torch.ones(128 << 20, dtype=torch.float32, device=dev)   # 512 MiB
-    stream = torch.cuda.current_stream()
-
-    ops = {
-        "ln_fwd": lambda: rn.ln_fwd(x, g, b, w.eps, y=y, mean=mean, rstd=rstd),
-        "rms_fwd": lambda: rn.rms_fwd(x, g, w.eps, y=y2, rstd=rstd2),
-        "fused_add_rms_fwd": lambda: rn.fused_add_rms_fwd(
-            x, r, g, FUSED_EPS, y=y3, h=hh, rstd=rstd3),
-        "ln_bwd": lambda: rn.ln_bwd(dy, x, g, mean, rstd, w.eps, dx=dx,
-                                    dgamma=dg, dbeta=db, workspace=ws_ln),
-        "rms_bwd": lambda: rn.rms_bwd(dy, x, g, rstd2, w.eps, dx=dx2,
-                                      dgamma=dg2, workspace=ws_rms),
-    }
-    names = list(ops) if not args.only else args.only.split(",")
+    sets = Sets(rn, arr, w.eps, args.sets, dev)
+    ops = list(OPS) if not args.only else args.only.split(",")
     nbytes = alg_bytes(N, H, 2)
-    ev = {k: [] for k in names}
 
-    def step(record):
-        for k in names:
-            if not args.warm_cache:
-                sweep.sum()           # read-only cache sweep (no dirty lines)
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                ops[k]()
-                e1.record(stream)
-                ev[k].append((e0, e1))
-            else:
-                ops[k]()
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
+    step_ms, wall_ms = time_steps(sets, ops, args.steps, args.warmup)
+    step_bytes = sum(nbytes[k] for k in ops)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    log(f"step: {step_ms * 1e3:.1f} us, {value:.0f} GB/s "
+        f"({100 * value / PEAK_GBS:.1f}% of peak)")
 
     per_op = {}
-    for k in names:
-        ms = np.array([a.elapsed_time(b_) for a, b_ in ev[k]])
-        med = float(np.median(ms))
-        per_op[k] = {
-            "us_median": med * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
-            "us_p90": float(np.percentile(ms, 90)) * 1e3,
-            "us_mean": float(ms.mean()) * 1e3,
-            "alg_bytes": nbytes[k],
-            "GBps": nbytes[k] / (med * 1e-3) / 1e9,
-        }
-        per_op[k]["pct_peak"] = 100.0 * per_op[k]["GBps"] / PEAK_GBS
-        log(f"{k:18s} {per_op[k]['us_median']:8.2f} us  "
-            f"{per_op[k]['GBps']:7.0f} GB/s  {per_op[k]['pct_peak']:5.1f}% of peak")
+    K = max(12, 2 * args.sets)
+    for k in ops:
+        us, reps = time_op(sets, k, K)
+        gbs = nbytes[k] / (us * 1e-6) / 1e9
+        per_op[k] = {"us": round(us, 3), "alg_bytes": nbytes[k],
+                     "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+        log(f"{k:18s} {us:8.2f} us  {gbs:7.0f} GB/s  {100 * gbs / PEAK_GBS:5.1f}% of peak")
+    if args.sweep:
+        sweep = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+        for k in ops:
+            us = time_op_swept(sets, k, 10, sweep)
+            per_op[k]["us_isolated_swept"] = round(us, 3)
+            log(f"{k:18s} isolated after sweep: {us:8.2f} us")
+        del sweep
 
-    step_ms = sum(float(np.mean([a.elapsed_time(b_) for a, b_ in ev[k]])) for k in names)
-    step_bytes = sum(nbytes[k] for k in names)
-    value = step_bytes / (step_ms * 1e-3) / 1e9
-
-    # streaming-copy ceiling (cold, 1 GiB -> 1 GiB), same sweep protocol
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    src.fill_(1)
-    cms = []
-    for i in range(6):
-        sweep.sum()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        rn.copy(src, dst)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        if i:
-            cms.append(e0.elapsed_time(e1))
-    copy_gbs = 2 * (1 << 30) / (float(np.median(cms)) * 1e-3) / 1e9
-    del src, dst
+    del sets
+    torch.cuda.empty_cache()
+    copy_gbs = copy_ceiling(rn, dev)
     log(f"copy ceiling {copy_gbs:.0f} GB/s ({100 * copy_gbs / PEAK_GBS:.1f}% of peak)")
 
-    # roofline: the op with the largest time share
-    dom = max(names, key=lambda k: per_op[k]["us_mean"])
-    achieved = nbytes[dom] / (per_op[dom]["us_mean"] * 1e-6) / 1e9
+    dom = max(ops, key=lambda k: per_op[k]["us"])
+    achieved = nbytes[dom] / (per_op[dom]["us"] * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
             "traffic": counters_traffic(dom, f"{N}x{H}"),
             "kernel": dom, "alg_bytes_per_launch": nbytes[dom],
-            "us_per_launch": round(per_op[dom]["us_mean"], 3)}
+            "us_per_launch": per_op[dom]["us"]}
 
     out = {
         "metric": "achieved HBM GB/s (% of peak) and us, LN/RMSNorm fwd+bwd bf16 32768x1024",
@@ -270,14 +341,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "N": N, "H": H,
-                   "ops": names, "cache": "warm" if args.warm_cache else "cold (512 MiB read sweep before each op)",
+        "config": {"workload": WORKLOAD, "N": N, "H": H, "ops": ops,
+                   "cache": f"cold: {args.sets} rotating tensor sets",
                    "parallelism": "single GPU"},
         "pct_peak": round(100.0 * value / PEAK_GBS, 2),
-        "per_op": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv
-                       for kk, vv in v.items()} for k, v in per_op.items()},
+        "per_op": per_op,
         "copy_ceiling_GBps": round(copy_gbs, 1),
-        "wall_ms_per_step_incl_sweeps": round(wall * 1e3 / args.steps, 4),
+        "wall_ms_per_step": round(wall_ms, 5),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -3,7 +3,7 @@
 
 namespace rn {
 int bwd_partials_f32(int64_t N, int H, bool vec, int cus) {
-    return bwd_partials_t<BwdPlansF32>(N, H, vec, cus);
+    return bwd_partials_t<float, BwdPlansF32>(N, H, vec, cus);
 }
 hipError_t launch_bwd_f32(bool ln, const BwdArgs &a, bool vec, int cus, int P,
                           void *dgamma, void *dbeta, hipStream_t s) {

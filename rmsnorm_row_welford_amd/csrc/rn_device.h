@@ -69,41 +69,37 @@ __device__ __forceinline__ void load_chunk(const bf16_bits *p, float *o) {
     }
 }
 
-template <int VEC, bool NT>
-__device__ __forceinline__ void store_chunk(float *p, const float *v) {
-    if constexpr (VEC == 4) {
-        f32x4 w = {v[0], v[1], v[2], v[3]};
-        if (NT) __builtin_nontemporal_store(w, (f32x4 *)p);
-        else *(f32x4 *)p = w;
-    } else {
-        static_assert(VEC == 1, "fp32 chunks are 4 or 1 elements");
-        if (NT) __builtin_nontemporal_store(v[0], p);
-        else *p = v[0];
-    }
-}
-template <int VEC, bool NT>
-__device__ __forceinline__ void store_chunk(bf16_bits *p, const float *v) {
-    if constexpr (VEC == 8) {
-        u32x4 w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
-        if (NT) __builtin_nontemporal_store(w, (u32x4 *)p);
-        else *(u32x4 *)p = w;
-    } else {
-        static_assert(VEC == 1, "bf16 chunks are 8 or 1 elements");
-        bf16_bits b = to_bf16(v[0]);
-        if (NT) __builtin_nontemporal_store(b, p);
-        else *p = b;
-    }
+// ------------------------------------------------------- buffer resources --
+// Row I/O goes through raw (untyped) buffer descriptors: a 128-bit SGPR
+// resource per row, a byte offset per lane in a VGPR.  The hardware range
+// check returns 0 for loads at or past `bytes` and drops such stores, so a
+// row's masked chunks need no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, GFX9-family format word
+constexpr int AUX_NT = 2;                // non-temporal hint
+// Cache-policy bits of the streaming row loads and of the row stores
+// (build-time tunable).
+#ifndef RN_LOAD_AUX
+#define RN_LOAD_AUX AUX_NT
+#endif
+#ifndef RN_STORE_AUX
+#define RN_STORE_AUX AUX_NT
+#endif
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes,
+                                             kRsrcWord3);
 }
 
 // One chunk kept in its storage form (bfloat16 stays packed two per
-// register) and widened to float32 on use; used for gamma/beta, which are
-// held in registers for a whole persistent loop.
+// register) and widened to float32 on use: gamma/beta for a whole
+// persistent loop, and the prefetched chunks of a team's next row.
 template <class T, int VEC> struct RawChunk;
 template <> struct RawChunk<bf16_bits, 8> {
     u32x4 v;
-    __device__ __forceinline__ void load(const bf16_bits *p) { v = *(const u32x4 *)p; }
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    }
     __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int k) const {
         return (k & 1) ? bf16_hi(v[k >> 1]) : bf16_lo(v[k >> 1]);
@@ -111,22 +107,63 @@ template <> struct RawChunk<bf16_bits, 8> {
 };
 template <> struct RawChunk<bf16_bits, 1> {
     unsigned v;
-    __device__ __forceinline__ void load(const bf16_bits *p) { v = *p; }
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+    }
     __device__ __forceinline__ void zero() { v = 0u; }
     __device__ __forceinline__ float get(int) const { return __uint_as_float(v << 16); }
 };
 template <> struct RawChunk<float, 4> {
     f32x4 v;
-    __device__ __forceinline__ void load(const float *p) { v = *(const f32x4 *)p; }
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    }
     __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ float get(int k) const { return v[k]; }
 };
 template <> struct RawChunk<float, 1> {
     float v;
-    __device__ __forceinline__ void load(const float *p) { v = *p; }
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
+    }
     __device__ __forceinline__ void zero() { v = 0.f; }
     __device__ __forceinline__ float get(int) const { return v; }
 };
+
+// Make a register value opaque to the optimizer (emits no instruction):
+// values widened from a packed chunk before this point are then widened
+// again after it instead of being kept live as float32 across a reduction.
+__device__ __forceinline__ void opaque(u32x4 &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(f32x4 &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(unsigned &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(float &v) { asm volatile("" : "+v"(v)); }
+
+// Store a chunk of VEC float32 values, rounded to the storage type, through
+// a buffer resource.
+template <int VEC>
+__device__ __forceinline__ void bstore_chunk(float *, rsrc_t r, int off, const float *v) {
+    if constexpr (VEC == 4) {
+        f32x4 w = {v[0], v[1], v[2], v[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), r, off, 0,
+                                               RN_STORE_AUX);
+    } else {
+        static_assert(VEC == 1, "fp32 chunks are 4 or 1 elements");
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[0]), r, off, 0,
+                                              RN_STORE_AUX);
+    }
+}
+template <int VEC>
+__device__ __forceinline__ void bstore_chunk(bf16_bits *, rsrc_t r, int off, const float *v) {
+    if constexpr (VEC == 8) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, RN_STORE_AUX);
+    } else {
+        static_assert(VEC == 1, "bf16 chunks are 8 or 1 elements");
+        __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v[0]), r, off, 0, RN_STORE_AUX);
+    }
+}
 
 // Store one float32 as the storage type.
 __device__ __forceinline__ void store_one(float *p, float v) { *p = v; }

@@ -5,12 +5,14 @@
 // VEC consecutive elements: chunk c covers elements [(c*64*TW + l)*VEC, +VEC),
 // so each chunk step of a wave is one fully coalesced 64 x 16-byte access.
 // The whole row stays in registers between the statistics and the output
-// pass, so every element is read from HBM once.  Chunks at or past H are
-// masked: they load as 0, contribute nothing, and are never stored.
+// pass, so every element is read from HBM once.  Rows are addressed through
+// buffer resources sized to the row: chunks at or past H load as 0 from the
+// hardware range check, contribute nothing, and their stores are dropped.
 //
 // Workgroups are persistent: the grid is capped near the number of resident
 // workgroups and each team strides over rows (grp = blockIdx.x, += gridDim.x;
-// row = grp*RT + team).  gamma/beta are loaded once per team into registers.
+// row = grp*RT + team).  gamma/beta are loaded once per team into registers,
+// and each team requests its next row before it works on the current one.
 //
 // Statistics (fp32 throughout):
 //  * LayerNorm works on x - pivot (pivot = the row's first element), so
@@ -27,12 +29,15 @@
 //
 // Backward.  Kernel 1 computes dx per row and accumulates dy*x_hat (and dy)
 // for its columns in float32 registers across all rows a team visits; at the
-// end the RT teams of a workgroup are merged through LDS in team order and
-// the workgroup writes ONE float32 partial row (two for LayerNorm).  The grid
+// end the RT teams of a workgroup are added column-wise through LDS in team
+// order and the workgroup writes ONE float32 partial row (two for
+// LayerNorm).  The grid
 // of kernel 1 is a small multiple of the CU count, so the partial buffer
 // does not grow with N.  Kernel 2 sums the partial rows column-wise in a
 // fixed order and rounds to the parameter type.
 #pragma once
+
+#include <atomic>
 
 #include "rn_device.h"
 #include "rn_internal.h"
@@ -68,6 +73,8 @@ struct Layout {
     __device__ __forceinline__ Layout(int tl, int H_) : base(tl * VEC), H(H_) {}
     __device__ __forceinline__ int off(int c) const { return c * STEP + base; }
     __device__ __forceinline__ bool valid(int c) const { return off(c) < H; }
+    template <class T>
+    __device__ __forceinline__ int boff(int c) const { return off(c) * (int)sizeof(T); }
 
     // Number of valid elements held by wave w of the team.
     __device__ static __forceinline__ int wave_count(int w, int H) {
@@ -82,44 +89,37 @@ struct Layout {
     }
 };
 
-template <class T, int VEC, int CPL, int TW, bool NT>
-__device__ __forceinline__ void load_row(const T *row, const Layout<VEC, CPL, TW> &L,
-                                         float *v) {
+// Row I/O through a buffer resource covering exactly the row's H elements:
+// chunks past the row load as 0 and are not stored.
+template <class T>
+__device__ __forceinline__ rsrc_t row_rsrc(const T *row, int H) {
+    return make_rsrc(row, (uint32_t)H * (uint32_t)sizeof(T));
+}
+
+template <int AUX, class T, int VEC, int CPL, int TW>
+__device__ __forceinline__ void load_raw_row(rsrc_t r, const Layout<VEC, CPL, TW> &L,
+                                             RawChunk<T, VEC> *v) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        if (L.valid(c)) {
-            load_chunk<VEC, NT>(row + L.off(c), v + c * VEC);
-        } else {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) v[c * VEC + k] = 0.0f;
-        }
-    }
+    for (int c = 0; c < CPL; ++c) v[c].template bload<AUX>(r, L.template boff<T>(c));
 }
 
 template <class T, int VEC, int CPL, int TW>
-__device__ __forceinline__ void load_raw_row(const T *row, const Layout<VEC, CPL, TW> &L,
-                                             RawChunk<T, VEC> *v) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        if (L.valid(c)) v[c].load(row + L.off(c));
-        else v[c].zero();
-    }
-}
-
-template <class T, int VEC, int CPL, int TW, bool NT>
-__device__ __forceinline__ void store_row(T *row, const Layout<VEC, CPL, TW> &L,
+__device__ __forceinline__ void store_row(rsrc_t r, const Layout<VEC, CPL, TW> &L,
                                           const float *v) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-        if (L.valid(c)) store_chunk<VEC, NT>(row + L.off(c), v + c * VEC);
+        bstore_chunk<VEC>((T *)nullptr, r, L.template boff<T>(c), v + c * VEC);
 }
 
 // ----------------------------------------------------------------- forward --
-template <class T, int VEC, int CPL, int TW, int RT, int OP>
+template <class T, int VEC, int CPL, int TW, int RT, int OP, bool PF>
 __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
+    using Raw = RawChunk<T, VEC>;
     constexpr int E = Lay::E;
     constexpr int NV = (OP == OP_LN) ? 2 : 1;
+    constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;   // row inputs: x [, residual]
+    constexpr bool PIVOT_LOAD = (OP == OP_LN) && (TW > 1);
     __shared__ float red[(TW > 1) ? 2 * RT * TW * NV : 1];
 
     const int lane = threadIdx.x & 63;
@@ -129,11 +129,11 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
     const int H = a.H;
     const Lay L(wit * 64 + lane, H);
 
-    RawChunk<T, VEC> g[CPL];
-    load_raw_row<T, VEC, CPL, TW>((const T *)a.gamma, L, g);
-    RawChunk<T, VEC> bt[(OP == OP_LN) ? CPL : 1];
+    Raw g[CPL];
+    load_raw_row<0>(row_rsrc((const T *)a.gamma, H), L, g);
+    Raw bt[(OP == OP_LN) ? CPL : 1];
     if constexpr (OP == OP_LN) {
-        if (a.beta != nullptr) load_raw_row<T, VEC, CPL, TW>((const T *)a.beta, L, bt);
+        if (a.beta != nullptr) load_raw_row<0>(row_rsrc((const T *)a.beta, H), L, bt);
         else
 #pragma unroll
             for (int c = 0; c < CPL; ++c) bt[c].zero();
@@ -151,7 +151,34 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
         n_lane = lane < TW ? (float)Lay::wave_count(lane, H) : 0.0f;
     }
 
+    const T *xb = (const T *)a.x;
+    const T *rb = (const T *)a.res;
     const int64_t N = a.N;
+    const int64_t step = (int64_t)gridDim.x * RT;
+
+    // Software pipeline (PF): the raw chunks of the team's NEXT row (and, for
+    // multi-wave LayerNorm, its pivot element) are requested before the
+    // current row is reduced and written, so HBM reads stay in flight
+    // across the reductions.  Without PF each row is fetched when its turn
+    // comes and latency is hidden by occupancy alone.
+    Raw cur[NIN][CPL], nxt[NIN][PF ? CPL : 1];
+    float pcur = 0.0f, pnxt = 0.0f;
+    auto fetch = [&](int64_t row, auto &dst, float &piv) {
+        if (row < N) {
+            load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, dst[0]);
+            if constexpr (OP == OP_FUSED)
+                load_raw_row<RN_LOAD_AUX>(row_rsrc(rb + row * a.ldr, H), L, dst[1]);
+            if constexpr (PIVOT_LOAD) load_chunk<1, false>(xb + row * a.ldx, &piv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NIN; ++i)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) dst[i][c].zero();
+            piv = 0.0f;
+        }
+    };
+    if constexpr (PF) fetch((int64_t)blockIdx.x * RT + team, cur, pcur);
+
     int parity = 0;
     for (int64_t grp = blockIdx.x; grp * RT < N; grp += gridDim.x) {
         const int64_t row = grp * RT + team;
@@ -159,29 +186,21 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
         if constexpr (TW == 1) {
             if (!active) break;
         }
+        if constexpr (PF) fetch(row + step, nxt, pnxt);
+        else fetch(row, cur, pcur);
+
         float v[E];
-        if constexpr (OP == OP_FUSED) {
-            float r[E];
-            if (active) {
-                load_row<T, VEC, CPL, TW, true>((const T *)a.x + row * a.ldx, L, v);
-                load_row<T, VEC, CPL, TW, true>((const T *)a.res + row * a.ldr, L, r);
-            } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) v[e] = r[e] = 0.0f;
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                v[c * VEC + k] = cur[0][c].get(k);
+                if constexpr (OP == OP_FUSED) v[c * VEC + k] += cur[1][c].get(k);
             }
-#pragma unroll
-            for (int e = 0; e < E; ++e) v[e] += r[e];
-            // h is written back in the same pass, before y; every element of
-            // this lane was loaded above, so h may alias x or the residual.
-            if (active) store_row<T, VEC, CPL, TW, false>((T *)a.h + row * a.ldh, L, v);
-        } else {
-            if (active) {
-                load_row<T, VEC, CPL, TW, true>((const T *)a.x + row * a.ldx, L, v);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) v[e] = 0.0f;
-            }
-        }
+        // h is written back in the same pass, before y; every element of
+        // this lane was loaded before, so h may alias x or the residual.
+        if constexpr (OP == OP_FUSED)
+            if (active) store_row<T>(row_rsrc((T *)a.h + row * a.ldh, H), L, v);
 
         float mean = 0.0f, var;
         if constexpr (OP == OP_LN) {
@@ -191,12 +210,8 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
             // itself would otherwise dominate x - mean.  v becomes x - pivot
             // on valid elements and 0 on masked ones.
             float pivot;
-            if constexpr (TW == 1) {
-                pivot = lane_value(v[0], 0);
-            } else {
-                pivot = 0.0f;
-                if (active) load_chunk<1, false>((const T *)a.x + row * a.ldx, &pivot);
-            }
+            if constexpr (TW == 1) pivot = lane_value(v[0], 0);
+            else pivot = pcur;
             float s = 0.0f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
@@ -271,7 +286,7 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
                 else
                     out[e] = (v[e] * rstd) * ge;
             }
-            store_row<T, VEC, CPL, TW, false>((T *)a.y + row * a.ldy, L, out);
+            store_row<T>(row_rsrc((T *)a.y + row * a.ldy, H), L, out);
             if (wit == 0 && lane == 0) {
                 if constexpr (OP == OP_LN) {
                     if (a.mean) a.mean[row] = mean;
@@ -279,17 +294,25 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
                 if (a.rstd) a.rstd[row] = rstd;
             }
         }
+        if constexpr (PF) {
+#pragma unroll
+            for (int i = 0; i < NIN; ++i)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) cur[i][c] = nxt[i][c];
+            pcur = pnxt;
+        }
     }
 }
 
 // ---------------------------------------------------------------- backward --
-template <class T, int VEC, int CPL, int TW, int RT, bool LN>
+template <class T, int VEC, int CPL, int TW, int RT, bool LN, bool PF>
 __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
+    using Raw = RawChunk<T, VEC>;
     constexpr int E = Lay::E;
     constexpr int NV = LN ? 2 : 1;
     __shared__ float red[(TW > 1) ? 2 * RT * TW * NV : 1];
-    extern __shared__ float accbuf[];   // RT > 1: NV * H floats
+    extern __shared__ f32x4 acc_lds[];   // RT > 1: RT * H floats
 
     const int lane = threadIdx.x & 63;
     const int wave = wave_id_uniform();
@@ -298,8 +321,8 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     const int H = a.H;
     const Lay L(wit * 64 + lane, H);
 
-    RawChunk<T, VEC> g[CPL];
-    load_raw_row<T, VEC, CPL, TW>((const T *)a.gamma, L, g);
+    Raw g[CPL];
+    load_raw_row<0>(row_rsrc((const T *)a.gamma, H), L, g);
     float adg[E], adb[LN ? E : 1];
 #pragma unroll
     for (int e = 0; e < E; ++e) adg[e] = 0.0f;
@@ -308,7 +331,34 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
         for (int e = 0; e < E; ++e) adb[e] = 0.0f;
     }
 
+    const T *xb = (const T *)a.x;
+    const T *dyb = (const T *)a.dy;
     const int64_t N = a.N;
+    const int64_t step = (int64_t)gridDim.x * RT;
+
+    // x and dy stay in their storage form (bf16: two per register); x_hat
+    // and g are formed from them once for the sums and once more for dx.
+    // With PF the next row's chunks and statistics are requested before the
+    // current row is worked on.
+    Raw cx[CPL], cdy[CPL], nx[PF ? CPL : 1], ndy[PF ? CPL : 1];
+    float cmu = 0.0f, cs = 0.0f, nmu = 0.0f, ns = 0.0f;
+    auto fetch = [&](int64_t row, auto &x_, auto &dy_, float &mu_, float &s_) {
+        if (row < N) {
+            load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, x_);
+            load_raw_row<RN_LOAD_AUX>(row_rsrc(dyb + row * a.lddy, H), L, dy_);
+            mu_ = LN ? a.mean[row] : 0.0f;
+            s_ = a.rstd[row];
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                x_[c].zero();
+                dy_[c].zero();
+            }
+            mu_ = s_ = 0.0f;
+        }
+    };
+    if constexpr (PF) fetch((int64_t)blockIdx.x * RT + team, cx, cdy, cmu, cs);
+
     int parity = 0;
     for (int64_t grp = blockIdx.x; grp * RT < N; grp += gridDim.x) {
         const int64_t row = grp * RT + team;
@@ -316,31 +366,24 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
         if constexpr (TW == 1) {
             if (!active) break;
         }
-        float xh[E], gg[E];
-        float mu = 0.0f, s = 0.0f;
-        if (active) {
-            load_row<T, VEC, CPL, TW, true>((const T *)a.x + row * a.ldx, L, xh);
-            load_row<T, VEC, CPL, TW, true>((const T *)a.dy + row * a.lddy, L, gg);
-            if constexpr (LN) mu = a.mean[row];
-            s = a.rstd[row];
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) xh[e] = gg[e] = 0.0f;
-        }
+        if constexpr (PF) fetch(row + step, nx, ndy, nmu, ns);
+        else fetch(row, cx, cdy, cmu, cs);
+
         // Masked elements have dy = 0, so they add nothing below.
         float sg = 0.0f, sgx = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float dyv = gg[e];
-            const float xhat = (xh[e] - mu) * s;
-            const float gv = dyv * g[e / VEC].get(e % VEC);
-            adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
-            if constexpr (LN) adb[e] += dyv;
-            sg += gv;
-            sgx = __builtin_fmaf(gv, xhat, sgx);
-            xh[e] = xhat;
-            gg[e] = gv;
-        }
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const int e = c * VEC + k;
+                const float dyv = cdy[c].get(k);
+                const float xhat = (cx[c].get(k) - cmu) * cs;
+                const float gv = dyv * g[c].get(k);
+                adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
+                if constexpr (LN) adb[e] += dyv;
+                sg += gv;
+                sgx = __builtin_fmaf(gv, xhat, sgx);
+            }
         if constexpr (LN) wave_sum2(sg, sgx);
         else sgx = wave_sum(sgx);
         if constexpr (TW > 1) {
@@ -362,22 +405,41 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
         const float c1 = LN ? sg * a.inv_H : 0.0f;
         const float c2 = sgx * a.inv_H;
         if (active) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                opaque(cx[c].v);
+                opaque(cdy[c].v);
+            }
             float dx[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float t = gg[e];
-                if constexpr (LN) t -= c1;
-                dx[e] = __builtin_fmaf(-xh[e], c2, t) * s;
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float xhat = (cx[c].get(k) - cmu) * cs;
+                    float t = cdy[c].get(k) * g[c].get(k);
+                    if constexpr (LN) t -= c1;
+                    dx[c * VEC + k] = __builtin_fmaf(-xhat, c2, t) * cs;
+                }
+            store_row<T>(row_rsrc((T *)a.dx + row * a.lddx, H), L, dx);
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                cx[c] = nx[c];
+                cdy[c] = ndy[c];
             }
-            store_row<T, VEC, CPL, TW, false>((T *)a.dx + row * a.lddx, L, dx);
+            cmu = nmu;
+            cs = ns;
         }
     }
 
-    // One partial row per workgroup (two for LayerNorm), teams merged in
-    // order 0, 1, ..., RT-1.
-    float *pg = a.part + (int64_t)blockIdx.x * H;
-    float *pb = a.part + ((int64_t)gridDim.x + blockIdx.x) * H;
+    // One partial row per workgroup and parameter: row blockIdx.x holds the
+    // dgamma partial, row gridDim.x + blockIdx.x the dbeta partial.  With
+    // several teams, each team parks its accumulators in LDS and every
+    // thread then adds a column over the teams in team order.
     if constexpr (RT == 1) {
+        float *pg = a.part + (int64_t)blockIdx.x * H;
+        float *pb = a.part + ((int64_t)gridDim.x + blockIdx.x) * H;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             if (!L.valid(c)) continue;
@@ -385,90 +447,148 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
             if constexpr (LN) store_f32s<VEC>(pb + L.off(c), adb + c * VEC);
         }
     } else {
-        for (int t = 0; t < RT; ++t) {
-            if (team == t) {
+        float *accbuf = (float *)acc_lds;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    if (!L.valid(c)) continue;
-                    float vg[VEC], vb[VEC];
+        for (int p = 0; p < NV; ++p) {
+            const float *acc = adg;
+            if constexpr (LN) acc = p == 0 ? adg : adb;
 #pragma unroll
-                    for (int k = 0; k < VEC; ++k) {
-                        const int col = L.off(c) + k;
-                        vg[k] = t > 0 ? accbuf[col] + adg[c * VEC + k] : adg[c * VEC + k];
-                        if constexpr (LN)
-                            vb[k] = t > 0 ? accbuf[H + col] + adb[c * VEC + k]
-                                          : adb[c * VEC + k];
-                    }
-                    if (t < RT - 1) {
+            for (int c = 0; c < CPL; ++c)
+                if (L.valid(c)) store_f32s<VEC>(accbuf + team * H + L.off(c), acc + c * VEC);
+            __syncthreads();
+            float *dst = a.part + ((int64_t)p * gridDim.x + blockIdx.x) * H;
+            for (int col = threadIdx.x; col < H; col += 64 * TW * RT) {
+                float t = accbuf[col];
 #pragma unroll
-                        for (int k = 0; k < VEC; ++k) {
-                            accbuf[L.off(c) + k] = vg[k];
-                            if constexpr (LN) accbuf[H + L.off(c) + k] = vb[k];
-                        }
-                    } else {
-                        store_f32s<VEC>(pg + L.off(c), vg);
-                        if constexpr (LN) store_f32s<VEC>(pb + L.off(c), vb);
-                    }
-                }
+                for (int tm = 1; tm < RT; ++tm) t += accbuf[tm * H + col];
+                dst[col] = t;
             }
-            if (t < RT - 1) __syncthreads();
+            if (p + 1 < NV) __syncthreads();
         }
     }
 }
 
-// Kernel 2: column sums of the partial rows.  Block (64 columns x 16
-// waves); wave w adds rows w, w+16, ... of its 64 columns in increasing
-// order, then the 16 wave sums are added in wave order.  blockIdx.y picks
-// dgamma (0) or dbeta (1).
-template <class T>
+// Kernel 2: column sums of the partial rows.  A workgroup of 1024 threads
+// owns COLS columns; its lanes form (1024 / COLS) row slots, slot j adding
+// the contiguous block of rows [j*R, (j+1)*R) (R = ceil(P / slots)) in
+// increasing order with up to 32 loads in flight, after which the slot sums
+// are added in slot order.  blockIdx.y picks dgamma (0) or dbeta (1).
+// Narrow tiles spread short rows over more CUs; wide rows use 64 columns
+// (256-byte segments per partial row).
+template <class T, int COLS>
 __global__ __launch_bounds__(1024) void bwd2_kernel(const float *part, int P,
                                                    int H, T *dgamma, T *dbeta) {
-    __shared__ float red[16][64];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + lane;
-    const float *base = part + (int64_t)blockIdx.y * P * H;
+    constexpr int SLOTS = 1024 / COLS;
+    __shared__ float red[SLOTS][COLS];
+    const int cl = threadIdx.x % COLS;
+    const int slot = threadIdx.x / COLS;
+    const int col = blockIdx.x * COLS + cl;
+    const int R = (P + SLOTS - 1) / SLOTS;
+    const int p0 = slot * R;
+    const int p1 = p0 + R < P ? p0 + R : P;
     float s = 0.0f;
     if (col < H) {
-        int p = wave;
-#pragma unroll 8
-        for (; p < P; p += 16) s += base[(int64_t)p * H + col];
-    }
-    red[wave][lane] = s;
-    __syncthreads();
-    if (wave == 0 && col < H) {
-        float t = red[0][lane];
+        const float *base = part + (int64_t)blockIdx.y * P * H + col;
+        for (int p = p0; p < p1; p += 32) {
+            float v[32];
 #pragma unroll
-        for (int w = 1; w < 16; ++w) t += red[w][lane];
+            for (int k = 0; k < 32; ++k)
+                v[k] = (p + k < p1) ? base[(int64_t)(p + k) * H] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) s += v[k];
+        }
+    }
+    red[slot][cl] = s;
+    __syncthreads();
+    if (slot == 0 && col < H) {
+        float t = red[0][cl];
+        for (int j = 1; j < SLOTS; ++j) t += red[j][cl];
         store_one(blockIdx.y == 0 ? dgamma + col : dbeta + col, t);
     }
 }
 
+#ifndef RN_K2_WIDE_H
+#define RN_K2_WIDE_H 4096   // rows at least this long use 64-column tiles
+#endif
+
+template <class T>
+hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void *db,
+                       hipStream_t s) {
+    if (H >= RN_K2_WIDE_H)
+        hipLaunchKernelGGL((bwd2_kernel<T, 64>), dim3((H + 63) / 64, ln ? 2 : 1),
+                           dim3(1024), 0, s, part, P, H, (T *)dg, (T *)db);
+    else
+        hipLaunchKernelGGL((bwd2_kernel<T, 32>), dim3((H + 31) / 32, ln ? 2 : 1),
+                           dim3(1024), 0, s, part, P, H, (T *)dg, (T *)db);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ plans --
 // A plan is <VEC, CPL, TW, RT>; rows up to 64*TW*VEC*CPL elements.
-template <int VEC_, int CPL_, int TW_, int RT_>
+template <int VEC_, int CPL_, int TW_, int RT_, bool PF_ = true>
 struct Plan {
     static constexpr int VEC = VEC_, CPL = CPL_, TW = TW_, RT = RT_;
+    static constexpr bool PF = PF_;   // prefetch the next row into registers
     static constexpr int SPAN = 64 * TW_ * VEC_ * CPL_;
     static constexpr int THREADS = 64 * TW_ * RT_;
 };
 
-// Persistent grid: enough workgroups for `waves_per_cu` resident waves per
-// CU, never more than there are row groups.
+// Workgroups of kernel K (with `threads` threads and `lds` bytes of dynamic
+// LDS) that can be resident on one CU at once, from the runtime's occupancy
+// calculator (register, LDS and wave-slot limits); cached per kernel and
+// LDS size in one atomic word.
+template <auto K>
+inline int resident_per_cu(int threads, int lds) {
+    static std::atomic<int64_t> cache{-1};
+    const int64_t c = cache.load(std::memory_order_relaxed);
+    if (c >= 0 && (c >> 16) == lds) return (int)(c & 0xffff);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, K, threads, lds) != hipSuccess ||
+        n < 1)
+        n = 1;
+    cache.store(((int64_t)lds << 16) | (n & 0xffff), std::memory_order_relaxed);
+    return n;
+}
+
+// Persistent grid: `per_cu` workgroups per CU, never more than there are
+// row groups (and, with RN_..._MIN_ROWS > 1, at least that many rows per
+// team).
 template <class P>
-inline int persistent_grid(int64_t N, int cus, int waves_per_cu) {
-    const int64_t groups = (N + P::RT - 1) / P::RT;
-    int64_t per_cu = waves_per_cu / (P::TW * P::RT);
+inline int persistent_grid(int64_t N, int cus, int per_cu, int min_rows) {
+    int64_t groups = (N + P::RT - 1) / P::RT;
+    groups = (groups + min_rows - 1) / min_rows;
     if (per_cu < 1) per_cu = 1;
-    const int64_t cap = per_cu * cus;
+    const int64_t cap = (int64_t)per_cu * cus;
     return (int)(groups < cap ? groups : cap);
 }
 
+// Build-time launch tuning (0 = the default rule): forward workgroups per
+// CU, backward workgroups per CU, and the minimum rows each backward team
+// of the multi-wave (wide-row) plans folds into its partial row.
+#ifndef RN_FWD_PER_CU
+#define RN_FWD_PER_CU 0
+#endif
+#ifndef RN_BWD_PER_CU
+#define RN_BWD_PER_CU 0
+#endif
+#ifndef RN_BWD_MIN_ROWS_WIDE
+#define RN_BWD_MIN_ROWS_WIDE 1
+#endif
+
+// Forward grid.  When at least two workgroups fit on a CU, one workgroup
+// per row group (no persistence): the dispatcher refills CUs as rows
+// finish, which streams better than a persistent loop.  When only one fits
+// (1024-thread rows), a persistent grid of one workgroup per CU whose teams
+// prefetch their next row.
 template <class T, class P, int OP>
 hipError_t launch_fwd_plan(const FwdArgs &a, int cus, hipStream_t s) {
-    const int grid = persistent_grid<P>(a.N, cus, 32);
-    hipLaunchKernelGGL((fwd_kernel<T, P::VEC, P::CPL, P::TW, P::RT, OP>),
-                       dim3(grid), dim3(P::THREADS), 0, s, a);
+    constexpr auto k = fwd_kernel<T, P::VEC, P::CPL, P::TW, P::RT, OP, P::PF>;
+    const int resident = resident_per_cu<k>(P::THREADS, 0);
+    const int per_cu = RN_FWD_PER_CU > 0 ? RN_FWD_PER_CU
+                       : resident >= 2   ? (1 << 20)
+                                         : resident;
+    const int grid = persistent_grid<P>(a.N, cus, per_cu, 1);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(P::THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -481,31 +601,33 @@ hipError_t launch_fwd_op(int op, const FwdArgs &a, int cus, hipStream_t s) {
     }
 }
 
-// Backward: kernel 1 partial-row count for a plan.
-template <class P>
-inline int bwd_grid(int64_t N, int cus) {
-    // 16 resident waves per CU: two 512-thread or one 1024-thread
-    // workgroup(s) per CU, i.e. P = 2*CUs or 1*CUs partial rows.
-    return persistent_grid<P>(N, cus, 16);
+// Backward: kernel 1's workgroup count, i.e. the number of partial rows P.
+// The LayerNorm kernel has the larger footprint, so both norms use its
+// occupancy, which keeps the workspace size independent of the norm.
+template <class T, class P>
+inline int bwd_grid(int64_t N, int H, int cus) {
+    const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
+    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true, P::PF>;
+    const int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU
+                                         : resident_per_cu<k>(P::THREADS, lds);
+    return persistent_grid<P>(N, cus, per_cu, P::TW > 1 ? RN_BWD_MIN_ROWS_WIDE : 1);
 }
 
 template <class T, class P>
 hipError_t launch_bwd_plan(bool ln, const BwdArgs &a, int P_, void *dg,
                            void *db, hipStream_t s) {
     if (P_ > 0) {
-        const int lds = P::RT > 1 ? (ln ? 2 : 1) * a.H * (int)sizeof(float) : 0;
+        const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
         if (ln)
-            hipLaunchKernelGGL((bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true>),
+            hipLaunchKernelGGL((bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true, P::PF>),
                                dim3(P_), dim3(P::THREADS), lds, s, a);
         else
-            hipLaunchKernelGGL((bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, false>),
+            hipLaunchKernelGGL((bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, false, P::PF>),
                                dim3(P_), dim3(P::THREADS), lds, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd2_kernel<T>), dim3((a.H + 63) / 64, ln ? 2 : 1),
-                       dim3(1024), 0, s, a.part, P_, a.H, (T *)dg, (T *)db);
-    return hipGetLastError();
+    return launch_bwd2<T>(a.part, P_, a.H, ln, dg, db, s);
 }
 
 }  // namespace rn

@@ -33,13 +33,37 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
     return pick_plan_int(PlanList<Ps...>{}, H, f);
 }
 
+// The bf16 plans for the benchmarked row lengths can be overridden at
+// build time (-DRN_FWD_BF16_1024=... etc.) to sweep team shapes.
+#ifndef RN_FWD_BF16_1024
+#define RN_FWD_BF16_1024 Plan<8, 2, 1, 4>
+#endif
+#ifndef RN_FWD_BF16_2048
+#define RN_FWD_BF16_2048 Plan<8, 4, 1, 4>
+#endif
+#ifndef RN_FWD_BF16_4096
+#define RN_FWD_BF16_4096 Plan<8, 2, 4, 1>
+#endif
+#ifndef RN_FWD_BF16_16384
+#define RN_FWD_BF16_16384 Plan<8, 2, 16, 1>
+#endif
+#ifndef RN_BWD_BF16_1024
+#define RN_BWD_BF16_1024 Plan<8, 2, 1, 8>
+#endif
+#ifndef RN_BWD_BF16_2048
+#define RN_BWD_BF16_2048 Plan<8, 2, 2, 4>
+#endif
+#ifndef RN_BWD_BF16_16384
+#define RN_BWD_BF16_16384 Plan<8, 2, 16, 1>
+#endif
+
 // ------------------------------------------------------------- forward --
 using FwdPlansBf16 = PlanList<Plan<8, 1, 1, 4>,     //   512
-                              Plan<8, 2, 1, 4>,     //  1024
-                              Plan<8, 4, 1, 4>,     //  2048
-                              Plan<8, 2, 4, 1>,     //  4096
+                              RN_FWD_BF16_1024,     //  1024
+                              RN_FWD_BF16_2048,     //  2048
+                              RN_FWD_BF16_4096,     //  4096
                               Plan<8, 2, 8, 1>,     //  8192
-                              Plan<8, 2, 16, 1>>;   // 16384
+                              RN_FWD_BF16_16384>;   // 16384
 using FwdPlansF32 = PlanList<Plan<4, 1, 1, 4>,      //   256
                              Plan<4, 2, 1, 4>,      //   512
                              Plan<4, 4, 1, 4>,      //  1024
@@ -55,18 +79,19 @@ using FwdPlansScalar = PlanList<Plan<1, 1, 1, 4>,   //    64
 
 // ------------------------------------------------------------ backward --
 using BwdPlansBf16 = PlanList<Plan<8, 1, 1, 8>,     //   512
-                              Plan<8, 2, 1, 8>,     //  1024
-                              Plan<8, 2, 2, 4>,     //  2048
+                              RN_BWD_BF16_1024,     //  1024
+                              RN_BWD_BF16_2048,     //  2048
                               Plan<8, 2, 4, 2>,     //  4096
                               Plan<8, 2, 8, 1>,     //  8192
-                              Plan<8, 2, 16, 1>>;   // 16384
-using BwdPlansF32 = PlanList<Plan<4, 1, 1, 8>,      //   256
-                             Plan<4, 2, 1, 8>,      //   512
-                             Plan<4, 4, 1, 8>,      //  1024
-                             Plan<4, 4, 2, 4>,      //  2048
-                             Plan<4, 4, 4, 2>,      //  4096
-                             Plan<4, 4, 8, 1>,      //  8192
-                             Plan<4, 4, 16, 1>>;    // 16384
+                              RN_BWD_BF16_16384>;   // 16384
+// float32 rows of 16 elements per lane are too wide to double-buffer.
+using BwdPlansF32 = PlanList<Plan<4, 1, 1, 8>,             //   256
+                             Plan<4, 2, 1, 8>,             //   512
+                             Plan<4, 4, 1, 8, false>,      //  1024
+                             Plan<4, 4, 2, 4, false>,      //  2048
+                             Plan<4, 4, 4, 2, false>,      //  4096
+                             Plan<4, 4, 8, 1, false>,      //  8192
+                             Plan<4, 4, 16, 1, false>>;    // 16384
 using BwdPlansScalar = PlanList<Plan<1, 1, 1, 8>,   //    64
                                 Plan<1, 4, 1, 8>,   //   256
                                 Plan<1, 4, 4, 2>,   //  1024
@@ -81,9 +106,9 @@ hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
                : pick_plan(FwdPlansScalar{}, a.H, f);
 }
 
-template <class VecPlans>
+template <class T, class VecPlans>
 int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
-    auto f = [&]<class P>() { return bwd_grid<P>(N, cus); };
+    auto f = [&]<class P>() { return bwd_grid<T, P>(N, H, cus); };
     return vec ? pick_plan_int(VecPlans{}, H, f)
                : pick_plan_int(BwdPlansScalar{}, H, f);
 }
