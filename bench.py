@@ -22,8 +22,6 @@ value = the step's algorithmic HBM bytes / ms_per_step.  Prints ONE JSON line
 on stdout (diagnostics go to stderr).  One GPU only.
 """
 import argparse
-import glob
-import hashlib
 import json
 import os
 import sys
@@ -55,13 +53,6 @@ def alg_bytes(N, H, e):
     }
 
 
-def kernel_source_digest():
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "rmsnorm_row_welford_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
-
-
 def counters_traffic(op, shape_tag):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources (else None)."""
@@ -72,6 +63,7 @@ def counters_traffic(op, shape_tag):
         d = json.load(open(path))
     except Exception:
         return None
+    from rmsnorm_row_welford_amd.profsum import kernel_source_digest
     if d.get("kernel_source_digest") != kernel_source_digest():
         return None
     return d.get("traffic_bytes_per_launch")

@@ -1,12 +1,35 @@
-"""Summarize rocprofv3 output (a rocpd SQLite database from --kernel-trace,
-or one from a --pmc counter run) into the short text tables kept under
-profiles/.
+"""Summaries of rocprofv3 output for profiles/.
 
-  python -m rmsnorm_row_welford_amd.profsum trace <run_results.db> [title...]
-  python -m rmsnorm_row_welford_amd.profsum pmc <run_results.db> [title...]
+  python -m rmsnorm_row_welford_amd.profsum trace <results.db> [title...]
+      per-kernel call count and average/min/max duration (us) from a
+      --kernel-trace database.
+  python -m rmsnorm_row_welford_amd.profsum pmc <results.db> [title...]
+      per-kernel average counter value per dispatch from a --pmc database.
+  python -m rmsnorm_row_welford_amd.profsum traffic <fetch.db> <write.db>
+         <kernel-substring> <out.json> [calib-substring calib-bytes]
+      HBM bytes per launch of one kernel from a FETCH_SIZE run and a
+      WRITE_SIZE run (both KiB per dispatch), each scaled by what the same
+      counter reads for the streaming copy kernel of known size
+      (rn::copy16_kernel moving `calib-bytes` each way); written as JSON with
+      a digest of the kernel sources it was measured on.
 """
+import glob
+import hashlib
+import json
+import os
 import sqlite3
 import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources (csrc/*): counter figures are only valid
+    for the kernels they were taken on."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def kernel_table(db: str):
@@ -24,23 +47,69 @@ def kernel_table(db: str):
     return out
 
 
-def pmc_table(db: str):
-    """Per kernel name: counter -> average value per dispatch."""
+def _pmc_rows(db: str):
     c = sqlite3.connect(db)
     cols = [r[1] for r in c.execute("pragma table_info(counters_collection)")]
     name_col = "kernel_name" if "kernel_name" in cols else "name"
     q = (f"select {name_col}, counter_name, count(distinct dispatch_id), "
          f"sum(value) / count(distinct dispatch_id) from counters_collection "
-         f"group by {name_col}, counter_name order by {name_col}, counter_name")
+         f"group by {name_col}, counter_name")
+    return list(c.execute(q))
+
+
+def pmc_table(db: str):
     out = [f"{'kernel':90s} {'counter':>14s} {'dispatches':>10s} {'avg_per_dispatch':>18s}"]
-    for name, cn, nd, v in c.execute(q):
+    for name, cn, nd, v in sorted(_pmc_rows(db)):
         short = name if len(name) <= 90 else name[:87] + "..."
         out.append(f"{short:90s} {cn:>14s} {nd:10d} {v:18.1f}")
     return out
 
 
+def _counter(db, counter, substr):
+    vals = [(n, nd, v) for n, cn, nd, v in _pmc_rows(db)
+            if cn == counter and substr in n]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {substr!r} in {db}")
+    tot_d = sum(nd for _, nd, _ in vals)
+    return sum(nd * v for _, nd, v in vals) / tot_d, tot_d
+
+
+def traffic(fetch_db, write_db, substr, out_json, calib="copy16_kernel",
+            calib_bytes=1 << 30):
+    f_k, nf = _counter(fetch_db, "FETCH_SIZE", substr)
+    w_k, nw = _counter(write_db, "WRITE_SIZE", substr)
+    f_c, _ = _counter(fetch_db, "FETCH_SIZE", calib)
+    w_c, _ = _counter(write_db, "WRITE_SIZE", calib)
+    f_scale = calib_bytes / f_c        # bytes per counter unit
+    w_scale = calib_bytes / w_c
+    d = {
+        "kernel_substring": substr,
+        "dispatches": {"fetch": nf, "write": nw},
+        "FETCH_SIZE_per_dispatch": f_k,
+        "WRITE_SIZE_per_dispatch": w_k,
+        "calibration": {"kernel": calib, "bytes_each_way": calib_bytes,
+                        "FETCH_SIZE": f_c, "WRITE_SIZE": w_c,
+                        "fetch_bytes_per_unit": f_scale,
+                        "write_bytes_per_unit": w_scale},
+        "fetch_bytes_per_launch": f_k * f_scale,
+        "write_bytes_per_launch": w_k * w_scale,
+        "traffic_bytes_per_launch": f_k * f_scale + w_k * w_scale,
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    with open(out_json, "w") as fh:
+        json.dump(d, fh, indent=1)
+    return d
+
+
 def main(argv):
-    mode, db = argv[1], argv[2]
+    mode = argv[1]
+    if mode == "traffic":
+        extra = argv[6:]
+        d = traffic(argv[2], argv[3], argv[4], argv[5],
+                    *(extra[:1]), *([int(extra[1])] if len(extra) > 1 else []))
+        print(json.dumps(d, indent=1))
+        return
+    db = argv[2]
     title = " ".join(argv[3:])
     lines = [f"# {title}"] if title else []
     lines += kernel_table(db) if mode == "trace" else pmc_table(db)
