@@ -218,12 +218,21 @@ extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
     }
     int cus = 0;
     RN_TRY(current_cus(&cus));
-    // The vector and element-wise plans may differ; size for the larger.
-    int P = partial_rows(dtype, N, H, true, cus);
-    const int P2 = partial_rows(dtype, N, H, false, cus);
-    if (P2 > P) P = P2;
-    if (P < 0) return RN_EUNSUPPORTED;
-    *bytes = (size_t)P * (size_t)H * sizeof(float) * (is_layernorm ? 2 : 1);
+    // The vector and element-wise plans may differ; size for the larger of
+    // the two that use partial rows (the column-sum strategy needs none).
+    const int e = (int)elem_size(dtype);
+    size_t need = 0;
+    bool any = false;
+    for (int v = 0; v < 2; ++v) {
+        const int P = partial_rows(dtype, N, H, v == 0, cus);
+        if (P < 0) continue;
+        any = true;
+        if (bwd_use_colsum(N, (int)H, e, P, is_layernorm != 0, cus)) continue;
+        const size_t b = (size_t)P * (size_t)H * sizeof(float) * (is_layernorm ? 2 : 1);
+        if (b > need) need = b;
+    }
+    if (!any) return RN_EUNSUPPORTED;
+    *bytes = need;
     return RN_OK;
 }
 
@@ -272,7 +281,8 @@ static int bwd_common(bool ln, const void *dy, int64_t lddy, const void *x,
     RN_TRY(current_cus(&cus));
     const int P = N == 0 ? 0 : partial_rows(dtype, N, H, vec, cus);
     if (P < 0) return RN_EUNSUPPORTED;
-    const size_t need = (size_t)P * (size_t)H * sizeof(float) * (ln ? 2 : 1);
+    const bool colsum = bwd_use_colsum(N, (int)H, (int)e, P, ln, cus);
+    const size_t need = colsum ? 0 : (size_t)P * (size_t)H * sizeof(float) * (ln ? 2 : 1);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RN_EWORKSPACE;
 
     BwdArgs a{};
@@ -282,8 +292,8 @@ static int bwd_common(bool ln, const void *dy, int64_t lddy, const void *x,
     a.N = N; a.H = (int)H; a.inv_H = 1.0f / (float)H;
     hipError_t err =
         dtype == RN_F32
-            ? launch_bwd_f32(ln, a, vec, cus, P, dgamma, dbeta, stream)
-            : launch_bwd_bf16(ln, a, vec, cus, P, dgamma, dbeta, stream);
+            ? launch_bwd_f32(ln, a, vec, cus, P, colsum, dgamma, dbeta, stream)
+            : launch_bwd_bf16(ln, a, vec, cus, P, colsum, dgamma, dbeta, stream);
     return hip_status(err);
 }
 

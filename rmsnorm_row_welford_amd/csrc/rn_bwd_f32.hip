@@ -6,8 +6,7 @@ int bwd_partials_f32(int64_t N, int H, bool vec, int cus) {
     return bwd_partials_t<float, BwdPlansF32>(N, H, vec, cus);
 }
 hipError_t launch_bwd_f32(bool ln, const BwdArgs &a, bool vec, int cus, int P,
-                          void *dgamma, void *dbeta, hipStream_t s) {
-    (void)cus;
-    return launch_bwd_t<float, BwdPlansF32>(ln, a, vec, P, dgamma, dbeta, s);
+                          bool colsum, void *dgamma, void *dbeta, hipStream_t s) {
+    return launch_bwd_t<float, BwdPlansF32>(ln, a, vec, P, colsum, cus, dgamma, dbeta, s);
 }
 }  // namespace rn

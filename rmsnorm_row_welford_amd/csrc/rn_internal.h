@@ -59,12 +59,32 @@ hipError_t launch_fwd_bf16(int op, const FwdArgs &a, bool vec, int cus,
 int bwd_partials_f32(int64_t N, int H, bool vec, int cus);
 int bwd_partials_bf16(int64_t N, int H, bool vec, int cus);
 
-// Backward: kernel 1 (dx + partial rows) then kernel 2 (partial rows ->
-// dgamma [, dbeta]).  `P` must equal bwd_partials_*(N, H, vec, cus).
+// Which reduction the backward uses for dgamma/dbeta.  Partial rows cost
+// 2*P*H*4 bytes per parameter (written by kernel 1, read by kernel 2); the
+// column-sum strategy instead reads x and dy a second time, 2*N*H*e bytes,
+// typically from the Infinity Cache right after kernel 1 read them.  The
+// cheaper one in bytes wins (RN_BWD_COLSUM_PCT scales the comparison).
+// Measured on MI355X, the column sums pay off only with a 2x byte margin
+// and when the row is wide enough for one 8-chunk column tile per CU.
+#ifndef RN_BWD_COLSUM_PCT
+#define RN_BWD_COLSUM_PCT 50
+#endif
+inline bool bwd_use_colsum(int64_t N, int H, int e, int P, bool ln, int cus) {
+    if (N <= 0 || P <= 0) return false;
+    const int cols_per_tile = 8 * (16 / e);
+    if (H / cols_per_tile < cus) return false;
+    const int64_t partial = (int64_t)8 * P * (ln ? 2 : 1);
+    const int64_t reread = (int64_t)2 * N * e;
+    return reread * 100 <= partial * RN_BWD_COLSUM_PCT;
+}
+
+// Backward: kernel 1 (dx [+ partial rows]) then kernel 2 (partial rows, or
+// the column sums of the rows, -> dgamma [, dbeta]).  `P` must equal
+// bwd_partials_*(N, H, vec, cus); `colsum` must be bwd_use_colsum(...).
 hipError_t launch_bwd_f32(bool ln, const BwdArgs &a, bool vec, int cus, int P,
-                          void *dgamma, void *dbeta, hipStream_t s);
+                          bool colsum, void *dgamma, void *dbeta, hipStream_t s);
 hipError_t launch_bwd_bf16(bool ln, const BwdArgs &a, bool vec, int cus, int P,
-                           void *dgamma, void *dbeta, hipStream_t s);
+                           bool colsum, void *dgamma, void *dbeta, hipStream_t s);
 
 hipError_t launch_copy(const void *src, void *dst, size_t bytes,
                        hipStream_t s);

@@ -112,8 +112,11 @@ __device__ __forceinline__ void store_row(rsrc_t r, const Layout<VEC, CPL, TW> &
 }
 
 // ----------------------------------------------------------------- forward --
+// 1024-thread forward workgroups ask for 8 waves per SIMD (<= 64 VGPRs), so
+// that two rows' workgroups share a CU.
 template <class T, int VEC, int CPL, int TW, int RT, int OP, bool PF>
-__global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(64 * TW * RT, (TW * RT == 16 && !PF) ? 8 : 1)
+void fwd_kernel(const FwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
     using Raw = RawChunk<T, VEC>;
     constexpr int E = Lay::E;
@@ -257,8 +260,17 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
                 var = wave_sum(__builtin_fmaf(n_lane * dm, dm, ql)) * a.inv_H;
                 parity ^= 1;
             }
+            // The float32 row is not kept across the statistics: it is
+            // widened again from the packed chunks (made opaque so the
+            // compiler cannot keep the first widening live), which frees E
+            // registers on the wide plans.  Same operations, same bits.
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[e] -= ms;   // v = x - mean
+            for (int c = 0; c < CPL; ++c) opaque(cur[0][c].v);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k)
+                    v[c * VEC + k] = (cur[0][c].get(k) - pivot) - ms;   // x - mean
             mean = pivot + ms;
         } else {
             float q = 0.0f;
@@ -305,7 +317,10 @@ __global__ __launch_bounds__(64 * TW * RT) void fwd_kernel(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------- backward --
-template <class T, int VEC, int CPL, int TW, int RT, bool LN, bool PF>
+// ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
+// kernel only writes dx (the column-sum strategy computes the parameter
+// gradients separately).
+template <class T, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC>
 __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
     using Raw = RawChunk<T, VEC>;
@@ -323,12 +338,14 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
 
     Raw g[CPL];
     load_raw_row<0>(row_rsrc((const T *)a.gamma, H), L, g);
-    float adg[E], adb[LN ? E : 1];
+    float adg[ACC ? E : 1], adb[(ACC && LN) ? E : 1];
+    if constexpr (ACC) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) adg[e] = 0.0f;
-    if constexpr (LN) {
+        for (int e = 0; e < E; ++e) adg[e] = 0.0f;
+        if constexpr (LN) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) adb[e] = 0.0f;
+            for (int e = 0; e < E; ++e) adb[e] = 0.0f;
+        }
     }
 
     const T *xb = (const T *)a.x;
@@ -379,8 +396,10 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
                 const float dyv = cdy[c].get(k);
                 const float xhat = (cx[c].get(k) - cmu) * cs;
                 const float gv = dyv * g[c].get(k);
-                adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
-                if constexpr (LN) adb[e] += dyv;
+                if constexpr (ACC) {
+                    adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
+                    if constexpr (LN) adb[e] += dyv;
+                }
                 sg += gv;
                 sgx = __builtin_fmaf(gv, xhat, sgx);
             }
@@ -437,7 +456,9 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     // dgamma partial, row gridDim.x + blockIdx.x the dbeta partial.  With
     // several teams, each team parks its accumulators in LDS and every
     // thread then adds a column over the teams in team order.
-    if constexpr (RT == 1) {
+    if constexpr (!ACC) {
+        return;
+    } else if constexpr (RT == 1) {
         float *pg = a.part + (int64_t)blockIdx.x * H;
         float *pb = a.part + ((int64_t)gridDim.x + blockIdx.x) * H;
 #pragma unroll
@@ -521,6 +542,70 @@ hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void 
         hipLaunchKernelGGL((bwd2_kernel<T, 32>), dim3((H + 31) / 32, ln ? 2 : 1),
                            dim3(1024), 0, s, part, P, H, (T *)dg, (T *)db);
     return hipGetLastError();
+}
+
+// Column sums straight from the rows: dgamma_j = sum_r dy_rj (x_rj - mean_r)
+// rstd_r and dbeta_j = sum_r dy_rj.  Used instead of partial rows when the
+// rows are so few that P partial rows would outweigh reading x and dy again
+// (see bwd_use_colsum).  A 1024-thread workgroup owns COLS = 8*VEC columns:
+// 8 lanes across the columns (one chunk each) times 128 row slots; slot j
+// adds rows j, j+128, ... in increasing order, and the slots are then added
+// in a fixed two-level order through LDS.
+template <class T, int VEC, bool LN>
+__global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, T *dgamma,
+                                                         T *dbeta) {
+    constexpr int CL = 8, SL = 1024 / CL, COLS = CL * VEC;
+    constexpr int NG = 1024 / COLS;      // second-level groups of slots
+    constexpr int SPG = SL / NG;         // slots per group
+    __shared__ float red[SL * COLS];
+    __shared__ float red2[NG * COLS];
+    const int lc = threadIdx.x % CL;
+    const int slot = threadIdx.x / CL;
+    const int c0 = blockIdx.x * COLS + lc * VEC;
+    const int H = a.H;
+    const int64_t N = a.N;
+    float ag[VEC], ab[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) ag[k] = ab[k] = 0.0f;
+    if (c0 < H) {
+        const T *xb = (const T *)a.x + c0;
+        const T *dyb = (const T *)a.dy + c0;
+#pragma unroll 4
+        for (int64_t r = slot; r < N; r += SL) {
+            float xv[VEC], dv[VEC];
+            load_chunk<VEC, true>(xb + r * a.ldx, xv);
+            load_chunk<VEC, true>(dyb + r * a.lddy, dv);
+            const float mu = LN ? a.mean[r] : 0.0f;
+            const float s = a.rstd[r];
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                ag[k] = __builtin_fmaf(dv[k], (xv[k] - mu) * s, ag[k]);
+                if constexpr (LN) ab[k] += dv[k];
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < (LN ? 2 : 1); ++p) {
+        const float *acc = p == 0 ? ag : ab;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) red[slot * COLS + lc * VEC + k] = acc[k];
+        __syncthreads();
+        const int cc = threadIdx.x % COLS, grp = threadIdx.x / COLS;
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < SPG; ++j) t += red[(grp * SPG + j) * COLS + cc];
+        red2[grp * COLS + cc] = t;
+        __syncthreads();
+        if (threadIdx.x < COLS) {
+            const int col = blockIdx.x * COLS + threadIdx.x;
+            if (col < H) {
+                float u = 0.0f;
+                for (int g = 0; g < NG; ++g) u += red2[g * COLS + threadIdx.x];
+                store_one(p == 0 ? dgamma + col : dbeta + col, u);
+            }
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ plans --
@@ -607,27 +692,47 @@ hipError_t launch_fwd_op(int op, const FwdArgs &a, int cus, hipStream_t s) {
 template <class T, class P>
 inline int bwd_grid(int64_t N, int H, int cus) {
     const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
-    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true, P::PF>;
+    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true>;
     const int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU
                                          : resident_per_cu<k>(P::THREADS, lds);
     return persistent_grid<P>(N, cus, per_cu, P::TW > 1 ? RN_BWD_MIN_ROWS_WIDE : 1);
 }
 
-template <class T, class P>
-hipError_t launch_bwd_plan(bool ln, const BwdArgs &a, int P_, void *dg,
-                           void *db, hipStream_t s) {
-    if (P_ > 0) {
-        const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
-        if (ln)
-            hipLaunchKernelGGL((bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true, P::PF>),
-                               dim3(P_), dim3(P::THREADS), lds, s, a);
-        else
-            hipLaunchKernelGGL((bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, false, P::PF>),
-                               dim3(P_), dim3(P::THREADS), lds, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+template <class T, class P, bool LN>
+hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *dg,
+                         void *db, hipStream_t s) {
+    if (!colsum) {
+        // partial rows: kernel 1 with the persistent grid P_, then kernel 2
+        if (P_ > 0) {
+            const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
+            hipLaunchKernelGGL(
+                (bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true>),
+                dim3(P_), dim3(P::THREADS), lds, s, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return launch_bwd2<T>(a.part, P_, a.H, LN, dg, db, s);
     }
-    return launch_bwd2<T>(a.part, P_, a.H, ln, dg, db, s);
+    // column sums: kernel 1 writes dx only (forward-style grid), then the
+    // column-sum kernel reads x and dy again
+    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, false>;
+    const int resident = resident_per_cu<k>(P::THREADS, 0);
+    const int grid = persistent_grid<P>(a.N, cus, resident >= 2 ? (1 << 20) : resident, 1);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(P::THREADS), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int VEC = P::VEC;
+    constexpr int COLS = 8 * VEC;
+    hipLaunchKernelGGL((bwd_colsum_kernel<T, VEC, LN>), dim3((a.H + COLS - 1) / COLS),
+                       dim3(1024), 0, s, a, (T *)dg, (T *)db);
+    return hipGetLastError();
+}
+
+template <class T, class P>
+hipError_t launch_bwd_plan(bool ln, const BwdArgs &a, int P_, bool colsum, int cus,
+                           void *dg, void *db, hipStream_t s) {
+    return ln ? launch_bwd_ln<T, P, true>(a, P_, colsum, cus, dg, db, s)
+              : launch_bwd_ln<T, P, false>(a, P_, colsum, cus, dg, db, s);
 }
 
 }  // namespace rn

@@ -35,14 +35,16 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 
 // The bf16 plans for the benchmarked row lengths can be overridden at
 // build time (-DRN_FWD_BF16_1024=... etc.) to sweep team shapes.
+// Forward plans that run one workgroup per row group (several fit per CU)
+// do not prefetch (PF = false): the registers would go unused.
 #ifndef RN_FWD_BF16_1024
-#define RN_FWD_BF16_1024 Plan<8, 2, 1, 4>
+#define RN_FWD_BF16_1024 Plan<8, 2, 1, 4, false>
 #endif
 #ifndef RN_FWD_BF16_2048
-#define RN_FWD_BF16_2048 Plan<8, 4, 1, 4>
+#define RN_FWD_BF16_2048 Plan<8, 4, 1, 4, false>
 #endif
 #ifndef RN_FWD_BF16_4096
-#define RN_FWD_BF16_4096 Plan<8, 2, 4, 1>
+#define RN_FWD_BF16_4096 Plan<8, 2, 4, 1, false>
 #endif
 #ifndef RN_FWD_BF16_16384
 #define RN_FWD_BF16_16384 Plan<8, 2, 16, 1>
@@ -58,19 +60,19 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 #endif
 
 // ------------------------------------------------------------- forward --
-using FwdPlansBf16 = PlanList<Plan<8, 1, 1, 4>,     //   512
-                              RN_FWD_BF16_1024,     //  1024
-                              RN_FWD_BF16_2048,     //  2048
-                              RN_FWD_BF16_4096,     //  4096
-                              Plan<8, 2, 8, 1>,     //  8192
-                              RN_FWD_BF16_16384>;   // 16384
-using FwdPlansF32 = PlanList<Plan<4, 1, 1, 4>,      //   256
-                             Plan<4, 2, 1, 4>,      //   512
-                             Plan<4, 4, 1, 4>,      //  1024
-                             Plan<4, 4, 2, 2>,      //  2048
-                             Plan<4, 4, 4, 1>,      //  4096
-                             Plan<4, 4, 8, 1>,      //  8192
-                             Plan<4, 4, 16, 1>>;    // 16384
+using FwdPlansBf16 = PlanList<Plan<8, 1, 1, 4, false>,     //   512
+                              RN_FWD_BF16_1024,            //  1024
+                              RN_FWD_BF16_2048,            //  2048
+                              RN_FWD_BF16_4096,            //  4096
+                              Plan<8, 2, 8, 1, false>,     //  8192
+                              RN_FWD_BF16_16384>;          // 16384
+using FwdPlansF32 = PlanList<Plan<4, 1, 1, 4, false>,      //   256
+                             Plan<4, 2, 1, 4, false>,      //   512
+                             Plan<4, 4, 1, 4, false>,      //  1024
+                             Plan<4, 4, 2, 2, false>,      //  2048
+                             Plan<4, 4, 4, 1, false>,      //  4096
+                             Plan<4, 4, 8, 1, false>,      //  8192
+                             Plan<4, 4, 16, 1>>;           // 16384
 using FwdPlansScalar = PlanList<Plan<1, 1, 1, 4>,   //    64
                                 Plan<1, 4, 1, 4>,   //   256
                                 Plan<1, 4, 4, 1>,   //  1024
@@ -114,9 +116,11 @@ int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
 }
 
 template <class T, class VecPlans>
-hipError_t launch_bwd_t(bool ln, const BwdArgs &a, bool vec, int P,
-                        void *dg, void *db, hipStream_t s) {
-    auto f = [&]<class Pl>() { return launch_bwd_plan<T, Pl>(ln, a, P, dg, db, s); };
+hipError_t launch_bwd_t(bool ln, const BwdArgs &a, bool vec, int P, bool colsum,
+                        int cus, void *dg, void *db, hipStream_t s) {
+    auto f = [&]<class Pl>() {
+        return launch_bwd_plan<T, Pl>(ln, a, P, colsum, cus, dg, db, s);
+    };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(BwdPlansScalar{}, a.H, f);
 }
