@@ -138,6 +138,29 @@ int rms_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
             void *dgamma, void *workspace, size_t workspace_bytes, int64_t N,
             int64_t H, int dtype, float eps, hipStream_t stream);
 
+/* Fused residual add + RMSNorm backward ("Write Triton Fused Add Rmsnorm
+ * Kernel", Required reasoning process, step 10).  The forward computed
+ * h = x + residual and y = RMSNorm(h); both inputs get the same gradient
+ * dL/dh, which is the RMSNorm backward of the STORED h plus dh_in, the
+ * gradient arriving at h through the residual stream (h is also the next
+ * block's residual):
+ *   dx = dres = rstd * (g - x_hat * c2) + dh_in,  x_hat = h * rstd,
+ *   dgamma = sum over rows of dy * x_hat.
+ *   dy, h  [N, H] in;  gamma [H] in;  rstd [N] float32 in (from
+ *     fused_add_rms_fwd; required);
+ *   dh_in [N, H] in, or NULL for no residual-stream gradient;
+ *   dx [N, H] out;  dres [N, H] out, or NULL to write the gradient once
+ *     (dx then serves both inputs);  dgamma [H] out;
+ *   workspace as for rms_bwd (rn_bwd_workspace_bytes(N, H, dtype, 0)).
+ * dx may be exactly dh_in (same pointer and stride: in-place accumulation);
+ * any other overlap is RN_EOVERLAP. */
+int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h, int64_t ldh,
+                      const void *gamma, const float *rstd, const void *dh_in,
+                      int64_t lddh_in, void *dx, int64_t lddx, void *dres,
+                      int64_t lddres, void *dgamma, void *workspace,
+                      size_t workspace_bytes, int64_t N, int64_t H, int dtype,
+                      float eps, hipStream_t stream);
+
 /* Bytes of backward workspace needed on the CURRENT device for (N, H,
  * dtype, LayerNorm or RMSNorm).  It grows with H and the device's
  * compute-unit count, and with N only up to a small multiple of the CU

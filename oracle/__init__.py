@@ -34,6 +34,8 @@ _SIGNATURES = {
                    _P, _P, _P, _P],
     "orc_rms_bwd": [_i64, _i64, _P, _i64, _P, _i64, _P, _dbl, _P, _i64,
                     _P, _P],
+    "orc_fused_add_rms_bwd": [_i64, _i64, _P, _i64, _P, _i64, _P, _P, _P,
+                              _i64, _P, _i64, _P],
     "orc_welford": [_P, _i64, _P, _P, _P],
     "orc_welford_merge": [_dbl, _dbl, _dbl, _dbl, _dbl, _dbl, _P, _P, _P],
     "orc_bf16_decode": [_P, _P, _i64],
@@ -181,6 +183,22 @@ class Oracle:
         self.lib.orc_rms_bwd(N, H, _p(dy), H, _p(x), H, _p(gamma), float(eps),
                              _p(dx), H, _p(dg), _p(rstd))
         return dx, dg, rstd
+
+    def fused_add_rms_bwd(self, dy, h, gamma, rstd, dh_in=None):
+        """Fused add+RMSNorm backward at the stored h with the forward's
+        saved rstd.  Returns (dx, dgamma); dx is also the residual's
+        gradient."""
+        dy = _f64(dy)
+        h = _f64(h)
+        N, H = h.shape
+        gamma = _f64(gamma)
+        rstd = _f64(rstd)
+        dh_in = None if dh_in is None else _f64(dh_in)
+        dx = np.empty_like(h)
+        dg = np.empty(H)
+        self.lib.orc_fused_add_rms_bwd(N, H, _p(dy), H, _p(h), H, _p(gamma),
+                                       _p(rstd), _p(dh_in), H, _p(dx), H, _p(dg))
+        return dx, dg
 
     # ---------------------------------------------------------- welford --
     def welford(self, x):

@@ -249,6 +249,40 @@ void orc_rms_bwd(int64_t N, int64_t H, const double *dy, int64_t lddy,
     param_grads(N, H, dy, lddy, x, ldx, NULL, rstd_out, dgamma, NULL);
 }
 
+/* Fused residual add + RMSNorm backward ("Write Triton Fused Add Rmsnorm
+ * Kernel", Required reasoning process, step 10).  The forward computed
+ * h = x + residual and y = RMSNorm(h); since dh/dx = dh/dresidual = 1, both
+ * inputs receive the same gradient dL/dh.  It is the RMSNorm backward at the
+ * stored h with the rstd the forward saved (the forward took it from the
+ * unrounded h; the backward has only the stored h), plus dh_in, the gradient
+ * that reaches h through the residual stream (h is also the next block's
+ * residual; NULL means none).  With xhat = h * rstd and g = dy * gamma:
+ *   c2 = sum(g * xhat)/H,   dx = dres = rstd * (g - xhat * c2) + dh_in,
+ *   dgamma = column sums of dy * xhat. */
+void orc_fused_add_rms_bwd(int64_t N, int64_t H, const double *dy, int64_t lddy,
+                           const double *h, int64_t ldh, const double *gamma,
+                           const double *rstd, const double *dh_in, int64_t lddh,
+                           double *dx, int64_t lddx, double *dgamma)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < N; ++r) {
+        const double *hr = h + r * ldh;
+        const double *dyr = dy + r * lddy;
+        double *dxr = dx + r * lddx;
+        double s = rstd[r];
+        double sgx = 0.0;
+        for (int64_t j = 0; j < H; ++j) sgx += dyr[j] * gamma[j] * (hr[j] * s);
+        double c2 = sgx / (double)H;
+        for (int64_t j = 0; j < H; ++j) {
+            double g = dyr[j] * gamma[j];
+            dxr[j] = s * (g - (hr[j] * s) * c2);
+        }
+        if (dh_in)
+            for (int64_t j = 0; j < H; ++j) dxr[j] += dh_in[r * lddh + j];
+    }
+    param_grads(N, H, dy, lddy, h, ldh, NULL, rstd, dgamma, NULL);
+}
+
 /* ------------------------------------------------------------------ */
 /* Welford recurrence and parallel merge (for self-checks only)         */
 /* ------------------------------------------------------------------ */

@@ -36,6 +36,8 @@ SIGNATURES = {
                 _I64, _I64, _I, _F, _P], _I),
     "rms_bwd": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _I64,
                  _I64, _I, _F, _P], _I),
+    "fused_add_rms_bwd": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _P,
+                           _I64, _P, _P, _SZ, _I64, _I64, _I, _F, _P], _I),
     "rn_bwd_workspace_bytes": ([_I64, _I64, _I, _I, ctypes.POINTER(_SZ)], _I),
     "rn_max_hidden": ([_I, _I], _I64),
     "rn_status_str": ([_I], ctypes.c_char_p),
@@ -255,6 +257,32 @@ def rms_bwd(dy, x, gamma, rstd, eps=1e-5, *, dx=None, dgamma=None,
         _rows(dx, "dx"), _ptr(dgamma), _ptr(ws), wsb, N, H, _dtype_code(x),
         float(eps), _stream(stream)))
     return dx, dgamma
+
+
+def fused_add_rms_bwd(dy, h, gamma, rstd, eps=1e-6, *, dh_in=None, dx=None,
+                      dres=None, write_dres=False, workspace=None, stream=None):
+    """Fused add+RMSNorm backward on the stored h.  Returns (dx, dres,
+    dgamma); dres is None unless passed or write_dres is set (dx holds the
+    gradient of both inputs).  Pass dx=dh_in to accumulate in place."""
+    import torch
+    N, H = h.shape
+    ldh = _rows(h, "h")
+    lddy = _rows(dy, "dy")
+    _vec(gamma, H, "gamma")
+    _stats(rstd, N, "rstd")
+    if dx is None:
+        dx = torch.empty((N, H), dtype=h.dtype, device=h.device)
+    if dres is None and write_dres:
+        dres = torch.empty((N, H), dtype=h.dtype, device=h.device)
+    dgamma = torch.empty(H, dtype=h.dtype, device=h.device)
+    ws, wsb = _workspace(workspace, N, H, h.dtype, False, h.device)
+    _check("fused_add_rms_bwd", lib().fused_add_rms_bwd(
+        _ptr(dy), lddy, _ptr(h), ldh, _ptr(gamma), _ptr(rstd), _ptr(dh_in),
+        _rows(dh_in, "dh_in") if dh_in is not None else H, _ptr(dx),
+        _rows(dx, "dx"), _ptr(dres), _rows(dres, "dres") if dres is not None else H,
+        _ptr(dgamma), _ptr(ws), wsb, N, H, _dtype_code(h), float(eps),
+        _stream(stream)))
+    return dx, dres, dgamma
 
 
 # ------------------------------------------------------------------ misc --

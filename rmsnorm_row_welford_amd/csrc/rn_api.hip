@@ -236,12 +236,17 @@ extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
     return RN_OK;
 }
 
-static int bwd_common(bool ln, const void *dy, int64_t lddy, const void *x,
-                      int64_t ldx, const void *gamma, const float *mean,
-                      const float *rstd, void *dx, int64_t lddx, void *dgamma,
-                      void *dbeta, void *workspace, size_t workspace_bytes,
-                      int64_t N, int64_t H, int dtype, float eps,
-                      hipStream_t stream) {
+// Shared by the three backward entry points.  `fused` = the fused
+// add+RMSNorm backward: `add` (may be NULL) is added to dx, `dx2` (may be
+// NULL) receives a copy of dx; dx may be exactly `add` (in-place
+// accumulation of the residual-stream gradient).
+static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
+                      const void *x, int64_t ldx, const void *gamma,
+                      const float *mean, const float *rstd, const void *add,
+                      int64_t ldadd, void *dx, int64_t lddx, void *dx2,
+                      int64_t lddx2, void *dgamma, void *dbeta, void *workspace,
+                      size_t workspace_bytes, int64_t N, int64_t H, int dtype,
+                      float eps, hipStream_t stream) {
     if (!dtype_ok(dtype)) return RN_EDTYPE;
     RN_TRY(check_shape(N, H));
     RN_TRY(check_eps(eps));
@@ -253,29 +258,39 @@ static int bwd_common(bool ln, const void *dy, int64_t lddy, const void *x,
     RN_TRY(check_ld(lddy, N, H));
     RN_TRY(check_ld(ldx, N, H));
     RN_TRY(check_ld(lddx, N, H));
-    const void *ptrs[] = {dy, x, gamma, dx, dgamma, ln ? dbeta : nullptr};
+    if (fused && add) RN_TRY(check_ld(ldadd, N, H));
+    if (fused && dx2) RN_TRY(check_ld(lddx2, N, H));
+    if (!fused) {
+        add = nullptr;
+        dx2 = nullptr;
+    }
+    const void *ptrs[] = {dy, x, gamma, dx, dgamma, ln ? dbeta : nullptr, add, dx2};
     for (const void *p : ptrs)
         if (p && !aligned(p, e)) return RN_EINVAL;
-    if (!aligned(rstd, 4) || (mean && !aligned(mean, 4))) return RN_EINVAL;
+    if ((rstd && !aligned(rstd, 4)) || (mean && !aligned(mean, 4))) return RN_EINVAL;
     if (workspace && !aligned(workspace, 256)) return RN_EINVAL;
 
     const Span sdy = span2d(dy, N, H, lddy, e), sx = span2d(x, N, H, ldx, e);
     const Span sg = span1d(gamma, H, e);
     const Span sm = span1d(ln ? mean : nullptr, N, 4), ss = span1d(rstd, N, 4);
-    const Span sdx = span2d(dx, N, H, lddx, e);
+    const Span sa = span2d(add, N, H, ldadd, e);
+    const Span sdx = span2d(dx, N, H, lddx, e), sdx2 = span2d(dx2, N, H, lddx2, e);
     const Span sdg = span1d(dgamma, H, e), sdb = span1d(ln ? dbeta : nullptr, H, e);
     const Span sw = span1d(workspace, (int64_t)workspace_bytes, 1);
-    const Span ins[] = {sdy, sx, sg, sm, ss};
-    const Span outs[] = {sdx, sdg, sdb, sw};
-    for (int i = 0; i < 4; ++i) {
-        for (const Span &in : ins)
-            if (overlaps(outs[i], in)) return RN_EOVERLAP;
-        for (int j = i + 1; j < 4; ++j)
+    const Span ins[] = {sdy, sx, sg, sm, ss, sa};
+    const Span outs[] = {sdx, sdx2, sdg, sdb, sw};
+    const bool dx_is_add = add && dx == add && lddx == ldadd;
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 6; ++j) {
+            if (i == 0 && j == 5 && dx_is_add) continue;   // in-place accumulate
+            if (overlaps(outs[i], ins[j])) return RN_EOVERLAP;
+        }
+        for (int j = i + 1; j < 5; ++j)
             if (overlaps(outs[i], outs[j])) return RN_EOVERLAP;
     }
 
-    const int64_t lds[] = {lddy, ldx, lddx};
-    const bool vec = bwd_vec_ok(e, H, ptrs, 6, lds, 3);
+    const int64_t lds[] = {lddy, ldx, lddx, add ? ldadd : lddx, dx2 ? lddx2 : lddx};
+    const bool vec = bwd_vec_ok(e, H, ptrs, 8, lds, 5);
     if (!vec && H > kMaxHiddenScalar) return RN_EUNSUPPORTED;
     int cus = 0;
     RN_TRY(current_cus(&cus));
@@ -287,13 +302,13 @@ static int bwd_common(bool ln, const void *dy, int64_t lddy, const void *x,
 
     BwdArgs a{};
     a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd;
-    a.dx = dx; a.part = (float *)workspace;
-    a.lddy = lddy; a.ldx = ldx; a.lddx = lddx;
+    a.dx = dx; a.part = (float *)workspace; a.add = add; a.dx2 = dx2;
+    a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.ldadd = ldadd; a.lddx2 = lddx2;
     a.N = N; a.H = (int)H; a.inv_H = 1.0f / (float)H;
     hipError_t err =
         dtype == RN_F32
-            ? launch_bwd_f32(ln, a, vec, cus, P, colsum, dgamma, dbeta, stream)
-            : launch_bwd_bf16(ln, a, vec, cus, P, colsum, dgamma, dbeta, stream);
+            ? launch_bwd_f32(ln, fused, a, vec, cus, P, colsum, dgamma, dbeta, stream)
+            : launch_bwd_bf16(ln, fused, a, vec, cus, P, colsum, dgamma, dbeta, stream);
     return hip_status(err);
 }
 
@@ -302,9 +317,9 @@ extern "C" int ln_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
                       void *dx, int64_t lddx, void *dgamma, void *dbeta,
                       void *workspace, size_t workspace_bytes, int64_t N,
                       int64_t H, int dtype, float eps, hipStream_t stream) {
-    return bwd_common(true, dy, lddy, x, ldx, gamma, mean, rstd, dx, lddx,
-                      dgamma, dbeta, workspace, workspace_bytes, N, H, dtype,
-                      eps, stream);
+    return bwd_common(true, false, dy, lddy, x, ldx, gamma, mean, rstd, nullptr, 0,
+                      dx, lddx, nullptr, 0, dgamma, dbeta, workspace,
+                      workspace_bytes, N, H, dtype, eps, stream);
 }
 
 extern "C" int rms_bwd(const void *dy, int64_t lddy, const void *x,
@@ -312,9 +327,21 @@ extern "C" int rms_bwd(const void *dy, int64_t lddy, const void *x,
                        void *dx, int64_t lddx, void *dgamma, void *workspace,
                        size_t workspace_bytes, int64_t N, int64_t H, int dtype,
                        float eps, hipStream_t stream) {
-    return bwd_common(false, dy, lddy, x, ldx, gamma, nullptr, rstd, dx, lddx,
-                      dgamma, nullptr, workspace, workspace_bytes, N, H, dtype,
-                      eps, stream);
+    return bwd_common(false, false, dy, lddy, x, ldx, gamma, nullptr, rstd, nullptr,
+                      0, dx, lddx, nullptr, 0, dgamma, nullptr, workspace,
+                      workspace_bytes, N, H, dtype, eps, stream);
+}
+
+extern "C" int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h,
+                                 int64_t ldh, const void *gamma, const float *rstd,
+                                 const void *dh_in, int64_t lddh_in, void *dx,
+                                 int64_t lddx, void *dres, int64_t lddres,
+                                 void *dgamma, void *workspace,
+                                 size_t workspace_bytes, int64_t N, int64_t H,
+                                 int dtype, float eps, hipStream_t stream) {
+    return bwd_common(false, true, dy, lddy, h, ldh, gamma, nullptr, rstd, dh_in,
+                      lddh_in, dx, lddx, dres, lddres, dgamma, nullptr, workspace,
+                      workspace_bytes, N, H, dtype, eps, stream);
 }
 
 // ------------------------------------------------------------------- misc --

@@ -30,6 +30,8 @@ struct FwdArgs {
 
 // Arguments of one backward call.  `part` is the float32 partial-row
 // workspace: rows [0, P) hold dgamma partials, rows [P, 2P) dbeta (LN).
+// Fused add+RMSNorm backward extras: `add` (NULL = none) is added to dx,
+// and `dx2` (NULL = none) receives a second copy of dx.
 struct BwdArgs {
     const void *dy;
     const void *x;
@@ -38,7 +40,9 @@ struct BwdArgs {
     const float *rstd;
     void *dx;
     float *part;
-    int64_t lddy, ldx, lddx;
+    const void *add;
+    void *dx2;
+    int64_t lddy, ldx, lddx, ldadd, lddx2;
     int64_t N;
     int H;
     float inv_H;
@@ -81,10 +85,12 @@ inline bool bwd_use_colsum(int64_t N, int H, int e, int P, bool ln, int cus) {
 // Backward: kernel 1 (dx [+ partial rows]) then kernel 2 (partial rows, or
 // the column sums of the rows, -> dgamma [, dbeta]).  `P` must equal
 // bwd_partials_*(N, H, vec, cus); `colsum` must be bwd_use_colsum(...).
-hipError_t launch_bwd_f32(bool ln, const BwdArgs &a, bool vec, int cus, int P,
-                          bool colsum, void *dgamma, void *dbeta, hipStream_t s);
-hipError_t launch_bwd_bf16(bool ln, const BwdArgs &a, bool vec, int cus, int P,
-                           bool colsum, void *dgamma, void *dbeta, hipStream_t s);
+// `fused` selects the RMSNorm kernel variant that also handles a.add and
+// a.dx2 (the fused add+RMSNorm backward; ln must then be false).
+hipError_t launch_bwd_f32(bool ln, bool fused, const BwdArgs &a, bool vec, int cus,
+                          int P, bool colsum, void *dgamma, void *dbeta, hipStream_t s);
+hipError_t launch_bwd_bf16(bool ln, bool fused, const BwdArgs &a, bool vec, int cus,
+                           int P, bool colsum, void *dgamma, void *dbeta, hipStream_t s);
 
 hipError_t launch_copy(const void *src, void *dst, size_t bytes,
                        hipStream_t s);

@@ -319,9 +319,13 @@ void fwd_kernel(const FwdArgs a) {
 // ---------------------------------------------------------------- backward --
 // ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
 // kernel only writes dx (the column-sum strategy computes the parameter
-// gradients separately).
-template <class T, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC>
+// gradients separately).  ADD (RMSNorm only): the fused add+RMSNorm
+// backward, where x is the stored h, a.add (if set) is added to dx and
+// a.dx2 (if set) receives the same values as dx.
+template <class T, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC,
+          bool ADD = false>
 __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
+    static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     using Lay = Layout<VEC, CPL, TW>;
     using Raw = RawChunk<T, VEC>;
     constexpr int E = Lay::E;
@@ -358,11 +362,17 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     // With PF the next row's chunks and statistics are requested before the
     // current row is worked on.
     Raw cx[CPL], cdy[CPL], nx[PF ? CPL : 1], ndy[PF ? CPL : 1];
+    Raw cad[ADD ? CPL : 1], nad[(ADD && PF) ? CPL : 1];
+    const T *addb = (const T *)a.add;
+    const bool has_add = ADD && addb != nullptr;
     float cmu = 0.0f, cs = 0.0f, nmu = 0.0f, ns = 0.0f;
-    auto fetch = [&](int64_t row, auto &x_, auto &dy_, float &mu_, float &s_) {
+    auto fetch = [&](int64_t row, auto &x_, auto &dy_, auto &ad_, float &mu_, float &s_) {
         if (row < N) {
             load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, x_);
             load_raw_row<RN_LOAD_AUX>(row_rsrc(dyb + row * a.lddy, H), L, dy_);
+            if constexpr (ADD) {
+                if (has_add) load_raw_row<RN_LOAD_AUX>(row_rsrc(addb + row * a.ldadd, H), L, ad_);
+            }
             mu_ = LN ? a.mean[row] : 0.0f;
             s_ = a.rstd[row];
         } else {
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
             mu_ = s_ = 0.0f;
         }
     };
-    if constexpr (PF) fetch((int64_t)blockIdx.x * RT + team, cx, cdy, cmu, cs);
+    if constexpr (PF) fetch((int64_t)blockIdx.x * RT + team, cx, cdy, cad, cmu, cs);
 
     int parity = 0;
     for (int64_t grp = blockIdx.x; grp * RT < N; grp += gridDim.x) {
@@ -383,8 +393,8 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
         if constexpr (TW == 1) {
             if (!active) break;
         }
-        if constexpr (PF) fetch(row + step, nx, ndy, nmu, ns);
-        else fetch(row, cx, cdy, cmu, cs);
+        if constexpr (PF) fetch(row + step, nx, ndy, nad, nmu, ns);
+        else fetch(row, cx, cdy, cad, cmu, cs);
 
         // Masked elements have dy = 0, so they add nothing below.
         float sg = 0.0f, sgx = 0.0f;
@@ -438,14 +448,22 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
                     float t = cdy[c].get(k) * g[c].get(k);
                     if constexpr (LN) t -= c1;
                     dx[c * VEC + k] = __builtin_fmaf(-xhat, c2, t) * cs;
+                    if constexpr (ADD) {
+                        if (has_add) dx[c * VEC + k] += cad[c].get(k);
+                    }
                 }
             store_row<T>(row_rsrc((T *)a.dx + row * a.lddx, H), L, dx);
+            if constexpr (ADD) {
+                if (a.dx2 != nullptr)
+                    store_row<T>(row_rsrc((T *)a.dx2 + row * a.lddx2, H), L, dx);
+            }
         }
         if constexpr (PF) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 cx[c] = nx[c];
                 cdy[c] = ndy[c];
+                if constexpr (ADD) cad[c] = nad[c];
             }
             cmu = nmu;
             cs = ns;
@@ -698,7 +716,7 @@ inline int bwd_grid(int64_t N, int H, int cus) {
     return persistent_grid<P>(N, cus, per_cu, P::TW > 1 ? RN_BWD_MIN_ROWS_WIDE : 1);
 }
 
-template <class T, class P, bool LN>
+template <class T, class P, bool LN, bool ADD>
 hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *dg,
                          void *db, hipStream_t s) {
     if (!colsum) {
@@ -706,7 +724,7 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
         if (P_ > 0) {
             const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
             hipLaunchKernelGGL(
-                (bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true>),
+                (bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD>),
                 dim3(P_), dim3(P::THREADS), lds, s, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
@@ -715,7 +733,7 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
     }
     // column sums: kernel 1 writes dx only (forward-style grid), then the
     // column-sum kernel reads x and dy again
-    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, false>;
+    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, false, ADD>;
     const int resident = resident_per_cu<k>(P::THREADS, 0);
     const int grid = persistent_grid<P>(a.N, cus, resident >= 2 ? (1 << 20) : resident, 1);
     hipLaunchKernelGGL(k, dim3(grid), dim3(P::THREADS), 0, s, a);
@@ -729,10 +747,11 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
 }
 
 template <class T, class P>
-hipError_t launch_bwd_plan(bool ln, const BwdArgs &a, int P_, bool colsum, int cus,
-                           void *dg, void *db, hipStream_t s) {
-    return ln ? launch_bwd_ln<T, P, true>(a, P_, colsum, cus, dg, db, s)
-              : launch_bwd_ln<T, P, false>(a, P_, colsum, cus, dg, db, s);
+hipError_t launch_bwd_plan(bool ln, bool fused, const BwdArgs &a, int P_, bool colsum,
+                           int cus, void *dg, void *db, hipStream_t s) {
+    if (ln) return launch_bwd_ln<T, P, true, false>(a, P_, colsum, cus, dg, db, s);
+    if (fused) return launch_bwd_ln<T, P, false, true>(a, P_, colsum, cus, dg, db, s);
+    return launch_bwd_ln<T, P, false, false>(a, P_, colsum, cus, dg, db, s);
 }
 
 }  // namespace rn

@@ -116,10 +116,10 @@ int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
 }
 
 template <class T, class VecPlans>
-hipError_t launch_bwd_t(bool ln, const BwdArgs &a, bool vec, int P, bool colsum,
-                        int cus, void *dg, void *db, hipStream_t s) {
+hipError_t launch_bwd_t(bool ln, bool fused, const BwdArgs &a, bool vec, int P,
+                        bool colsum, int cus, void *dg, void *db, hipStream_t s) {
     auto f = [&]<class Pl>() {
-        return launch_bwd_plan<T, Pl>(ln, a, P, colsum, cus, dg, db, s);
+        return launch_bwd_plan<T, Pl>(ln, fused, a, P, colsum, cus, dg, db, s);
     };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(BwdPlansScalar{}, a.H, f);

@@ -5,8 +5,9 @@ arithmetic, and both the HIP path's tests and the CPU oracle read the bytes
 it produces.
 
 Recipe (per workload): numpy ``Generator(PCG64)`` streams, one child of
-``SeedSequence(seed).spawn(5)`` per tensor, in the fixed order
-[x, residual, dy, gamma, beta].  Each tensor is a binary64 standard-normal
+``SeedSequence(seed).spawn(6)`` per tensor, in the fixed order
+[x, residual, dy, gamma, beta, dh] (child k depends only on seed and k, so a
+tensor's values do not depend on which others a workload draws).  Each tensor is a binary64 standard-normal
 draw z of its shape, mapped to ``mu + sigma * z`` (or the row-split mixture
 for the cancellation workload), then rounded to the storage type: binary32
 by numpy's round-to-nearest-even cast, bfloat16 by torch's CPU cast of that
@@ -27,6 +28,10 @@ shapes and test lists describe them):
                        eps 1e-6
   step_bf16_32768x1024  the benchmark step: x, residual, dy ~ N(0,1),
                        gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1), eps 1e-5
+  fused_bwd_bf16_32768x4096  fused add+RMSNorm fwd then bwd, bf16, the fused
+                       forward's shape; x, residual, dy, dh ~ N(0,1) (dh: the
+                       gradient reaching h through the residual stream);
+                       gamma = 1 + N(0, 0.05); eps 1e-6
   bwd_bf16_32768x1024, bwd_bf16_16384x2048  (tall-narrow)
   bwd_bf16_512x16384,  bwd_bf16_2048x16384  (wide)
                        LayerNorm and RMSNorm fwd+bwd, bf16; x, dy ~ N(0,1),
@@ -37,7 +42,7 @@ from typing import Dict, Optional, Tuple
 
 import numpy as np
 
-ORDER = ("x", "residual", "dy", "gamma", "beta")
+ORDER = ("x", "residual", "dy", "gamma", "beta", "dh")
 
 
 @dataclass(frozen=True)
@@ -54,6 +59,7 @@ class Workload:
     residual: Optional[Tuple[float, float]] = None
     dy: Optional[Tuple[float, float]] = (0.0, 1.0)
     half_shifted: Optional[Tuple[float, float]] = None  # rows [N/2, N)
+    dh: Optional[Tuple[float, float]] = None
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -66,6 +72,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("fused_bf16_32768x4096", 1003, 32768, 4096, "bf16", 1e-6,
                  x=(0.0, 1.0), gamma=(1.0, 0.05), beta=None,
                  residual=(0.0, 1.0), dy=None),
+        Workload("fused_bwd_bf16_32768x4096", 1006, 32768, 4096, "bf16", 1e-6,
+                 x=(0.0, 1.0), gamma=(1.0, 0.05), beta=None,
+                 residual=(0.0, 1.0), dh=(0.0, 1.0)),
         Workload("bwd_bf16_32768x1024", 1004, 32768, 1024, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         # one full training-style pass at the headline shape: LN and RMS
@@ -105,7 +114,7 @@ def generate(w: Workload, N: Optional[int] = None, H: Optional[int] = None,
              seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Storage-typed arrays for workload ``w`` (optionally at another shape
     or seed, same distributions).  Keys present: x, gamma, and whichever of
-    residual, dy, beta the workload has."""
+    residual, dy, beta, dh the workload has."""
     N = w.N if N is None else N
     H = w.H if H is None else H
     rng = _streams(w.seed if seed is None else seed)
@@ -131,14 +140,19 @@ def generate(w: Workload, N: Optional[int] = None, H: Optional[int] = None,
         mu, sd = w.beta
         out["beta"] = to_storage(mu + sd * rng["beta"].standard_normal(H),
                                  w.dtype)
+    if w.dh is not None:
+        mu, sd = w.dh
+        out["dh"] = to_storage(mu + sd * rng["dh"].standard_normal((N, H)),
+                               w.dtype)
     return out
 
 
 def custom(seed: int, N: int, H: int, dtype: str, x=(0.0, 1.0),
            gamma=(1.0, 0.1), beta=(0.0, 0.1), residual=(0.0, 1.0),
-           dy=(0.0, 1.0), half_shifted=None) -> Dict[str, np.ndarray]:
+           dy=(0.0, 1.0), half_shifted=None, dh=(0.0, 1.0)
+           ) -> Dict[str, np.ndarray]:
     """Arrays for an ad-hoc shape (edge cases, ragged tails)."""
     w = Workload("custom", seed, N, H, dtype, 1e-5, x=x, gamma=gamma,
                  beta=beta, residual=residual, dy=dy,
-                 half_shifted=half_shifted)
+                 half_shifted=half_shifted, dh=dh)
     return generate(w)

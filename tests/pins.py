@@ -294,6 +294,51 @@ def check_bwd_finite_differences(orc):
                 _close(dgr, fgr, 1e-7, "RMS dgamma vs FD " + tag)
 
 
+def check_fused_bwd_finite_differences(orc):
+    """Fused add+RMSNorm backward: central differences of
+    L(x, r) = sum(dy * y) + sum(dh * h), (y, h) = fused(x, r), with respect
+    to x AND to r both equal the oracle's gradient at the forward's h and
+    rstd; with dh omitted, the y-path alone."""
+    rng = _rng(26)
+    for N, H, eps in ((1, 1, 1e-5), (2, 3, 0.2), (3, 8, 1e-6), (2, 17, 1e-3)):
+        x = rng.standard_normal((N, H))
+        r = rng.standard_normal((N, H))
+        dy = rng.standard_normal((N, H))
+        dh = rng.standard_normal((N, H))
+        g = 1 + 0.05 * rng.standard_normal(H)
+        for use_dh in (False, True):
+            def L(xx, rr):
+                y, h, _ = orc.fused_add_rms_fwd(xx, rr, g, eps)
+                v = float(np.sum(dy * y))
+                return v + (float(np.sum(dh * h)) if use_dh else 0.0)
+            _, h, rs = orc.fused_add_rms_fwd(x, r, g, eps)
+            dx, dg = orc.fused_add_rms_bwd(dy, h, g, rs, dh if use_dh else None)
+            fx = np.zeros_like(x)
+            fr = np.zeros_like(x)
+            for i in range(N):
+                for j in range(H):
+                    st = 1e-6 * max(1.0, abs(x[i, j]))
+                    e = np.zeros_like(x)
+                    e[i, j] = st
+                    fx[i, j] = (L(x + e, r) - L(x - e, r)) / (2 * st)
+                    st = 1e-6 * max(1.0, abs(r[i, j]))
+                    e = np.zeros_like(x)
+                    e[i, j] = st
+                    fr[i, j] = (L(x, r + e) - L(x, r - e)) / (2 * st)
+            fg = np.zeros(H)
+            for j in range(H):
+                st = 1e-6 * max(1.0, abs(g[j]))
+                gp = g.copy(); gp[j] += st
+                gm = g.copy(); gm[j] -= st
+                yp, _, _ = orc.fused_add_rms_fwd(x, r, gp, eps)
+                ym, _, _ = orc.fused_add_rms_fwd(x, r, gm, eps)
+                fg[j] = (float(np.sum(dy * yp)) - float(np.sum(dy * ym))) / (2 * st)
+            tag = f"N={N} H={H} dh={use_dh}"
+            _close(dx, fx, 1e-7, "fused dx vs FD in x " + tag)
+            _close(dx, fr, 1e-7, "fused dres vs FD in r " + tag)
+            _close(dg, fg, 1e-7, "fused dgamma vs FD " + tag)
+
+
 def check_bwd_invariants(orc):
     """LayerNorm: each dx row sums to 0 and sum_j dx*x_hat equals
     rstd*H*c2*eps/(v+eps).  RMSNorm: sum_j dx*x_hat equals
@@ -478,7 +523,8 @@ ALL_CHECKS = [
     check_ln_moments, check_ln_scale_law, check_ln_affine, check_rms_moments,
     check_rms_scale_law, check_rms_equals_ln_zero_mean, check_fused,
     check_against_torch_fwd, check_golden_closed_forms, check_welford,
-    check_bwd_finite_differences, check_bwd_invariants,
+    check_bwd_finite_differences, check_fused_bwd_finite_differences,
+    check_bwd_invariants,
     check_bwd_against_torch, check_special_cases, check_bf16_codec,
     check_bf16_encode_vs_torch,
 ]

@@ -172,3 +172,33 @@ def test_copy_argument_errors(L):
     assert L.rn_copy(X, Y, 0, S) == OK
     assert L.rn_copy(None, Y, 16, S) == EINVAL
     assert L.rn_copy(X, X + 8, 64, S) == EOVERLAP
+
+
+DH = A * 14
+
+
+def fused_bwd(L, dy=DY, lddy=1024, h=H_, ldh=1024, g=G, r=R, dh=DH, lddh=1024,
+              dx=DX, lddx=1024, dres=RES, lddres=1024, dg=DG, w=W, wb=1 << 24,
+              N=8, H=1024, dt=BF16, eps=1e-6):
+    return L.fused_add_rms_bwd(dy, lddy, h, ldh, g, r, dh, lddh, dx, lddx, dres,
+                               lddres, dg, w, wb, N, H, dt, eps, S)
+
+
+@pytest.mark.parametrize("kw,want", [
+    # dx == dh_in with equal strides is accepted (the GPU tests cover it);
+    # even N = 0 launches the dgamma fill, so no OK case runs here
+    (dict(dx=DH, lddx=1032), EOVERLAP),       # same base, other stride
+    (dict(dx=DH + 64), EOVERLAP),             # partial overlap with dh_in
+    (dict(dres=DH), EOVERLAP),                # dres may not alias dh_in
+    (dict(dres=DX), EOVERLAP),                # dres == dx
+    (dict(dres=H_), EOVERLAP), (dict(dx=DY), EOVERLAP),
+    (dict(dg=DH + 8), EOVERLAP), (dict(w=DH), EOVERLAP),
+    (dict(r=None), EINVAL), (dict(h=None), EINVAL), (dict(dg=None), EINVAL),
+    (dict(dh=DH + 1), EINVAL), (dict(dres=RES + 1), EINVAL),
+    (dict(lddh=1000), EINVAL), (dict(lddres=512), EINVAL),
+    (dict(eps=0.0), EINVAL), (dict(dt=4), EDTYPE),
+    (dict(H=16385, lddy=16385, ldh=16385, lddx=16385, lddh=16385,
+          lddres=16385), EUNSUP),
+])
+def test_fused_bwd_argument_errors(L, kw, want):
+    assert fused_bwd(L, **kw) == want

@@ -104,6 +104,45 @@ def check_bwd(orc, arr, dtype, eps, layernorm, rows=None):
     return stats, rr
 
 
+def fused_bwd_oracle(orc, arr, dtype, eps, with_dh=True):
+    """Oracle side of the fused backward: its own forward gives the stored h
+    (RNE of the exact sum) and the saved rstd (of the exact sum)."""
+    e = oracle.eps_at_boundary(eps)
+    xd, rd = orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype)
+    gd, dyd = orc.decode(arr["gamma"], dtype), orc.decode(arr["dy"], dtype)
+    _, h_o, rs_o = orc.fused_add_rms_fwd(xd, rd, gd, e)
+    h_stored = orc.decode(orc.encode(h_o, dtype), dtype)
+    dhd = orc.decode(arr["dh"], dtype) if with_dh else None
+    dx_o, dg_o = orc.fused_add_rms_bwd(dyd, h_stored, gd, rs_o, dhd)
+    return dx_o, dg_o, tol.dx_term_scale(dyd, gd, rs_o), h_o
+
+
+def check_fused_bwd(orc, arr, dtype, eps, rows=None, with_dh=True,
+                    write_dres=True, in_place=False):
+    """GPU fused forward (h, rstd), GPU fused backward, oracle backward."""
+    x, r, g, dy = (to_dev(arr[k]) for k in ("x", "residual", "gamma", "dy"))
+    _, h, rstd = rn.fused_add_rms_fwd(x, r, g, eps)
+    dh = to_dev(arr["dh"]) if with_dh else None
+    dx, dres, dg = rn.fused_add_rms_bwd(
+        dy, h, g, rstd, eps, dh_in=dh, dx=dh if in_place else None,
+        write_dres=write_dres)
+    torch.cuda.synchronize()
+    if in_place:
+        assert dx.data_ptr() == dh.data_ptr()
+    N = arr["x"].shape[0]
+    rows = np.arange(N) if rows is None else rows
+    dx_o, dg_o, ts, h_o = fused_bwd_oracle(orc, arr, dtype, eps, with_dh)
+    assert np.array_equal(host(h), orc.encode(h_o, dtype)), "h not RNE(x + r)"
+    stats = tol.check_out(host(dx)[rows], dx_o[rows], dtype, orc, "fused dx",
+                          term_scale=ts[rows])
+    if write_dres:
+        assert torch.equal(dres, dx), "dres differs from dx"
+    else:
+        assert dres is None
+    rr = tol.check_param(orc.decode(host(dg), dtype), dg_o, "fused dgamma")
+    return stats, rr
+
+
 # ------------------------------------------------------- the workloads --
 def test_ln_f32_64x1000_fwd_bwd(orc):
     w = synth.WORKLOADS["ln_f32_64x1000"]
@@ -148,6 +187,12 @@ def test_fused_bf16_32768x4096(orc):
     tol.check_rstd(host(rstd)[rows], r_o, "fused rstd")
 
 
+def test_fused_bwd_bf16_32768x4096(orc):
+    w = synth.WORKLOADS["fused_bwd_bf16_32768x4096"]
+    arr = synth.generate(w)
+    check_fused_bwd(orc, arr, "bf16", w.eps, rows=sample_rows(w.N))
+
+
 BWD = ["bwd_bf16_32768x1024", "bwd_bf16_16384x2048", "bwd_bf16_512x16384",
        "bwd_bf16_2048x16384"]
 
@@ -190,6 +235,7 @@ def test_shapes_all_ops(orc, dtype, H):
     assert np.array_equal(host(h), orc.encode(h_o, dtype))
     tol.check_out(host(y), y_o, dtype, orc, "fused y")
     tol.check_rstd(host(rstd), r_o, "fused rstd")
+    check_fused_bwd(orc, arr, dtype, 1e-6)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -266,6 +312,56 @@ def test_fused_in_place(orc, alias):
     tol.check_bf16(host(y), y_o, orc, "in-place fused y")
 
 
+@pytest.mark.parametrize("with_dh,write_dres,in_place", [
+    (True, True, False), (True, False, False), (False, True, False),
+    (False, False, False), (True, True, True), (True, False, True)])
+@pytest.mark.parametrize("N,H", [(129, 4096), (300, 16384), (2051, 1000)])
+def test_fused_bwd_variants(orc, N, H, with_dh, write_dres, in_place):
+    """With and without the residual-stream gradient, one or two outputs,
+    dx accumulated in place over dh_in; a short-wide shape (column sums),
+    and H = 1000 (element-wise path)."""
+    arr = synth.custom(16 + H, N, H, "bf16")
+    check_fused_bwd(orc, arr, "bf16", 1e-6, with_dh=with_dh,
+                    write_dres=write_dres, in_place=in_place)
+
+
+@pytest.mark.parametrize("pad", [24, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_bwd_strided(orc, dtype, pad):
+    """Fused backward with every row tensor at stride H + pad: padding and a
+    guard row after the last row stay untouched."""
+    N, H = 33, 2048
+    arr = synth.custom(17, N, H, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    SENT = -7.0
+
+    def buf(a=None):
+        t = torch.full((N + 1, H + pad), SENT, dtype=tdt, device=DEV)
+        if a is not None:
+            t[:N, :H] = to_dev(a)
+        return t
+
+    def view(t):
+        return t.as_strided((N, H), (H + pad, 1))
+
+    X, R, DY, DH = (buf(arr[k]) for k in ("x", "residual", "dy", "dh"))
+    HH, Y, DX, DR = buf(), buf(), buf(), buf()
+    g = to_dev(arr["gamma"])
+    _, _, rstd = rn.fused_add_rms_fwd(view(X), view(R), g, 1e-6, y=view(Y),
+                                      h=view(HH))
+    rn.fused_add_rms_bwd(view(DY), view(HH), g, rstd, 1e-6, dh_in=view(DH),
+                         dx=view(DX), dres=view(DR))
+    torch.cuda.synchronize()
+    for t, name in ((DX, "dx"), (DR, "dres")):
+        hb = t.float().cpu().numpy()
+        assert np.all(hb[:N, H:] == SENT), f"{name}: row padding written"
+        assert np.all(hb[N, :] == SENT), f"{name}: guard row written"
+    dx_o, _, ts, _ = fused_bwd_oracle(orc, arr, dtype, 1e-6)
+    tol.check_out(host(DX[:N, :H].contiguous()), dx_o, dtype, orc,
+                  "strided fused dx", term_scale=ts)
+    assert torch.equal(DX, DR)
+
+
 # (4099, 16384) reduces through partial rows, (300, 16384) through column
 # sums of the rows (too few rows for partial rows to pay off).
 @pytest.mark.parametrize("N,H", [(4099, 1024), (4099, 16384), (300, 16384)])
@@ -278,8 +374,10 @@ def test_bitwise_deterministic(N, H):
         dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5)
         _, rs2 = rn.rms_fwd(x, g, 1e-5)
         dx2, dg2 = rn.rms_bwd(dy, x, g, rs2, 1e-5)
+        dx3, _, dg3 = rn.fused_add_rms_bwd(dy, x, g, rs2, 1e-5, dh_in=dy)
         torch.cuda.synchronize()
-        outs.append([t.clone() for t in (y, mean, rstd, dx, dg, db, dx2, dg2)])
+        outs.append([t.clone() for t in (y, mean, rstd, dx, dg, db, dx2, dg2,
+                                         dx3, dg3)])
     for a, b_ in zip(*outs):
         assert torch.equal(a, b_)
 
@@ -296,13 +394,16 @@ def test_row_counts(orc, N):
         dg = torch.full((H,), 3.0, dtype=torch.bfloat16, device=DEV)
         db = torch.full((H,), 3.0, dtype=torch.bfloat16, device=DEV)
         rn.ln_bwd(x, x, g, mean, rstd, 1e-5, dgamma=dg, dbeta=db)
+        _, _, dg2 = rn.fused_add_rms_bwd(x, x, g, rstd, 1e-5, dh_in=x)
         torch.cuda.synchronize()
         assert torch.all(dg == 0) and torch.all(db == 0)
+        assert torch.all(dg2 == 0)
         return
     arr = synth.custom(14 + N, N, H, "bf16")
     check_ln_fwd(orc, arr, "bf16", 1e-5)
     check_bwd(orc, arr, "bf16", 1e-5, layernorm=True)
     check_bwd(orc, arr, "bf16", 1e-5, layernorm=False)
+    check_fused_bwd(orc, arr, "bf16", 1e-5)
 
 
 def test_many_short_rows(orc):

@@ -51,6 +51,15 @@ MUTANTS = [
     ("bf16_ties_away", "double r = nearbyint(scaled);",
      "double r = round(scaled);"),
     ("bf16_no_subnormal_spacing", "if (k < -126) k = -126;", ";"),
+    ("fused_bwd_drops_dh_in",
+     "for (int64_t j = 0; j < H; ++j) dxr[j] += dh_in[r * lddh + j];", ";"),
+    ("fused_bwd_dh_in_twice",
+     "for (int64_t j = 0; j < H; ++j) dxr[j] += dh_in[r * lddh + j];",
+     "for (int64_t j = 0; j < H; ++j) dxr[j] += 2.0 * dh_in[r * lddh + j];"),
+    ("fused_bwd_c2_sign", "dxr[j] = s * (g - (hr[j] * s) * c2);",
+     "dxr[j] = s * (g + (hr[j] * s) * c2);"),
+    ("fused_bwd_c2_without_gamma",
+     "sgx += dyr[j] * gamma[j] * (hr[j] * s);", "sgx += dyr[j] * (hr[j] * s);"),
 ]
 
 
