@@ -20,6 +20,13 @@ launch latency.
 
 value = the step's algorithmic HBM bytes / ms_per_step.  Prints ONE JSON line
 on stdout (diagnostics go to stderr).  One GPU only.
+
+Outside the step, per_op also times (same protocol, same shape):
+  fused_add_rms_bwd        the fused op's backward: dx from dy, the stored h,
+                           the saved rstd and a residual-stream gradient dh_in
+  fused_add_rms_fwd_inplace  the fused forward writing h over the residual
+  unfused_add_rms          the unfused comparison: torch.add (h = x + r, one
+                           launch) then rms_fwd on h, 5 N H e bytes in all
 """
 import argparse
 import json
@@ -36,6 +43,7 @@ PEAK_GBS = 8000.0          # MI355X HBM3E, published
 WORKLOAD = "step_bf16_32768x1024"
 FUSED_EPS = 1e-6
 OPS = ("ln_fwd", "rms_fwd", "fused_add_rms_fwd", "ln_bwd", "rms_bwd")
+EXTRA_OPS = ("fused_add_rms_bwd", "fused_add_rms_fwd_inplace", "unfused_add_rms")
 
 
 def log(*a):
@@ -50,6 +58,10 @@ def alg_bytes(N, H, e):
         "fused_add_rms_fwd": 4 * N * H * e + H * e + 4 * N,   # x,r,h,y,gamma,rstd
         "ln_bwd": 3 * N * H * e + 3 * H * e + 8 * N,          # dy,x,dx,gamma,dg,db,stats
         "rms_bwd": 3 * N * H * e + 2 * H * e + 4 * N,         # dy,x,dx,gamma,dg,rstd
+        "fused_add_rms_bwd": 4 * N * H * e + 2 * H * e + 4 * N,  # dy,h,dh_in,dx,gamma,dg,rstd
+        "fused_add_rms_fwd_inplace": 4 * N * H * e + H * e + 4 * N,
+        # add: x, r read, h written; rms_fwd: h read, y written
+        "unfused_add_rms": 5 * N * H * e + H * e + 4 * N,
     }
 
 
@@ -73,7 +85,7 @@ class Sets:
     """M copies of the step's tensors on the GPU, and the five ops bound to
     one copy each."""
 
-    def __init__(self, rn, arr, eps, M, dev):
+    def __init__(self, rn, arr, eps, M, dev, extras=False):
         import torch
         self.rn, self.eps, self.M = rn, eps, M
         bf = torch.bfloat16
@@ -98,10 +110,20 @@ class Sets:
             t["ws_ln"] = torch.empty(ws_ln, dtype=torch.uint8, device=dev)
             t["ws_rms"] = torch.empty(ws_rms, dtype=torch.uint8, device=dev)
             self.s.append(t)
+        if extras:
+            for t in self.s:
+                t["dh"] = dy0.clone()
+                t["r_in"] = r0.clone()
+                for k in ("y4", "y5", "h5", "dx3"):
+                    t[k] = torch.empty((N, H), dtype=bf, device=dev)
+                for k in ("rstd4", "rstd5"):
+                    t[k] = torch.empty(N, dtype=torch.float32, device=dev)
+                t["dg3"] = torch.empty(H, dtype=bf, device=dev)
         del x0, r0, dy0
         for i in range(M):       # saved statistics for the backward ops
             self.run("ln_fwd", i)
             self.run("rms_fwd", i)
+            self.run("fused_add_rms_fwd", i)
 
     def run(self, op, i):
         rn, t, g, b, eps = self.rn, self.s[i % self.M], self.g, self.b, self.eps
@@ -118,6 +140,17 @@ class Sets:
         elif op == "rms_bwd":
             rn.rms_bwd(t["dy"], t["x"], g, t["rstd2"], eps, dx=t["dx2"],
                        dgamma=t["dg2"], workspace=t["ws_rms"])
+        elif op == "fused_add_rms_bwd":
+            rn.fused_add_rms_bwd(t["dy"], t["h"], g, t["rstd3"], FUSED_EPS,
+                                 dh_in=t["dh"], dx=t["dx3"], dgamma=t["dg3"],
+                                 workspace=t["ws_rms"])
+        elif op == "fused_add_rms_fwd_inplace":
+            rn.fused_add_rms_fwd(t["x"], t["r_in"], g, FUSED_EPS, y=t["y4"],
+                                 h=t["r_in"], rstd=t["rstd4"])
+        elif op == "unfused_add_rms":
+            import torch
+            torch.add(t["x"], t["r"], out=t["h5"])
+            rn.rms_fwd(t["h5"], g, FUSED_EPS, y=t["y5"], rstd=t["rstd5"])
         else:
             raise ValueError(op)
 
@@ -258,7 +291,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="also time each op isolated after a cache sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None, help="comma list of ops")
+    ap.add_argument("--only", default=None, help="comma list of step ops")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the ops timed outside the step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -281,8 +316,9 @@ def main():
     t0 = time.time()
     arr = synth.generate(w)
     log(f"inputs generated in {time.time() - t0:.1f}s")
-    sets = Sets(rn, arr, w.eps, args.sets, dev)
     ops = list(OPS) if not args.only else args.only.split(",")
+    extras = [] if (args.no_extras or args.only) else list(EXTRA_OPS)
+    sets = Sets(rn, arr, w.eps, args.sets, dev, extras=bool(extras))
     nbytes = alg_bytes(N, H, 2)
 
     step_ms, wall_ms = time_steps(sets, ops, args.steps, args.warmup)
@@ -293,12 +329,18 @@ def main():
 
     per_op = {}
     K = max(12, 2 * args.sets)
-    for k in ops:
+    for k in ops + extras:
         us, reps = time_op(sets, k, K)
         gbs = nbytes[k] / (us * 1e-6) / 1e9
         per_op[k] = {"us": round(us, 3), "alg_bytes": nbytes[k],
                      "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+        if k in extras:
+            per_op[k]["in_step"] = False
         log(f"{k:18s} {us:8.2f} us  {gbs:7.0f} GB/s  {100 * gbs / PEAK_GBS:5.1f}% of peak")
+    if "unfused_add_rms" in per_op and "fused_add_rms_fwd" in per_op:
+        sp = per_op["unfused_add_rms"]["us"] / per_op["fused_add_rms_fwd"]["us"]
+        per_op["unfused_add_rms"]["fused_speedup"] = round(sp, 3)
+        log(f"fused add+RMSNorm vs unfused (add, then rms_fwd): {sp:.2f}x")
     if args.sweep:
         sweep = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
         for k in ops:

@@ -260,7 +260,8 @@ def rms_bwd(dy, x, gamma, rstd, eps=1e-5, *, dx=None, dgamma=None,
 
 
 def fused_add_rms_bwd(dy, h, gamma, rstd, eps=1e-6, *, dh_in=None, dx=None,
-                      dres=None, write_dres=False, workspace=None, stream=None):
+                      dres=None, write_dres=False, dgamma=None, workspace=None,
+                      stream=None):
     """Fused add+RMSNorm backward on the stored h.  Returns (dx, dres,
     dgamma); dres is None unless passed or write_dres is set (dx holds the
     gradient of both inputs).  Pass dx=dh_in to accumulate in place."""
@@ -274,7 +275,8 @@ def fused_add_rms_bwd(dy, h, gamma, rstd, eps=1e-6, *, dh_in=None, dx=None,
         dx = torch.empty((N, H), dtype=h.dtype, device=h.device)
     if dres is None and write_dres:
         dres = torch.empty((N, H), dtype=h.dtype, device=h.device)
-    dgamma = torch.empty(H, dtype=h.dtype, device=h.device)
+    if dgamma is None:
+        dgamma = torch.empty(H, dtype=h.dtype, device=h.device)
     ws, wsb = _workspace(workspace, N, H, h.dtype, False, h.device)
     _check("fused_add_rms_bwd", lib().fused_add_rms_bwd(
         _ptr(dy), lddy, _ptr(h), ldh, _ptr(gamma), _ptr(rstd), _ptr(dh_in),
