@@ -6,8 +6,8 @@ benchmark's CPU-baseline leg, never by the product package.  It shares no
 code with the HIP path; see oracle.c for the definitions and the passages
 each one follows.
 
-Arrays are numpy.  Storage formats: bfloat16 tensors are carried as uint16
-bit patterns, fp32 as float32.  The math functions take and return float64.
+Arrays are numpy.  Storage formats: bfloat16 and IEEE binary16 tensors are
+carried as uint16 bit patterns, fp32 as float32.  The math functions take and return float64.
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, invariants, finite differences, brute force or exact
@@ -41,6 +41,8 @@ _SIGNATURES = {
     "orc_bf16_decode": [_P, _P, _i64],
     "orc_bf16_encode": [_P, _P, _i64],
     "orc_f32_encode": [_P, _P, _i64],
+    "orc_f16_decode": [_P, _P, _i64],
+    "orc_f16_encode": [_P, _P, _i64],
     "orc_num_threads": [],
 }
 
@@ -92,6 +94,18 @@ class Oracle:
         self.lib.orc_bf16_encode(_p(v), _p(out), v.size)
         return out
 
+    def f16_decode(self, bits):
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, dtype=np.float64)
+        self.lib.orc_f16_decode(_p(bits), _p(out), bits.size)
+        return out
+
+    def f16_encode(self, v):
+        v = _f64(v)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.orc_f16_encode(_p(v), _p(out), v.size)
+        return out
+
     def f32_encode(self, v):
         v = _f64(v)
         out = np.empty(v.shape, dtype=np.float32)
@@ -102,6 +116,8 @@ class Oracle:
         """Storage array -> float64 (exact)."""
         if dtype == "bf16":
             return self.bf16_decode(a)
+        if dtype == "f16":
+            return self.f16_decode(a)
         if dtype == "f32":
             return np.asarray(a, dtype=np.float32).astype(np.float64)
         raise ValueError(dtype)
@@ -110,6 +126,8 @@ class Oracle:
         """float64 -> storage array, one correctly rounded step (RNE)."""
         if dtype == "bf16":
             return self.bf16_encode(v)
+        if dtype == "f16":
+            return self.f16_encode(v)
         if dtype == "f32":
             return self.f32_encode(v)
         raise ValueError(dtype)

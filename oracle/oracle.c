@@ -371,6 +371,57 @@ void orc_bf16_encode(const double *in, uint16_t *out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = bf16_round_one(in[i]);
 }
 
+/* IEEE binary16 -> binary64, exact: 1 sign, 5 exponent (bias 15) and 10
+ * fraction bits; exponent 0 holds zero and the subnormals (fraction *
+ * 2^-24), exponent 31 infinity and NaN. */
+void orc_f16_decode(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        unsigned u = in[i];
+        double sgn = (u & 0x8000u) ? -1.0 : 1.0;
+        unsigned ex = (u >> 10) & 0x1Fu, fr = u & 0x3FFu;
+        double v;
+        if (ex == 0) v = ldexp((double)fr, -24);
+        else if (ex == 31) v = fr ? NAN : INFINITY;
+        else v = ldexp((double)(1024u + fr), (int)ex - 25);
+        out[i] = sgn * v;
+    }
+}
+
+/* binary64 -> binary16, round to nearest, ties to even, in one step.
+ * binary16 has 11 significant bits: the spacing near |v| in [2^k, 2^(k+1))
+ * is 2^(k-10), and 2^-24 below 2^-14 (subnormals).  Values whose rounded
+ * magnitude exceeds the largest finite value 65504 become infinity; NaN
+ * becomes a quiet NaN with the same sign. */
+static uint16_t f16_round_one(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);            /* 2^(e-1) <= a < 2^e          */
+    int k = e - 1;
+    if (k < -14) k = -14;          /* subnormal spacing           */
+    int q = k - 10;                /* spacing exponent            */
+    double r = nearbyint(ldexp(a, -q));   /* exact scale, then RNE */
+    double rv = ldexp(r, q);
+    if (rv > 65504.0) return (uint16_t)(sign | 0x7C00u);
+    if (rv < 0x1p-14)              /* subnormal (or rounded to 0)  */
+        return (uint16_t)(sign | (uint16_t)ldexp(rv, 24));
+    int er;
+    (void)frexp(rv, &er);          /* rounding may have carried    */
+    int kr = er - 1;
+    unsigned frac = (unsigned)(ldexp(rv, 10 - kr) - 1024.0);
+    return (uint16_t)(sign | (unsigned)(kr + 15) << 10 | frac);
+}
+
+void orc_f16_encode(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_round_one(in[i]);
+}
+
 /* binary64 -> binary32 with the C conversion (round to nearest even). */
 void orc_f32_encode(const double *in, float *out, int64_t n)
 {

@@ -10,9 +10,11 @@ Recipe (per workload): numpy ``Generator(PCG64)`` streams, one child of
 tensor's values do not depend on which others a workload draws).  Each tensor is a binary64 standard-normal
 draw z of its shape, mapped to ``mu + sigma * z`` (or the row-split mixture
 for the cancellation workload), then rounded to the storage type: binary32
-by numpy's round-to-nearest-even cast, bfloat16 by torch's CPU cast of that
-binary32 value (round-to-nearest-even).  bfloat16 arrays are carried as
-uint16 bit patterns, binary32 as float32.
+by numpy's round-to-nearest-even cast, bfloat16 and IEEE binary16 by torch's
+CPU cast of that binary32 value (round-to-nearest-even).  bfloat16 and
+binary16 arrays are carried as uint16 bit patterns, binary32 as float32.
+gamma and beta take the workload's parameter type (``wdtype``, default: the
+activation type).
 
 Workloads (sizes and distributions as the normalization pages' benchmark
 shapes and test lists describe them):
@@ -32,6 +34,10 @@ shapes and test lists describe them):
                        forward's shape; x, residual, dy, dh ~ N(0,1) (dh: the
                        gradient reaching h through the residual stream);
                        gamma = 1 + N(0, 0.05); eps 1e-6
+  mixed_bf16_f32w_32768x1024  LayerNorm/RMSNorm/fused fwd+bwd with bf16
+                       activations and float32 gamma, beta, dgamma, dbeta;
+                       distributions as step_bf16_32768x1024
+  f16_32768x1024       the same in IEEE binary16 throughout
   bwd_bf16_32768x1024, bwd_bf16_16384x2048  (tall-narrow)
   bwd_bf16_512x16384,  bwd_bf16_2048x16384  (wide)
                        LayerNorm and RMSNorm fwd+bwd, bf16; x, dy ~ N(0,1),
@@ -51,7 +57,7 @@ class Workload:
     seed: int
     N: int
     H: int
-    dtype: str                 # "bf16" or "f32"
+    dtype: str                 # activations: "bf16", "f16" or "f32"
     eps: float
     x: Tuple[float, float]     # (mu, sigma) of x
     gamma: Tuple[float, float]
@@ -60,6 +66,7 @@ class Workload:
     dy: Optional[Tuple[float, float]] = (0.0, 1.0)
     half_shifted: Optional[Tuple[float, float]] = None  # rows [N/2, N)
     dh: Optional[Tuple[float, float]] = None
+    wdtype: Optional[str] = None   # gamma/beta storage; None = dtype
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -82,6 +89,12 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("step_bf16_32768x1024", 1004, 32768, 1024, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1),
                  residual=(0.0, 1.0)),
+        Workload("mixed_bf16_f32w_32768x1024", 1007, 32768, 1024, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1),
+                 residual=(0.0, 1.0), dh=(0.0, 1.0), wdtype="f32"),
+        Workload("f16_32768x1024", 1008, 32768, 1024, "f16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1),
+                 residual=(0.0, 1.0), dh=(0.0, 1.0)),
         Workload("bwd_bf16_16384x2048", 1004, 16384, 2048, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         Workload("bwd_bf16_512x16384", 1005, 512, 16384, "bf16", 1e-5,
@@ -97,9 +110,10 @@ def to_storage(a64: np.ndarray, dtype: str) -> np.ndarray:
     a32 = np.asarray(a64, dtype=np.float64).astype(np.float32)
     if dtype == "f32":
         return a32
-    if dtype == "bf16":
+    if dtype in ("bf16", "f16"):
         import torch
-        t = torch.from_numpy(np.ascontiguousarray(a32)).to(torch.bfloat16)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        t = torch.from_numpy(np.ascontiguousarray(a32)).to(tdt)
         return t.view(torch.int16).numpy().view(np.uint16).copy()
     raise ValueError(f"unknown dtype {dtype!r}")
 
@@ -133,13 +147,12 @@ def generate(w: Workload, N: Optional[int] = None, H: Optional[int] = None,
         mu, sd = w.dy
         out["dy"] = to_storage(mu + sd * rng["dy"].standard_normal((N, H)),
                                w.dtype)
+    wdt = w.wdtype or w.dtype
     mu, sd = w.gamma
-    out["gamma"] = to_storage(mu + sd * rng["gamma"].standard_normal(H),
-                              w.dtype)
+    out["gamma"] = to_storage(mu + sd * rng["gamma"].standard_normal(H), wdt)
     if w.beta is not None:
         mu, sd = w.beta
-        out["beta"] = to_storage(mu + sd * rng["beta"].standard_normal(H),
-                                 w.dtype)
+        out["beta"] = to_storage(mu + sd * rng["beta"].standard_normal(H), wdt)
     if w.dh is not None:
         mu, sd = w.dh
         out["dh"] = to_storage(mu + sd * rng["dh"].standard_normal((N, H)),
@@ -149,10 +162,10 @@ def generate(w: Workload, N: Optional[int] = None, H: Optional[int] = None,
 
 def custom(seed: int, N: int, H: int, dtype: str, x=(0.0, 1.0),
            gamma=(1.0, 0.1), beta=(0.0, 0.1), residual=(0.0, 1.0),
-           dy=(0.0, 1.0), half_shifted=None, dh=(0.0, 1.0)
+           dy=(0.0, 1.0), half_shifted=None, dh=(0.0, 1.0), wdtype=None
            ) -> Dict[str, np.ndarray]:
     """Arrays for an ad-hoc shape (edge cases, ragged tails)."""
     w = Workload("custom", seed, N, H, dtype, 1e-5, x=x, gamma=gamma,
                  beta=beta, residual=residual, dy=dy,
-                 half_shifted=half_shifted, dh=dh)
+                 half_shifted=half_shifted, dh=dh, wdtype=wdtype)
     return generate(w)

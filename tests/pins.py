@@ -519,6 +519,86 @@ def check_bf16_encode_vs_torch(orc):
     assert bad.size == 0, f"{bad.size} mismatches, e.g. {f[bad[:3]]}"
 
 
+def _exact_round_f16(v: float, finite_sorted, finite_bits):
+    """Reference RNE to binary16 by exact rational comparison against the
+    enumerated set of all finite binary16 values (overflow at or beyond
+    65504 + 16, half an ulp past the largest value)."""
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    if Fraction(abs(v)) >= Fraction(65504) + 16:
+        return 0xFC00 if v < 0 else 0x7C00
+    i = int(np.searchsorted(finite_sorted, v))
+    fv = Fraction(v)
+    best = None
+    for k in (i - 1, i):
+        if 0 <= k < len(finite_sorted):
+            key = (abs(Fraction(finite_sorted[k]) - fv), int(finite_bits[k]) & 1)
+            if best is None or key < best[0]:
+                best = (key, k)
+    bits = int(finite_bits[best[1]])
+    if Fraction(finite_sorted[best[1]]) == 0:
+        return 0x8000 if v < 0 else 0
+    return bits
+
+
+def check_f16_codec(orc):
+    """IEEE binary16: decode of all 2^16 patterns equals numpy's exact
+    float16 -> float64 widening; encode equals exact rational rounding to
+    the nearest finite value (ties to the even pattern) on random, tie,
+    subnormal and overflow inputs, and equals numpy's direct float64 ->
+    float16 cast on a million random binary64 values."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    dec = orc.f16_decode(bits)
+    nan = np.isnan(vals)
+    assert np.array_equal(np.isnan(dec), nan)
+    assert np.array_equal(dec[~nan], vals[~nan])
+    assert np.array_equal(np.signbit(dec[~nan]), np.signbit(vals[~nan]))
+    fin = np.isfinite(vals)
+    order = np.argsort(vals[fin], kind="stable")
+    fs, fb = vals[fin][order], bits[fin][order]
+    keep = np.concatenate([[True], np.diff(fs) > 0])
+    fs, fb = fs[keep], fb[keep]
+    rng = _rng(27)
+    tests = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 6, 2000))
+    for k in rng.integers(0, len(fs) - 1, 400):
+        mid = (fs[k] + fs[k + 1]) / 2.0
+        tests += [mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)]
+    tiny = 2.0 ** -24
+    tests += [0.0, -0.0, tiny, tiny / 2, tiny * 0.75, tiny * 1.5, -tiny * 2.5,
+              2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -12), 65504.0, 65519.99,
+              65520.0, -65520.0, 1e6, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11,
+              2047.5, 2048.5, 2049.0]
+    tests = np.array(tests, dtype=np.float64)
+    got = orc.f16_encode(tests)
+    for v, gb in zip(tests, got):
+        want = _exact_round_f16(float(v), fs, fb)
+        assert int(gb) == want, f"f16({v!r}) = {int(gb):#06x}, want {want:#06x}"
+    sp = orc.f16_encode(np.array([np.inf, -np.inf, np.nan]))
+    assert int(sp[0]) == 0x7C00 and int(sp[1]) == 0xFC00
+    assert (int(sp[2]) & 0x7C00) == 0x7C00 and (int(sp[2]) & 0x3FF) != 0
+    w = rng.standard_normal(1 << 20) * 10.0 ** rng.integers(-8, 5, 1 << 20)
+    with np.errstate(over="ignore"):
+        want = w.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(orc.f16_encode(w) != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches vs numpy, e.g. {w[bad[:3]]}"
+
+
+def check_f16_encode_vs_torch(orc):
+    """binary32 inputs: one-step rounding from binary64 equals torch's
+    float32 -> float16 cast (round to nearest even)."""
+    import torch
+    rng = _rng(28)
+    u = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.float16).view(torch.int16)
+    want = want.numpy().view(np.uint16)
+    got = orc.f16_encode(f.astype(np.float64))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, e.g. {f[bad[:3]]}"
+
+
 ALL_CHECKS = [
     check_ln_moments, check_ln_scale_law, check_ln_affine, check_rms_moments,
     check_rms_scale_law, check_rms_equals_ln_zero_mean, check_fused,
@@ -526,5 +606,5 @@ ALL_CHECKS = [
     check_bwd_finite_differences, check_fused_bwd_finite_differences,
     check_bwd_invariants,
     check_bwd_against_torch, check_special_cases, check_bf16_codec,
-    check_bf16_encode_vs_torch,
+    check_bf16_encode_vs_torch, check_f16_codec, check_f16_encode_vs_torch,
 ]

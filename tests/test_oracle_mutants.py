@@ -60,6 +60,12 @@ MUTANTS = [
      "dxr[j] = s * (g + (hr[j] * s) * c2);"),
     ("fused_bwd_c2_without_gamma",
      "sgx += dyr[j] * gamma[j] * (hr[j] * s);", "sgx += dyr[j] * (hr[j] * s);"),
+    ("f16_truncates", "double r = nearbyint(ldexp(a, -q));",
+     "double r = trunc(ldexp(a, -q));"),
+    ("f16_no_subnormal_spacing", "if (k < -14) k = -14;", ";"),
+    ("f16_no_overflow_to_inf", "if (rv > 65504.0)", "if (rv > 1e300)"),
+    ("f16_decode_subnormal_scale", "v = ldexp((double)fr, -24);",
+     "v = ldexp((double)fr, -25);"),
 ]
 
 

@@ -1,6 +1,9 @@
 """Parity bars between the HIP path and the binary64 oracle.
 
-bf16 outputs: the GPU value must be within 1 bf16 ulp of the correctly
+bf16 and fp16 outputs (same rule, each in its own format; for fp16 the
+  ulp is 2^-11..2^-10 * |v| and the floor below still sits far above the
+  float32 pipeline's error):
+  the GPU value must be within 1 ulp of the correctly
   rounded oracle value (distance measured on the ordered integer image of the
   bit patterns, +0 == -0), or, for values produced by cancellation, within an
   absolute floor of 2^-16 times the row's scale.  The float32 pipeline's own
@@ -25,7 +28,8 @@ PARAM_REL_RMS = 5e-3
 
 
 def ordered(bits_u16: np.ndarray) -> np.ndarray:
-    """Map bfloat16 bit patterns to integers ordered like their values."""
+    """Map bfloat16 / binary16 bit patterns (sign-magnitude) to integers
+    ordered like their values."""
     b = bits_u16.astype(np.int32)
     mag = b & 0x7FFF
     return np.where(b & 0x8000, -mag, mag)
@@ -43,14 +47,15 @@ def _scale(oracle_vals, term_scale):
     return s
 
 
-def check_bf16(gpu_bits, oracle_vals, orc, what, term_scale=None):
-    """gpu_bits: uint16 [N, H]; oracle_vals: float64 [N, H] (unrounded);
-    term_scale: optional per-row scale of the terms that cancel."""
+def check_bf16(gpu_bits, oracle_vals, orc, what, term_scale=None, dtype="bf16"):
+    """gpu_bits: uint16 [N, H] (bf16, or fp16 with dtype="f16");
+    oracle_vals: float64 [N, H] (unrounded); term_scale: optional per-row
+    scale of the terms that cancel."""
     gpu_bits = np.atleast_2d(gpu_bits)
     oracle_vals = np.atleast_2d(oracle_vals)
-    want = orc.bf16_encode(oracle_vals)
+    want = orc.encode(oracle_vals, dtype)
     ulp = np.abs(ordered(gpu_bits) - ordered(want))
-    gv = orc.bf16_decode(gpu_bits)
+    gv = orc.decode(gpu_bits, dtype)
     floor = BF16_FLOOR * _scale(oracle_vals, term_scale)
     ok = (ulp <= 1) | (np.abs(gv - oracle_vals) <= floor)
     bad = np.argwhere(~ok)
@@ -80,8 +85,8 @@ def check_f32(gpu, oracle_vals, what, rel=F32_REL, term_scale=None):
 
 
 def check_out(gpu_host, oracle_vals, dtype, orc, what, term_scale=None):
-    if dtype == "bf16":
-        return check_bf16(gpu_host, oracle_vals, orc, what, term_scale)
+    if dtype in ("bf16", "f16"):
+        return check_bf16(gpu_host, oracle_vals, orc, what, term_scale, dtype)
     return check_f32(gpu_host, oracle_vals, what, term_scale=term_scale)
 
 
