@@ -16,11 +16,15 @@
  * gamma, beta, dgamma, dbeta are vectors of H elements shared by all rows
  * (no row offset is ever applied to them).
  *
- * Types.  One `dtype` (rn_dtype) covers every activation and parameter
- * tensor of a call: x, residual, h, y, dy, dx, gamma, beta, dgamma, dbeta.
- * mean and rstd are always float32 vectors of N elements.  All arithmetic
- * runs in float32 after the load; results are rounded to `dtype` (round to
- * nearest even) at the store.
+ * Types.  One `dtype` (rn_dtype) names the storage of every tensor of a
+ * call: the activations (x, residual, h, y, dy, dx, dh_in, dres) and the
+ * parameters (gamma, beta, dgamma, dbeta), which are either of the
+ * activation type or, with the *_F32W codes, float32 ("Write Cuda Layernorm
+ * Kernel", Required reasoning process and Kernel design rules, keep the
+ * affine parameters in float32 whatever the activations are).  mean and
+ * rstd are always float32 vectors of N elements.  All arithmetic runs in
+ * float32 after the load; results are rounded to their storage type (round
+ * to nearest even; fp16 overflow gives infinity) at the store.
  *
  * eps.  Added INSIDE the square root: rstd = 1 / sqrt(var + eps).  It must be
  * finite and > 0.
@@ -57,7 +61,13 @@
 extern "C" {
 #endif
 
-typedef enum { RN_F32 = 0, RN_BF16 = 1 } rn_dtype;
+typedef enum {
+    RN_F32 = 0,         /* float32 activations and parameters               */
+    RN_BF16 = 1,        /* bfloat16 activations and parameters              */
+    RN_F16 = 2,         /* IEEE binary16 activations and parameters         */
+    RN_BF16_F32W = 3,   /* bfloat16 activations, float32 parameters         */
+    RN_F16_F32W = 4     /* binary16 activations, float32 parameters         */
+} rn_dtype;
 
 enum {
     RN_OK = 0,

@@ -8,9 +8,10 @@ All arithmetic runs in the library's HIP kernels; there is no CPU fallback —
 if the library is missing every call raises.
 
 Tensors are 2-D [N, H] with contiguous rows (stride(1) == 1, any row stride
->= H), on one GPU, dtype torch.float32 or torch.bfloat16.  gamma/beta and the
-parameter gradients are [H] tensors of the same dtype; mean/rstd are float32
-[N] tensors.
+>= H), on one GPU, dtype torch.float32, torch.bfloat16 or torch.float16.
+gamma/beta are [H] tensors of the activation dtype or float32 (with 16-bit
+activations); the parameter gradients take gamma's dtype.  mean/rstd are
+float32 [N] tensors.
 """
 import ctypes
 import os
@@ -18,7 +19,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librownorm.so")
 
-RN_F32, RN_BF16 = 0, 1
+RN_F32, RN_BF16, RN_F16, RN_BF16_F32W, RN_F16_F32W = 0, 1, 2, 3, 4
 RN_OK = 0
 STATUS_NAMES = {0: "RN_OK", -1: "RN_EINVAL", -2: "RN_EDTYPE",
                 -3: "RN_EOVERLAP", -4: "RN_EWORKSPACE", -5: "RN_EHIP",
@@ -78,13 +79,21 @@ def _check(fn, status):
 
 
 # ------------------------------------------------------------ marshalling --
-def _dtype_code(t):
+def _code_of(act, param):
+    """rn_dtype code for (activation dtype, parameter dtype)."""
     import torch
-    if t.dtype == torch.float32:
-        return RN_F32
-    if t.dtype == torch.bfloat16:
-        return RN_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    table = {(torch.float32, torch.float32): RN_F32,
+             (torch.bfloat16, torch.bfloat16): RN_BF16,
+             (torch.float16, torch.float16): RN_F16,
+             (torch.bfloat16, torch.float32): RN_BF16_F32W,
+             (torch.float16, torch.float32): RN_F16_F32W}
+    if (act, param) not in table:
+        raise TypeError(f"unsupported dtypes: activations {act}, parameters {param}")
+    return table[(act, param)]
+
+
+def _dtype_code(t, gamma):
+    return _code_of(t.dtype, gamma.dtype)
 
 
 def _ptr(t):
@@ -148,7 +157,7 @@ def ln_fwd(x, gamma, beta=None, eps=1e-5, *, y=None, mean=None, rstd=None,
     _stats(rstd, N, "rstd")
     _check("ln_fwd", lib().ln_fwd(
         _ptr(x), ldx, _ptr(gamma), _ptr(beta), _ptr(y), _rows(y, "y"),
-        _ptr(mean), _ptr(rstd), N, H, _dtype_code(x), float(eps),
+        _ptr(mean), _ptr(rstd), N, H, _dtype_code(x, gamma), float(eps),
         _stream(stream)))
     return y, mean, rstd
 
@@ -167,7 +176,7 @@ def rms_fwd(x, gamma, eps=1e-5, *, y=None, rstd=None, save_stats=True,
     _stats(rstd, N, "rstd")
     _check("rms_fwd", lib().rms_fwd(
         _ptr(x), ldx, _ptr(gamma), _ptr(y), _rows(y, "y"), _ptr(rstd), N, H,
-        _dtype_code(x), float(eps), _stream(stream)))
+        _dtype_code(x, gamma), float(eps), _stream(stream)))
     return y, rstd
 
 
@@ -190,27 +199,28 @@ def fused_add_rms_fwd(x, residual, gamma, eps=1e-6, *, y=None, h=None,
     _check("fused_add_rms_fwd", lib().fused_add_rms_fwd(
         _ptr(x), ldx, _ptr(residual), ldr, _ptr(gamma), _ptr(y),
         _rows(y, "y"), _ptr(h), _rows(h, "h"), _ptr(rstd), N, H,
-        _dtype_code(x), float(eps), _stream(stream)))
+        _dtype_code(x, gamma), float(eps), _stream(stream)))
     return y, h, rstd
 
 
 # --------------------------------------------------------------- backward --
-def workspace_bytes(N, H, dtype, layernorm: bool) -> int:
-    """Backward workspace size on the current device (rn_bwd_workspace_bytes)."""
-    import torch
-    code = {torch.float32: RN_F32, torch.bfloat16: RN_BF16}[dtype]
+def workspace_bytes(N, H, dtype, layernorm: bool, param_dtype=None) -> int:
+    """Backward workspace size on the current device (rn_bwd_workspace_bytes)
+    for activations of `dtype` and parameters of `param_dtype` (default:
+    the same)."""
+    code = _code_of(dtype, dtype if param_dtype is None else param_dtype)
     out = ctypes.c_size_t(0)
     _check("rn_bwd_workspace_bytes", lib().rn_bwd_workspace_bytes(
         N, H, code, 1 if layernorm else 0, ctypes.byref(out)))
     return int(out.value)
 
 
-def _workspace(workspace, N, H, dtype, layernorm, device):
+def _workspace(workspace, N, H, x, gamma, layernorm):
     import torch
-    need = workspace_bytes(N, H, dtype, layernorm)
+    need = workspace_bytes(N, H, x.dtype, layernorm, gamma.dtype)
     if workspace is None:
         # 256-byte aligned by torch's caching allocator
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -227,14 +237,14 @@ def ln_bwd(dy, x, gamma, mean, rstd, eps=1e-5, *, dx=None, dgamma=None,
     if dx is None:
         dx = torch.empty((N, H), dtype=x.dtype, device=x.device)
     if dgamma is None:
-        dgamma = torch.empty(H, dtype=x.dtype, device=x.device)
+        dgamma = torch.empty(H, dtype=gamma.dtype, device=x.device)
     if dbeta is None:
-        dbeta = torch.empty(H, dtype=x.dtype, device=x.device)
-    ws, wsb = _workspace(workspace, N, H, x.dtype, True, x.device)
+        dbeta = torch.empty(H, dtype=gamma.dtype, device=x.device)
+    ws, wsb = _workspace(workspace, N, H, x, gamma, True)
     _check("ln_bwd", lib().ln_bwd(
         _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(mean), _ptr(rstd),
         _ptr(dx), _rows(dx, "dx"), _ptr(dgamma), _ptr(dbeta), _ptr(ws), wsb,
-        N, H, _dtype_code(x), float(eps), _stream(stream)))
+        N, H, _dtype_code(x, gamma), float(eps), _stream(stream)))
     return dx, dgamma, dbeta
 
 
@@ -250,12 +260,12 @@ def rms_bwd(dy, x, gamma, rstd, eps=1e-5, *, dx=None, dgamma=None,
     if dx is None:
         dx = torch.empty((N, H), dtype=x.dtype, device=x.device)
     if dgamma is None:
-        dgamma = torch.empty(H, dtype=x.dtype, device=x.device)
-    ws, wsb = _workspace(workspace, N, H, x.dtype, False, x.device)
+        dgamma = torch.empty(H, dtype=gamma.dtype, device=x.device)
+    ws, wsb = _workspace(workspace, N, H, x, gamma, False)
     _check("rms_bwd", lib().rms_bwd(
         _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(rstd), _ptr(dx),
-        _rows(dx, "dx"), _ptr(dgamma), _ptr(ws), wsb, N, H, _dtype_code(x),
-        float(eps), _stream(stream)))
+        _rows(dx, "dx"), _ptr(dgamma), _ptr(ws), wsb, N, H,
+        _dtype_code(x, gamma), float(eps), _stream(stream)))
     return dx, dgamma
 
 
@@ -276,13 +286,13 @@ def fused_add_rms_bwd(dy, h, gamma, rstd, eps=1e-6, *, dh_in=None, dx=None,
     if dres is None and write_dres:
         dres = torch.empty((N, H), dtype=h.dtype, device=h.device)
     if dgamma is None:
-        dgamma = torch.empty(H, dtype=h.dtype, device=h.device)
-    ws, wsb = _workspace(workspace, N, H, h.dtype, False, h.device)
+        dgamma = torch.empty(H, dtype=gamma.dtype, device=h.device)
+    ws, wsb = _workspace(workspace, N, H, h, gamma, False)
     _check("fused_add_rms_bwd", lib().fused_add_rms_bwd(
         _ptr(dy), lddy, _ptr(h), ldh, _ptr(gamma), _ptr(rstd), _ptr(dh_in),
         _rows(dh_in, "dh_in") if dh_in is not None else H, _ptr(dx),
         _rows(dx, "dx"), _ptr(dres), _rows(dres, "dres") if dres is not None else H,
-        _ptr(dgamma), _ptr(ws), wsb, N, H, _dtype_code(h), float(eps),
+        _ptr(dgamma), _ptr(ws), wsb, N, H, _dtype_code(h, gamma), float(eps),
         _stream(stream)))
     return dx, dres, dgamma
 

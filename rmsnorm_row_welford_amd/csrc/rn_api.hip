@@ -2,6 +2,7 @@
 // plan inputs (vectorizability, CU count) and kernel launches.  All checks
 // run before anything is enqueued.
 #include <math.h>
+#include <initializer_list>
 #include <mutex>
 #include <stdint.h>
 
@@ -34,9 +35,44 @@ int current_cus(int *cus) {
     return RN_OK;
 }
 
+// Bytes per element of the rn_dtype codes: activations (x, residual, h, y,
+// dy, dx, ...) and parameters (gamma, beta, dgamma, dbeta).
+bool dtype_ok(int dtype) { return dtype >= RN_F32 && dtype <= RN_F16_F32W; }
 size_t elem_size(int dtype) { return dtype == RN_F32 ? 4 : 2; }
+size_t param_size(int dtype) { return (dtype == RN_BF16 || dtype == RN_F16) ? 2 : 4; }
 
-bool dtype_ok(int dtype) { return dtype == RN_F32 || dtype == RN_BF16; }
+hipError_t launch_fwd(int dtype, int op, const FwdArgs &a, bool vec, int cus,
+                      hipStream_t s) {
+    switch (dtype) {
+    case RN_F32: return launch_fwd_f32(op, a, vec, cus, s);
+    case RN_BF16: return launch_fwd_bf16(op, a, vec, cus, s);
+    case RN_F16: return launch_fwd_f16(op, a, vec, cus, s);
+    case RN_BF16_F32W: return launch_fwd_bf16_f32w(op, a, vec, cus, s);
+    default: return launch_fwd_f16_f32w(op, a, vec, cus, s);
+    }
+}
+
+int bwd_partials(int dtype, int64_t N, int H, bool vec, int cus) {
+    switch (dtype) {
+    case RN_F32: return bwd_partials_f32(N, H, vec, cus);
+    case RN_BF16: return bwd_partials_bf16(N, H, vec, cus);
+    case RN_F16: return bwd_partials_f16(N, H, vec, cus);
+    case RN_BF16_F32W: return bwd_partials_bf16_f32w(N, H, vec, cus);
+    default: return bwd_partials_f16_f32w(N, H, vec, cus);
+    }
+}
+
+hipError_t launch_bwd(int dtype, bool ln, bool fused, const BwdArgs &a, bool vec,
+                      int cus, int P, bool colsum, void *dg, void *db, hipStream_t s) {
+    switch (dtype) {
+    case RN_F32: return launch_bwd_f32(ln, fused, a, vec, cus, P, colsum, dg, db, s);
+    case RN_BF16: return launch_bwd_bf16(ln, fused, a, vec, cus, P, colsum, dg, db, s);
+    case RN_F16: return launch_bwd_f16(ln, fused, a, vec, cus, P, colsum, dg, db, s);
+    case RN_BF16_F32W:
+        return launch_bwd_bf16_f32w(ln, fused, a, vec, cus, P, colsum, dg, db, s);
+    default: return launch_bwd_f16_f32w(ln, fused, a, vec, cus, P, colsum, dg, db, s);
+    }
+}
 
 // Byte range [lo, hi) touched by an [N, H] tensor with row stride ld.
 struct Span {
@@ -108,7 +144,7 @@ static int fwd_common(int op, const void *x, int64_t ldx, const void *res,
     if (!dtype_ok(dtype)) return RN_EDTYPE;
     RN_TRY(check_shape(N, H));
     RN_TRY(check_eps(eps));
-    const size_t e = elem_size(dtype);
+    const size_t e = elem_size(dtype), ep = param_size(dtype);
     // Row tensors may be NULL only when there are no rows.
     if (!gamma || (N > 0 && (!x || !y))) return RN_EINVAL;
     if (op == OP_FUSED && N > 0 && (!res || !h)) return RN_EINVAL;
@@ -119,15 +155,17 @@ static int fwd_common(int op, const void *x, int64_t ldx, const void *res,
         RN_TRY(check_ld(ldh, N, H));
     }
     const void *ptrs[] = {x, res, gamma, beta, y, h};
-    for (const void *p : ptrs)
+    for (const void *p : std::initializer_list<const void *>{x, res, y, h})
         if (p && !aligned(p, e)) return RN_EINVAL;
+    for (const void *p : std::initializer_list<const void *>{gamma, beta})
+        if (p && !aligned(p, ep)) return RN_EINVAL;
     if ((mean && !aligned(mean, 4)) || (rstd && !aligned(rstd, 4)))
         return RN_EINVAL;
 
     // Overlaps.  Inputs: x, res, gamma, beta.  Outputs: y, h, mean, rstd.
     // h may be exactly x or exactly res (in-place residual update).
     const Span sx = span2d(x, N, H, ldx, e), sr = span2d(res, N, H, ldr, e);
-    const Span sg = span1d(gamma, H, e), sb = span1d(beta, H, e);
+    const Span sg = span1d(gamma, H, ep), sb = span1d(beta, H, ep);
     const Span sy = span2d(y, N, H, ldy, e), sh = span2d(h, N, H, ldh, e);
     const Span sm = span1d(mean, N, 4), ss = span1d(rstd, N, 4);
     const Span ins[] = {sx, sr, sg, sb};
@@ -163,9 +201,7 @@ static int fwd_common(int op, const void *x, int64_t ldx, const void *res,
     a.y = y; a.h = h; a.mean = mean; a.rstd = rstd;
     a.ldx = ldx; a.ldr = ldr; a.ldy = ldy; a.ldh = ldh;
     a.N = N; a.H = (int)H; a.eps = eps; a.inv_H = 1.0f / (float)H;
-    hipError_t err = dtype == RN_F32 ? launch_fwd_f32(op, a, vc.ok, cus, stream)
-                                     : launch_fwd_bf16(op, a, vc.ok, cus, stream);
-    return hip_status(err);
+    return hip_status(launch_fwd(dtype, op, a, vc.ok, cus, stream));
 }
 
 extern "C" int ln_fwd(const void *x, int64_t ldx, const void *gamma,
@@ -203,8 +239,7 @@ static bool bwd_vec_ok(size_t e, int64_t H, const void *const *ptrs, int np,
 }
 
 static int partial_rows(int dtype, int64_t N, int64_t H, bool vec, int cus) {
-    return dtype == RN_F32 ? bwd_partials_f32(N, (int)H, vec, cus)
-                           : bwd_partials_bf16(N, (int)H, vec, cus);
+    return bwd_partials(dtype, N, (int)H, vec, cus);
 }
 
 extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
@@ -250,7 +285,7 @@ static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
     if (!dtype_ok(dtype)) return RN_EDTYPE;
     RN_TRY(check_shape(N, H));
     RN_TRY(check_eps(eps));
-    const size_t e = elem_size(dtype);
+    const size_t e = elem_size(dtype), ep = param_size(dtype);
     // Row tensors and saved statistics may be NULL only when there are no
     // rows; the parameter gradients are always written.
     if (!gamma || !dgamma || (ln && !dbeta)) return RN_EINVAL;
@@ -265,17 +300,19 @@ static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
         dx2 = nullptr;
     }
     const void *ptrs[] = {dy, x, gamma, dx, dgamma, ln ? dbeta : nullptr, add, dx2};
-    for (const void *p : ptrs)
+    for (const void *p : std::initializer_list<const void *>{dy, x, dx, add, dx2})
         if (p && !aligned(p, e)) return RN_EINVAL;
+    for (const void *p : std::initializer_list<const void *>{gamma, dgamma, ln ? dbeta : nullptr})
+        if (p && !aligned(p, ep)) return RN_EINVAL;
     if ((rstd && !aligned(rstd, 4)) || (mean && !aligned(mean, 4))) return RN_EINVAL;
     if (workspace && !aligned(workspace, 256)) return RN_EINVAL;
 
     const Span sdy = span2d(dy, N, H, lddy, e), sx = span2d(x, N, H, ldx, e);
-    const Span sg = span1d(gamma, H, e);
+    const Span sg = span1d(gamma, H, ep);
     const Span sm = span1d(ln ? mean : nullptr, N, 4), ss = span1d(rstd, N, 4);
     const Span sa = span2d(add, N, H, ldadd, e);
     const Span sdx = span2d(dx, N, H, lddx, e), sdx2 = span2d(dx2, N, H, lddx2, e);
-    const Span sdg = span1d(dgamma, H, e), sdb = span1d(ln ? dbeta : nullptr, H, e);
+    const Span sdg = span1d(dgamma, H, ep), sdb = span1d(ln ? dbeta : nullptr, H, ep);
     const Span sw = span1d(workspace, (int64_t)workspace_bytes, 1);
     const Span ins[] = {sdy, sx, sg, sm, ss, sa};
     const Span outs[] = {sdx, sdx2, sdg, sdb, sw};
@@ -305,11 +342,8 @@ static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
     a.dx = dx; a.part = (float *)workspace; a.add = add; a.dx2 = dx2;
     a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.ldadd = ldadd; a.lddx2 = lddx2;
     a.N = N; a.H = (int)H; a.inv_H = 1.0f / (float)H;
-    hipError_t err =
-        dtype == RN_F32
-            ? launch_bwd_f32(ln, fused, a, vec, cus, P, colsum, dgamma, dbeta, stream)
-            : launch_bwd_bf16(ln, fused, a, vec, cus, P, colsum, dgamma, dbeta, stream);
-    return hip_status(err);
+    return hip_status(
+        launch_bwd(dtype, ln, fused, a, vec, cus, P, colsum, dgamma, dbeta, stream));
 }
 
 extern "C" int ln_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,

@@ -1,12 +1,6 @@
-// Backward kernels, bfloat16 storage.
+// Backward kernels: bfloat16 activations and parameters.
 #include "rn_plans.h"
 
 namespace rn {
-int bwd_partials_bf16(int64_t N, int H, bool vec, int cus) {
-    return bwd_partials_t<bf16_bits, BwdPlansBf16>(N, H, vec, cus);
-}
-hipError_t launch_bwd_bf16(bool ln, bool fused, const BwdArgs &a, bool vec, int cus,
-                          int P, bool colsum, void *dgamma, void *dbeta, hipStream_t s) {
-    return launch_bwd_t<bf16_bits, BwdPlansBf16>(ln, fused, a, vec, P, colsum, cus, dgamma, dbeta, s);
-}
+RN_DEFINE_BWD(bf16, bf16_bits, bf16_bits, BwdPlans2B)
 }  // namespace rn

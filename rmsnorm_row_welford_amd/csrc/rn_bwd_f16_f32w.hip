@@ -1,0 +1,6 @@
+// Backward kernels: binary16 activations, float32 parameters.
+#include "rn_plans.h"
+
+namespace rn {
+RN_DEFINE_BWD(f16_f32w, f16_t, float, BwdPlans2B)
+}  // namespace rn

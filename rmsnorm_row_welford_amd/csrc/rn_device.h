@@ -1,6 +1,7 @@
 // Device primitives for the gfx950 row-normalization kernels: vector
-// load/store of row chunks with float32 conversion, bfloat16 rounding, and
-// wave64 reductions built from DPP row permutations and ds_swizzle.
+// load/store of row chunks with float32 conversion, bfloat16 and binary16
+// rounding, and wave64 reductions built from DPP row permutations and
+// ds_swizzle.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,14 +13,18 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// bfloat16 values travel as their 16-bit patterns.
+// bfloat16 values travel as their 16-bit patterns; IEEE binary16 as the
+// compiler's _Float16.
 typedef uint16_t bf16_bits;
+typedef _Float16 f16_t;
 
 // Elements per 16-byte chunk.
 template <class T> struct Vec16;
 template <> struct Vec16<float> { static constexpr int N = 4; };
 template <> struct Vec16<bf16_bits> { static constexpr int N = 8; };
+template <> struct Vec16<f16_t> { static constexpr int N = 8; };
 
 // ------------------------------------------------------------------ codec --
 __device__ __forceinline__ float bf16_lo(unsigned u) {
@@ -36,6 +41,18 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 }
 __device__ __forceinline__ bf16_bits to_bf16(float a) {
     return __builtin_bit_cast(bf16_bits, (__bf16)a);
+}
+// binary16 <-> float32: widening is exact; narrowing rounds to nearest even
+// (the default rounding mode; overflow gives infinity).
+__device__ __forceinline__ float f16_lo(unsigned u) {
+    return (float)__builtin_bit_cast(f16x2, u)[0];
+}
+__device__ __forceinline__ float f16_hi(unsigned u) {
+    return (float)__builtin_bit_cast(f16x2, u)[1];
+}
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
 }
 
 // ------------------------------------------------------------ chunk I/O --
@@ -66,6 +83,21 @@ __device__ __forceinline__ void load_chunk(const bf16_bits *p, float *o) {
         static_assert(VEC == 1, "bf16 chunks are 8 or 1 elements");
         unsigned u = NT ? __builtin_nontemporal_load(p) : *p;
         o[0] = __uint_as_float(u << 16);
+    }
+}
+template <int VEC, bool NT>
+__device__ __forceinline__ void load_chunk(const f16_t *p, float *o) {
+    if constexpr (VEC == 8) {
+        u32x4 v = NT ? __builtin_nontemporal_load((const u32x4 *)p)
+                     : *(const u32x4 *)p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[2 * k] = f16_lo(v[k]);
+            o[2 * k + 1] = f16_hi(v[k]);
+        }
+    } else {
+        static_assert(VEC == 1, "fp16 chunks are 8 or 1 elements");
+        o[0] = (float)(NT ? __builtin_nontemporal_load(p) : *p);
     }
 }
 
@@ -112,6 +144,36 @@ template <> struct RawChunk<bf16_bits, 1> {
     }
     __device__ __forceinline__ void zero() { v = 0u; }
     __device__ __forceinline__ float get(int) const { return __uint_as_float(v << 16); }
+};
+template <> struct RawChunk<f16_t, 8> {
+    u32x4 v;
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    }
+    __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float get(int k) const {
+        return (k & 1) ? f16_hi(v[k >> 1]) : f16_lo(v[k >> 1]);
+    }
+};
+template <> struct RawChunk<f16_t, 1> {
+    unsigned v;
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+    }
+    __device__ __forceinline__ void zero() { v = 0u; }
+    __device__ __forceinline__ float get(int) const { return f16_lo(v); }
+};
+// float32 parameters beside 8-element (2-byte) activation chunks: two
+// 16-byte loads per chunk.
+template <> struct RawChunk<float, 8> {
+    f32x4 v[2];
+    template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
+        v[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+        v[1] = __builtin_bit_cast(f32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, AUX));
+    }
+    __device__ __forceinline__ void zero() { v[0] = v[1] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ float get(int k) const { return v[k >> 2][k & 3]; }
 };
 template <> struct RawChunk<float, 4> {
     f32x4 v;
@@ -165,9 +227,24 @@ __device__ __forceinline__ void bstore_chunk(bf16_bits *, rsrc_t r, int off, con
     }
 }
 
+template <int VEC>
+__device__ __forceinline__ void bstore_chunk(f16_t *, rsrc_t r, int off, const float *v) {
+    if constexpr (VEC == 8) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pack_f16(v[2 * k], v[2 * k + 1]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, RN_STORE_AUX);
+    } else {
+        static_assert(VEC == 1, "fp16 chunks are 8 or 1 elements");
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16_t)v[0]), r,
+                                              off, 0, RN_STORE_AUX);
+    }
+}
+
 // Store one float32 as the storage type.
 __device__ __forceinline__ void store_one(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_one(bf16_bits *p, float v) { *p = to_bf16(v); }
+__device__ __forceinline__ void store_one(f16_t *p, float v) { *p = (f16_t)v; }
 
 // ------------------------------------------------------ wave reductions --
 // DPP controls (GFX9 encoding).

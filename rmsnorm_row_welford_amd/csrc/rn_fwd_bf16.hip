@@ -1,9 +1,6 @@
-// Forward kernels, bfloat16 storage.
+// Forward kernels: bfloat16 activations and parameters.
 #include "rn_plans.h"
 
 namespace rn {
-hipError_t launch_fwd_bf16(int op, const FwdArgs &a, bool vec, int cus,
-                           hipStream_t s) {
-    return launch_fwd_t<bf16_bits, FwdPlansBf16>(op, a, vec, cus, s);
-}
+RN_DEFINE_FWD(bf16, bf16_bits, bf16_bits, FwdPlans2B)
 }  // namespace rn

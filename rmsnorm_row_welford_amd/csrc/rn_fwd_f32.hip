@@ -1,9 +1,6 @@
-// Forward kernels, float32 storage.
+// Forward kernels: float32 activations and parameters.
 #include "rn_plans.h"
 
 namespace rn {
-hipError_t launch_fwd_f32(int op, const FwdArgs &a, bool vec, int cus,
-                          hipStream_t s) {
-    return launch_fwd_t<float, FwdPlansF32>(op, a, vec, cus, s);
-}
+RN_DEFINE_FWD(f32, float, float, FwdPlansF32)
 }  // namespace rn

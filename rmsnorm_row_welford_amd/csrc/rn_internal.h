@@ -52,16 +52,33 @@ struct BwdArgs {
 constexpr int kMaxHidden = 16384;
 constexpr int kMaxHiddenScalar = 8192;
 
-// Forward: picks the kernel for (op, H, vec) and launches it.  Returns a
-// hipError_t.
-hipError_t launch_fwd_f32(int op, const FwdArgs &a, bool vec, int cus,
-                          hipStream_t s);
-hipError_t launch_fwd_bf16(int op, const FwdArgs &a, bool vec, int cus,
-                           hipStream_t s);
-
-// Backward kernel 1 grid (the number of partial rows P) for a shape.
-int bwd_partials_f32(int64_t N, int H, bool vec, int cus);
-int bwd_partials_bf16(int64_t N, int H, bool vec, int cus);
+// Per storage pair (activations / parameters), one translation unit per
+// direction defines:
+//   launch_fwd_<S>:   picks the kernel for (op, H, vec) and launches it;
+//   bwd_partials_<S>: backward kernel 1's grid (the number of partial rows
+//                     P) for a shape, or -1 if H has no plan;
+//   launch_bwd_<S>:   the backward: kernel 1 (dx [+ partial rows]) then
+//                     kernel 2 (partial rows, or the column sums of the
+//                     rows, -> dgamma [, dbeta]).  `P` must equal
+//                     bwd_partials_<S>(N, H, vec, cus) and `colsum` must be
+//                     bwd_use_colsum(...).  `fused` selects the RMSNorm
+//                     kernel variant that also handles a.add and a.dx2 (the
+//                     fused add+RMSNorm backward; ln must then be false).
+// S: f32, bf16, f16 (parameters in the activation type) and bf16_f32w,
+// f16_f32w (float32 parameters).
+#define RN_DECLARE_STORAGE(S)                                                        \
+    hipError_t launch_fwd_##S(int op, const FwdArgs &a, bool vec, int cus,           \
+                              hipStream_t s);                                        \
+    int bwd_partials_##S(int64_t N, int H, bool vec, int cus);                      \
+    hipError_t launch_bwd_##S(bool ln, bool fused, const BwdArgs &a, bool vec,       \
+                              int cus, int P, bool colsum, void *dgamma, void *dbeta, \
+                              hipStream_t s);
+RN_DECLARE_STORAGE(f32)
+RN_DECLARE_STORAGE(bf16)
+RN_DECLARE_STORAGE(f16)
+RN_DECLARE_STORAGE(bf16_f32w)
+RN_DECLARE_STORAGE(f16_f32w)
+#undef RN_DECLARE_STORAGE
 
 // Which reduction the backward uses for dgamma/dbeta.  Partial rows cost
 // 2*P*H*4 bytes per parameter (written by kernel 1, read by kernel 2); the
@@ -81,16 +98,6 @@ inline bool bwd_use_colsum(int64_t N, int H, int e, int P, bool ln, int cus) {
     const int64_t reread = (int64_t)2 * N * e;
     return reread * 100 <= partial * RN_BWD_COLSUM_PCT;
 }
-
-// Backward: kernel 1 (dx [+ partial rows]) then kernel 2 (partial rows, or
-// the column sums of the rows, -> dgamma [, dbeta]).  `P` must equal
-// bwd_partials_*(N, H, vec, cus); `colsum` must be bwd_use_colsum(...).
-// `fused` selects the RMSNorm kernel variant that also handles a.add and
-// a.dx2 (the fused add+RMSNorm backward; ln must then be false).
-hipError_t launch_bwd_f32(bool ln, bool fused, const BwdArgs &a, bool vec, int cus,
-                          int P, bool colsum, void *dgamma, void *dbeta, hipStream_t s);
-hipError_t launch_bwd_bf16(bool ln, bool fused, const BwdArgs &a, bool vec, int cus,
-                           int P, bool colsum, void *dgamma, void *dbeta, hipStream_t s);
 
 hipError_t launch_copy(const void *src, void *dst, size_t bytes,
                        hipStream_t s);

@@ -114,11 +114,12 @@ __device__ __forceinline__ void store_row(rsrc_t r, const Layout<VEC, CPL, TW> &
 // ----------------------------------------------------------------- forward --
 // 1024-thread forward workgroups ask for 8 waves per SIMD (<= 64 VGPRs), so
 // that two rows' workgroups share a CU.
-template <class T, int VEC, int CPL, int TW, int RT, int OP, bool PF>
+template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF>
 __global__ __launch_bounds__(64 * TW * RT, (TW * RT == 16 && !PF) ? 8 : 1)
 void fwd_kernel(const FwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
     using Raw = RawChunk<T, VEC>;
+    using RawW = RawChunk<W, VEC>;
     constexpr int E = Lay::E;
     constexpr int NV = (OP == OP_LN) ? 2 : 1;
     constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;   // row inputs: x [, residual]
@@ -132,11 +133,11 @@ void fwd_kernel(const FwdArgs a) {
     const int H = a.H;
     const Lay L(wit * 64 + lane, H);
 
-    Raw g[CPL];
-    load_raw_row<0>(row_rsrc((const T *)a.gamma, H), L, g);
-    Raw bt[(OP == OP_LN) ? CPL : 1];
+    RawW g[CPL];
+    load_raw_row<0>(row_rsrc((const W *)a.gamma, H), L, g);
+    RawW bt[(OP == OP_LN) ? CPL : 1];
     if constexpr (OP == OP_LN) {
-        if (a.beta != nullptr) load_raw_row<0>(row_rsrc((const T *)a.beta, H), L, bt);
+        if (a.beta != nullptr) load_raw_row<0>(row_rsrc((const W *)a.beta, H), L, bt);
         else
 #pragma unroll
             for (int c = 0; c < CPL; ++c) bt[c].zero();
@@ -322,7 +323,7 @@ void fwd_kernel(const FwdArgs a) {
 // gradients separately).  ADD (RMSNorm only): the fused add+RMSNorm
 // backward, where x is the stored h, a.add (if set) is added to dx and
 // a.dx2 (if set) receives the same values as dx.
-template <class T, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC,
+template <class T, class W, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC,
           bool ADD = false>
 __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     const int H = a.H;
     const Lay L(wit * 64 + lane, H);
 
-    Raw g[CPL];
-    load_raw_row<0>(row_rsrc((const T *)a.gamma, H), L, g);
+    RawChunk<W, VEC> g[CPL];
+    load_raw_row<0>(row_rsrc((const W *)a.gamma, H), L, g);
     float adg[ACC ? E : 1], adb[(ACC && LN) ? E : 1];
     if constexpr (ACC) {
 #pragma unroll
@@ -569,9 +570,9 @@ hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void 
 // 8 lanes across the columns (one chunk each) times 128 row slots; slot j
 // adds rows j, j+128, ... in increasing order, and the slots are then added
 // in a fixed two-level order through LDS.
-template <class T, int VEC, bool LN>
-__global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, T *dgamma,
-                                                         T *dbeta) {
+template <class T, class W, int VEC, bool LN>
+__global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, W *dgamma,
+                                                         W *dbeta) {
     constexpr int CL = 8, SL = 1024 / CL, COLS = CL * VEC;
     constexpr int NG = 1024 / COLS;      // second-level groups of slots
     constexpr int SPG = SL / NG;         // slots per group
@@ -683,9 +684,9 @@ inline int persistent_grid(int64_t N, int cus, int per_cu, int min_rows) {
 // finish, which streams better than a persistent loop.  When only one fits
 // (1024-thread rows), a persistent grid of one workgroup per CU whose teams
 // prefetch their next row.
-template <class T, class P, int OP>
+template <class T, class W, class P, int OP>
 hipError_t launch_fwd_plan(const FwdArgs &a, int cus, hipStream_t s) {
-    constexpr auto k = fwd_kernel<T, P::VEC, P::CPL, P::TW, P::RT, OP, P::PF>;
+    constexpr auto k = fwd_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, OP, P::PF>;
     const int resident = resident_per_cu<k>(P::THREADS, 0);
     const int per_cu = RN_FWD_PER_CU > 0 ? RN_FWD_PER_CU
                        : resident >= 2   ? (1 << 20)
@@ -695,28 +696,28 @@ hipError_t launch_fwd_plan(const FwdArgs &a, int cus, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class T, class P>
+template <class T, class W, class P>
 hipError_t launch_fwd_op(int op, const FwdArgs &a, int cus, hipStream_t s) {
     switch (op) {
-    case OP_LN: return launch_fwd_plan<T, P, OP_LN>(a, cus, s);
-    case OP_RMS: return launch_fwd_plan<T, P, OP_RMS>(a, cus, s);
-    default: return launch_fwd_plan<T, P, OP_FUSED>(a, cus, s);
+    case OP_LN: return launch_fwd_plan<T, W, P, OP_LN>(a, cus, s);
+    case OP_RMS: return launch_fwd_plan<T, W, P, OP_RMS>(a, cus, s);
+    default: return launch_fwd_plan<T, W, P, OP_FUSED>(a, cus, s);
     }
 }
 
 // Backward: kernel 1's workgroup count, i.e. the number of partial rows P.
 // The LayerNorm kernel has the larger footprint, so both norms use its
 // occupancy, which keeps the workspace size independent of the norm.
-template <class T, class P>
+template <class T, class W, class P>
 inline int bwd_grid(int64_t N, int H, int cus) {
     const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
-    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true>;
+    constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true>;
     const int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU
                                          : resident_per_cu<k>(P::THREADS, lds);
     return persistent_grid<P>(N, cus, per_cu, P::TW > 1 ? RN_BWD_MIN_ROWS_WIDE : 1);
 }
 
-template <class T, class P, bool LN, bool ADD>
+template <class T, class W, class P, bool LN, bool ADD>
 hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *dg,
                          void *db, hipStream_t s) {
     if (!colsum) {
@@ -724,16 +725,16 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
         if (P_ > 0) {
             const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
             hipLaunchKernelGGL(
-                (bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD>),
+                (bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD>),
                 dim3(P_), dim3(P::THREADS), lds, s, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        return launch_bwd2<T>(a.part, P_, a.H, LN, dg, db, s);
+        return launch_bwd2<W>(a.part, P_, a.H, LN, dg, db, s);
     }
     // column sums: kernel 1 writes dx only (forward-style grid), then the
     // column-sum kernel reads x and dy again
-    constexpr auto k = bwd1_kernel<T, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, false, ADD>;
+    constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, false, ADD>;
     const int resident = resident_per_cu<k>(P::THREADS, 0);
     const int grid = persistent_grid<P>(a.N, cus, resident >= 2 ? (1 << 20) : resident, 1);
     hipLaunchKernelGGL(k, dim3(grid), dim3(P::THREADS), 0, s, a);
@@ -741,17 +742,17 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
     if (e != hipSuccess) return e;
     constexpr int VEC = P::VEC;
     constexpr int COLS = 8 * VEC;
-    hipLaunchKernelGGL((bwd_colsum_kernel<T, VEC, LN>), dim3((a.H + COLS - 1) / COLS),
-                       dim3(1024), 0, s, a, (T *)dg, (T *)db);
+    hipLaunchKernelGGL((bwd_colsum_kernel<T, W, VEC, LN>), dim3((a.H + COLS - 1) / COLS),
+                       dim3(1024), 0, s, a, (W *)dg, (W *)db);
     return hipGetLastError();
 }
 
-template <class T, class P>
+template <class T, class W, class P>
 hipError_t launch_bwd_plan(bool ln, bool fused, const BwdArgs &a, int P_, bool colsum,
                            int cus, void *dg, void *db, hipStream_t s) {
-    if (ln) return launch_bwd_ln<T, P, true, false>(a, P_, colsum, cus, dg, db, s);
-    if (fused) return launch_bwd_ln<T, P, false, true>(a, P_, colsum, cus, dg, db, s);
-    return launch_bwd_ln<T, P, false, false>(a, P_, colsum, cus, dg, db, s);
+    if (ln) return launch_bwd_ln<T, W, P, true, false>(a, P_, colsum, cus, dg, db, s);
+    if (fused) return launch_bwd_ln<T, W, P, false, true>(a, P_, colsum, cus, dg, db, s);
+    return launch_bwd_ln<T, W, P, false, false>(a, P_, colsum, cus, dg, db, s);
 }
 
 }  // namespace rn

@@ -33,8 +33,9 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
     return pick_plan_int(PlanList<Ps...>{}, H, f);
 }
 
-// The bf16 plans for the benchmarked row lengths can be overridden at
-// build time (-DRN_FWD_BF16_1024=... etc.) to sweep team shapes.
+// Plans for 2-byte activations (bf16, fp16).  Those for the benchmarked
+// row lengths can be overridden at build time (-DRN_FWD_BF16_1024=... etc.)
+// to sweep team shapes.
 // Forward plans that run one workgroup per row group (several fit per CU)
 // do not prefetch (PF = false): the registers would go unused.
 #ifndef RN_FWD_BF16_1024
@@ -60,7 +61,7 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 #endif
 
 // ------------------------------------------------------------- forward --
-using FwdPlansBf16 = PlanList<Plan<8, 1, 1, 4, false>,     //   512
+using FwdPlans2B = PlanList<Plan<8, 1, 1, 4, false>,     //   512
                               RN_FWD_BF16_1024,            //  1024
                               RN_FWD_BF16_2048,            //  2048
                               RN_FWD_BF16_4096,            //  4096
@@ -80,7 +81,7 @@ using FwdPlansScalar = PlanList<Plan<1, 1, 1, 4>,   //    64
                                 Plan<1, 8, 16, 1>>; //  8192
 
 // ------------------------------------------------------------ backward --
-using BwdPlansBf16 = PlanList<Plan<8, 1, 1, 8>,     //   512
+using BwdPlans2B = PlanList<Plan<8, 1, 1, 8>,     //   512
                               RN_BWD_BF16_1024,     //  1024
                               RN_BWD_BF16_2048,     //  2048
                               Plan<8, 2, 4, 2>,     //  4096
@@ -100,29 +101,47 @@ using BwdPlansScalar = PlanList<Plan<1, 1, 1, 8>,   //    64
                                 Plan<1, 4, 16, 1>,  //  4096
                                 Plan<1, 8, 16, 1>>; //  8192
 
-template <class T, class VecPlans>
+template <class T, class W, class VecPlans>
 hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
                         hipStream_t s) {
-    auto f = [&]<class P>() { return launch_fwd_op<T, P>(op, a, cus, s); };
+    auto f = [&]<class P>() { return launch_fwd_op<T, W, P>(op, a, cus, s); };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(FwdPlansScalar{}, a.H, f);
 }
 
-template <class T, class VecPlans>
+template <class T, class W, class VecPlans>
 int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
-    auto f = [&]<class P>() { return bwd_grid<T, P>(N, H, cus); };
+    auto f = [&]<class P>() { return bwd_grid<T, W, P>(N, H, cus); };
     return vec ? pick_plan_int(VecPlans{}, H, f)
                : pick_plan_int(BwdPlansScalar{}, H, f);
 }
 
-template <class T, class VecPlans>
+template <class T, class W, class VecPlans>
 hipError_t launch_bwd_t(bool ln, bool fused, const BwdArgs &a, bool vec, int P,
                         bool colsum, int cus, void *dg, void *db, hipStream_t s) {
     auto f = [&]<class Pl>() {
-        return launch_bwd_plan<T, Pl>(ln, fused, a, P, colsum, cus, dg, db, s);
+        return launch_bwd_plan<T, W, Pl>(ln, fused, a, P, colsum, cus, dg, db, s);
     };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(BwdPlansScalar{}, a.H, f);
 }
+
+// Body of the translation units: the three entry points for storage pair
+// S = (T activations, W parameters) with the given vector plan lists.
+#define RN_DEFINE_FWD(S, T, W, PLANS)                                              \
+    hipError_t launch_fwd_##S(int op, const FwdArgs &a, bool vec, int cus,         \
+                              hipStream_t s) {                                     \
+        return launch_fwd_t<T, W, PLANS>(op, a, vec, cus, s);                      \
+    }
+#define RN_DEFINE_BWD(S, T, W, PLANS)                                              \
+    int bwd_partials_##S(int64_t N, int H, bool vec, int cus) {                    \
+        return bwd_partials_t<T, W, PLANS>(N, H, vec, cus);                        \
+    }                                                                              \
+    hipError_t launch_bwd_##S(bool ln, bool fused, const BwdArgs &a, bool vec,     \
+                              int cus, int P, bool colsum, void *dgamma,           \
+                              void *dbeta, hipStream_t s) {                        \
+        return launch_bwd_t<T, W, PLANS>(ln, fused, a, vec, P, colsum, cus, dgamma, \
+                                         dbeta, s);                                \
+    }
 
 }  // namespace rn

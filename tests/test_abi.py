@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rownorm.h")
 
 OK, EINVAL, EDTYPE, EOVERLAP, EWORKSPACE, EHIP, EUNSUP = 0, -1, -2, -3, -4, -5, -6
-F32, BF16 = 0, 1
+F32, BF16, F16, BF16_F32W, F16_F32W = 0, 1, 2, 3, 4
 
 
 @pytest.fixture(scope="module")
@@ -59,7 +59,10 @@ def test_max_hidden(L):
     assert L.rn_max_hidden(BF16, 1) == 16384
     assert L.rn_max_hidden(F32, 1) == 16384
     assert L.rn_max_hidden(BF16, 0) == 8192
+    for dt in (F16, BF16_F32W, F16_F32W):
+        assert L.rn_max_hidden(dt, 1) == 16384
     assert L.rn_max_hidden(9, 1) == 0
+    assert L.rn_max_hidden(5, 1) == 0
 
 
 A = 1 << 30          # fake device addresses, far apart, 256-byte aligned
@@ -100,7 +103,8 @@ def test_rms_fwd_argument_errors(L):
     assert L.rms_fwd(X, 64, G, Y, 64, R, 4, 64, BF16, 0.0, S) == EINVAL
     assert L.rms_fwd(X, 64, G, X, 64, R, 4, 64, BF16, 1e-6, S) == EOVERLAP
     assert L.rms_fwd(X, 64, G, Y, 64, None, 0, 64, F32, 1e-6, S) == OK
-    assert L.rms_fwd(X, 64, G, Y, 64, None, 4, 64, 3, 1e-6, S) == EDTYPE
+    assert L.rms_fwd(X, 64, G, Y, 64, None, 4, 64, 5, 1e-6, S) == EDTYPE
+    assert L.rms_fwd(X, 64, G, Y, 64, None, 4, 64, -1, 1e-6, S) == EDTYPE
 
 
 def fused(L, x=X, ldx=4096, res=RES, ldr=4096, g=G, y=Y, ldy=4096, h=H_,
@@ -196,9 +200,33 @@ def fused_bwd(L, dy=DY, lddy=1024, h=H_, ldh=1024, g=G, r=R, dh=DH, lddh=1024,
     (dict(r=None), EINVAL), (dict(h=None), EINVAL), (dict(dg=None), EINVAL),
     (dict(dh=DH + 1), EINVAL), (dict(dres=RES + 1), EINVAL),
     (dict(lddh=1000), EINVAL), (dict(lddres=512), EINVAL),
-    (dict(eps=0.0), EINVAL), (dict(dt=4), EDTYPE),
+    (dict(eps=0.0), EINVAL), (dict(dt=5), EDTYPE),
     (dict(H=16385, lddy=16385, ldh=16385, lddx=16385, lddh=16385,
           lddres=16385), EUNSUP),
 ])
 def test_fused_bwd_argument_errors(L, kw, want):
     assert fused_bwd(L, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    # float32 parameters beside 16-bit activations: gamma/beta 4-byte
+    # aligned, and their extent is 4*H bytes
+    (dict(dt=BF16_F32W, g=G + 2), EINVAL),
+    (dict(dt=F16_F32W, b=B + 2), EINVAL),
+    (dict(dt=BF16_F32W, x=X + 2), OK),        # 2-byte activations: fine
+    (dict(dt=BF16_F32W, y=G + 2048), EOVERLAP),   # inside gamma's 4 KiB
+    (dict(dt=F16, g=G + 1), EINVAL),
+    (dict(dt=F16, m=R), EOVERLAP),
+])
+def test_mixed_param_argument_checks(L, kw, want):
+    if want == OK:
+        kw["N"] = 0     # valid: N = 0 returns before touching the device
+    assert ln_fwd(L, **kw) == want
+
+
+def test_mixed_param_backward_checks(L):
+    # dgamma float32 with bf16 activations: 4-aligned, 4*H bytes long
+    assert ln_bwd(L, dt=BF16_F32W, dg=DG + 2) == EINVAL
+    assert ln_bwd(L, dt=BF16_F32W, db=DG + 2048) == EOVERLAP
+    assert fused_bwd(L, dt=F16_F32W, dg=DG + 2) == EINVAL
+    assert fused_bwd(L, dt=F16_F32W, dx=G + 2048) == EOVERLAP

@@ -19,17 +19,27 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def to_dev(a):
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def to_dev(a, dt="bf16"):
+    """Storage array -> GPU tensor; uint16 patterns are bf16 or fp16 (dt),
+    float32 arrays stay float32 whatever dt says."""
     if a.dtype == np.uint16:
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+        return torch.from_numpy(a.view(np.int16)).view(TORCH_DT[dt]).to(DEV)
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
 def host(t):
     t = t.detach().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def pdt(arr, dtype):
+    """Storage type of the parameters: float32 or the activation type."""
+    return "f32" if arr["gamma"].dtype == np.float32 else dtype
 
 
 def sample_rows(N, k=96, seed=0):
@@ -39,14 +49,14 @@ def sample_rows(N, k=96, seed=0):
 
 
 def dec(orc, arr, k, dtype):
-    return orc.decode(arr[k], dtype)
+    return orc.decode(arr[k], pdt(arr, dtype) if k in ("gamma", "beta") else dtype)
 
 
 # ----------------------------------------------------------------- helpers --
 def check_ln_fwd(orc, arr, dtype, eps, rows=None, use_beta=True):
-    x = to_dev(arr["x"])
-    g = to_dev(arr["gamma"])
-    b = to_dev(arr["beta"]) if (use_beta and "beta" in arr) else None
+    x = to_dev(arr["x"], dtype)
+    g = to_dev(arr["gamma"], dtype)
+    b = to_dev(arr["beta"], dtype) if (use_beta and "beta" in arr) else None
     y, mean, rstd = rn.ln_fwd(x, g, b, eps)
     torch.cuda.synchronize()
     rows = np.arange(arr["x"].shape[0]) if rows is None else rows
@@ -62,8 +72,8 @@ def check_ln_fwd(orc, arr, dtype, eps, rows=None, use_beta=True):
 
 
 def check_rms_fwd(orc, arr, dtype, eps, rows=None):
-    x = to_dev(arr["x"])
-    g = to_dev(arr["gamma"])
+    x = to_dev(arr["x"], dtype)
+    g = to_dev(arr["gamma"], dtype)
     y, rstd = rn.rms_fwd(x, g, eps)
     torch.cuda.synchronize()
     rows = np.arange(arr["x"].shape[0]) if rows is None else rows
@@ -77,14 +87,14 @@ def check_rms_fwd(orc, arr, dtype, eps, rows=None):
 
 def check_bwd(orc, arr, dtype, eps, layernorm, rows=None):
     """GPU forward (for the saved stats), GPU backward, oracle backward."""
-    x = to_dev(arr["x"])
-    dy = to_dev(arr["dy"])
-    g = to_dev(arr["gamma"])
+    x = to_dev(arr["x"], dtype)
+    dy = to_dev(arr["dy"], dtype)
+    g = to_dev(arr["gamma"], dtype)
     N = arr["x"].shape[0]
     e = oracle.eps_at_boundary(eps)
     xd = orc.decode(arr["x"], dtype)
     dyd = orc.decode(arr["dy"], dtype)
-    gd = orc.decode(arr["gamma"], dtype)
+    gd = dec(orc, arr, "gamma", dtype)
     rows = np.arange(N) if rows is None else rows
     if layernorm:
         _, mean, rstd = rn.ln_fwd(x, g, None, eps)
@@ -96,11 +106,12 @@ def check_bwd(orc, arr, dtype, eps, layernorm, rows=None):
         dx, dg = rn.rms_bwd(dy, x, g, rstd, eps)
         torch.cuda.synchronize()
         dx_o, dg_o, rstd_o = orc.rms_bwd(dyd, xd, gd, e)
+    assert dg.dtype == TORCH_DT[pdt(arr, dtype)] and dx.dtype == TORCH_DT[dtype]
     ts = tol.dx_term_scale(dyd[rows], gd, rstd_o[rows])
     stats = tol.check_out(host(dx)[rows], dx_o[rows], dtype, orc, "dx", term_scale=ts)
-    rr = tol.check_param(orc.decode(host(dg), dtype), dg_o, "dgamma")
+    rr = tol.check_param(orc.decode(host(dg), pdt(arr, dtype)), dg_o, "dgamma")
     if layernorm:
-        tol.check_param(orc.decode(host(db), dtype), db_o, "dbeta")
+        tol.check_param(orc.decode(host(db), pdt(arr, dtype)), db_o, "dbeta")
     return stats, rr
 
 
@@ -109,7 +120,7 @@ def fused_bwd_oracle(orc, arr, dtype, eps, with_dh=True):
     (RNE of the exact sum) and the saved rstd (of the exact sum)."""
     e = oracle.eps_at_boundary(eps)
     xd, rd = orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype)
-    gd, dyd = orc.decode(arr["gamma"], dtype), orc.decode(arr["dy"], dtype)
+    gd, dyd = dec(orc, arr, "gamma", dtype), orc.decode(arr["dy"], dtype)
     _, h_o, rs_o = orc.fused_add_rms_fwd(xd, rd, gd, e)
     h_stored = orc.decode(orc.encode(h_o, dtype), dtype)
     dhd = orc.decode(arr["dh"], dtype) if with_dh else None
@@ -120,9 +131,9 @@ def fused_bwd_oracle(orc, arr, dtype, eps, with_dh=True):
 def check_fused_bwd(orc, arr, dtype, eps, rows=None, with_dh=True,
                     write_dres=True, in_place=False):
     """GPU fused forward (h, rstd), GPU fused backward, oracle backward."""
-    x, r, g, dy = (to_dev(arr[k]) for k in ("x", "residual", "gamma", "dy"))
+    x, r, g, dy = (to_dev(arr[k], dtype) for k in ("x", "residual", "gamma", "dy"))
     _, h, rstd = rn.fused_add_rms_fwd(x, r, g, eps)
-    dh = to_dev(arr["dh"]) if with_dh else None
+    dh = to_dev(arr["dh"], dtype) if with_dh else None
     dx, dres, dg = rn.fused_add_rms_bwd(
         dy, h, g, rstd, eps, dh_in=dh, dx=dh if in_place else None,
         write_dres=write_dres)
@@ -139,7 +150,7 @@ def check_fused_bwd(orc, arr, dtype, eps, rows=None, with_dh=True,
         assert torch.equal(dres, dx), "dres differs from dx"
     else:
         assert dres is None
-    rr = tol.check_param(orc.decode(host(dg), dtype), dg_o, "fused dgamma")
+    rr = tol.check_param(orc.decode(host(dg), pdt(arr, dtype)), dg_o, "fused dgamma")
     return stats, rr
 
 
@@ -193,6 +204,21 @@ def test_fused_bwd_bf16_32768x4096(orc):
     check_fused_bwd(orc, arr, "bf16", w.eps, rows=sample_rows(w.N))
 
 
+@pytest.mark.parametrize("name", ["mixed_bf16_f32w_32768x1024", "f16_32768x1024"])
+def test_storage_workloads(orc, name):
+    """Full-size runs of the float32-parameter and fp16 paths: every op,
+    sampled rows, parameter gradients over all rows."""
+    w = synth.WORKLOADS[name]
+    arr = synth.generate(w)
+    rows = sample_rows(w.N)
+    y, _, _, _ = check_ln_fwd(orc, arr, w.dtype, w.eps, rows=rows)
+    assert y.dtype == TORCH_DT[w.dtype]
+    check_rms_fwd(orc, arr, w.dtype, w.eps, rows=rows)
+    check_bwd(orc, arr, w.dtype, w.eps, layernorm=True, rows=rows)
+    check_bwd(orc, arr, w.dtype, w.eps, layernorm=False, rows=rows)
+    check_fused_bwd(orc, arr, w.dtype, w.eps, rows=rows)
+
+
 BWD = ["bwd_bf16_32768x1024", "bwd_bf16_16384x2048", "bwd_bf16_512x16384",
        "bwd_bf16_2048x16384"]
 
@@ -217,20 +243,25 @@ SHAPES = [64, 128, 512, 768, 1024, 2049, 1, 2, 3, 1000, 3000, 4095, 4096,
           8192, 12288, 16384]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+# storage pairs: activations[/parameters]
+STORAGE = ["bf16", "f32", "f16", "bf16/f32", "f16/f32"]
+
+
+@pytest.mark.parametrize("storage", STORAGE)
 @pytest.mark.parametrize("H", SHAPES)
-def test_shapes_all_ops(orc, dtype, H):
+def test_shapes_all_ops(orc, storage, H):
     N = 67 if H <= 4096 else 19
-    arr = synth.custom(100 + H, N, H, dtype)
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(100 + H, N, H, dtype, wdtype=wdt or None)
     check_ln_fwd(orc, arr, dtype, 1e-5)
     check_rms_fwd(orc, arr, dtype, 1e-5)
     check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
     check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
-    x, r, g = (to_dev(arr[k]) for k in ("x", "residual", "gamma"))
+    x, r, g = (to_dev(arr[k], dtype) for k in ("x", "residual", "gamma"))
     y, h, rstd = rn.fused_add_rms_fwd(x, r, g, 1e-6)
     torch.cuda.synchronize()
     xd, rd = orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype)
-    y_o, h_o, r_o = orc.fused_add_rms_fwd(xd, rd, orc.decode(arr["gamma"], dtype),
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(xd, rd, dec(orc, arr, "gamma", dtype),
                                           oracle.eps_at_boundary(1e-6))
     assert np.array_equal(host(h), orc.encode(h_o, dtype))
     tol.check_out(host(y), y_o, dtype, orc, "fused y")
