@@ -635,6 +635,7 @@ struct Plan {
     static constexpr bool PF = PF_;   // prefetch the next row into registers
     static constexpr int SPAN = 64 * TW_ * VEC_ * CPL_;
     static constexpr int THREADS = 64 * TW_ * RT_;
+    static constexpr int SEG = 0;     // not a several-rows-per-wave plan
 };
 
 // Workgroups of kernel K (with `threads` threads and `lds` bytes of dynamic

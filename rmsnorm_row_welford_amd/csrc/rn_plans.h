@@ -7,9 +7,100 @@
 // element-wise (VEC = 1) plans.
 #pragma once
 
+#include <initializer_list>
+
 #include "rn_kernels.h"
+#include "rn_seg.h"
 
 namespace rn {
+
+// ------------------------------------------------ several rows per wave --
+// Rows of at most SEG*VEC elements: SEG lanes per row, 64/SEG rows per wave,
+// WPG waves per workgroup, IT row groups per wave in the forward.  Row
+// strides too large for 32-bit group offsets fall back to one row per wave.
+template <int VEC_, int SEG_, int WPG_, int IT_>
+struct SegPlan {
+    static constexpr int VEC = VEC_, SEG = SEG_, WPG = WPG_, IT = IT_;
+    static constexpr int RPW = 64 / SEG_;
+    static constexpr int SPAN = SEG_ * VEC_;
+    static constexpr int THREADS = 64 * WPG_;
+    using Fallback = Plan<VEC_, 1, 1, 4, false>;
+};
+
+inline bool seg_fits(int rpw, int e, std::initializer_list<int64_t> lds) {
+    for (int64_t ld : lds)
+        if (ld * e * rpw >= ((int64_t)1 << 31)) return false;
+    return true;
+}
+
+template <class T, class W, class P, int OP>
+hipError_t launch_fwd_seg(const FwdArgs &a, hipStream_t s) {
+    constexpr int rows = P::WPG * P::RPW * P::IT;
+    const int64_t grid = (a.N + rows - 1) / rows;
+    hipLaunchKernelGGL((fwd_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, P::IT, OP>),
+                       dim3((unsigned)grid), dim3(P::THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class T, class W, class P>
+hipError_t launch_fwd_any(int op, const FwdArgs &a, int cus, hipStream_t s) {
+    if constexpr (P::SEG > 0) {
+        if (seg_fits(P::RPW, (int)sizeof(T), {a.ldx, a.ldr, a.ldy, a.ldh})) {
+            switch (op) {
+            case OP_LN: return launch_fwd_seg<T, W, P, OP_LN>(a, s);
+            case OP_RMS: return launch_fwd_seg<T, W, P, OP_RMS>(a, s);
+            default: return launch_fwd_seg<T, W, P, OP_FUSED>(a, s);
+            }
+        }
+        return launch_fwd_op<T, W, typename P::Fallback>(op, a, cus, s);
+    } else {
+        return launch_fwd_op<T, W, P>(op, a, cus, s);
+    }
+}
+
+// Kernel 1's workgroup count (= partial rows) of a several-rows-per-wave
+// plan; its one-row-per-wave fallback runs with the same count.
+template <class T, class W, class P>
+int bwd_grid_any(int64_t N, int H, int cus) {
+    if constexpr (P::SEG > 0) {
+        constexpr auto k = bwd1_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, true, false>;
+        const int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU
+                                             : resident_per_cu<k>(P::THREADS, 0);
+        const int64_t groups = (N + P::RPW * P::WPG - 1) / (P::RPW * P::WPG);
+        const int64_t cap = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
+        return (int)(groups < cap ? groups : cap);
+    } else {
+        return bwd_grid<T, W, P>(N, H, cus);
+    }
+}
+
+template <class T, class W, class P, bool LN, bool ADD>
+hipError_t launch_bwd_seg(const BwdArgs &a, int P_, void *dg, void *db, hipStream_t s) {
+    if (P_ > 0) {
+        hipLaunchKernelGGL((bwd1_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, LN, ADD>),
+                           dim3(P_), dim3(P::THREADS), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_bwd2<W>(a.part, P_, a.H, LN, dg, db, s);
+}
+
+template <class T, class W, class P>
+hipError_t launch_bwd_any(bool ln, bool fused, const BwdArgs &a, int P_, bool colsum,
+                          int cus, void *dg, void *db, hipStream_t s) {
+    if constexpr (P::SEG > 0) {
+        if (!colsum && seg_fits(P::RPW, (int)sizeof(T),
+                                {a.lddy, a.ldx, a.lddx, a.ldadd, a.lddx2})) {
+            if (ln) return launch_bwd_seg<T, W, P, true, false>(a, P_, dg, db, s);
+            if (fused) return launch_bwd_seg<T, W, P, false, true>(a, P_, dg, db, s);
+            return launch_bwd_seg<T, W, P, false, false>(a, P_, dg, db, s);
+        }
+        return launch_bwd_plan<T, W, typename P::Fallback>(ln, fused, a, P_, colsum, cus,
+                                                           dg, db, s);
+    } else {
+        return launch_bwd_plan<T, W, P>(ln, fused, a, P_, colsum, cus, dg, db, s);
+    }
+}
 
 // Walk a list of plans and run `f.template operator()<P>()` on the first
 // plan whose span covers H.
@@ -61,41 +152,59 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 #endif
 
 // ------------------------------------------------------------- forward --
-using FwdPlans2B = PlanList<Plan<8, 1, 1, 4, false>,     //   512
+using FwdPlans2B = PlanList<SegPlan<8, 8, 4, 2>,          //    64
+                            SegPlan<8, 16, 4, 2>,         //   128
+                            SegPlan<8, 32, 4, 2>,         //   256
+                            Plan<8, 1, 1, 4, false>,      //   512
                               RN_FWD_BF16_1024,            //  1024
                               RN_FWD_BF16_2048,            //  2048
                               RN_FWD_BF16_4096,            //  4096
                               Plan<8, 2, 8, 1, false>,     //  8192
                               RN_FWD_BF16_16384>;          // 16384
-using FwdPlansF32 = PlanList<Plan<4, 1, 1, 4, false>,      //   256
+using FwdPlansF32 = PlanList<SegPlan<4, 8, 4, 2>,         //    32
+                             SegPlan<4, 16, 4, 2>,        //    64
+                             SegPlan<4, 32, 4, 2>,        //   128
+                             Plan<4, 1, 1, 4, false>,      //   256
                              Plan<4, 2, 1, 4, false>,      //   512
                              Plan<4, 4, 1, 4, false>,      //  1024
                              Plan<4, 4, 2, 2, false>,      //  2048
                              Plan<4, 4, 4, 1, false>,      //  4096
                              Plan<4, 4, 8, 1, false>,      //  8192
                              Plan<4, 4, 16, 1>>;           // 16384
-using FwdPlansScalar = PlanList<Plan<1, 1, 1, 4>,   //    64
+using FwdPlansScalar = PlanList<SegPlan<1, 8, 4, 2>,   //     8
+                                SegPlan<1, 16, 4, 2>,  //    16
+                                SegPlan<1, 32, 4, 2>,  //    32
+                                Plan<1, 1, 1, 4>,   //    64
                                 Plan<1, 4, 1, 4>,   //   256
                                 Plan<1, 4, 4, 1>,   //  1024
                                 Plan<1, 4, 16, 1>,  //  4096
                                 Plan<1, 8, 16, 1>>; //  8192
 
 // ------------------------------------------------------------ backward --
-using BwdPlans2B = PlanList<Plan<8, 1, 1, 8>,     //   512
+using BwdPlans2B = PlanList<SegPlan<8, 8, 4, 1>,    //    64
+                            SegPlan<8, 16, 4, 1>,   //   128
+                            SegPlan<8, 32, 4, 1>,   //   256
+                            Plan<8, 1, 1, 8>,       //   512
                               RN_BWD_BF16_1024,     //  1024
                               RN_BWD_BF16_2048,     //  2048
                               Plan<8, 2, 4, 2>,     //  4096
                               Plan<8, 2, 8, 1>,     //  8192
                               RN_BWD_BF16_16384>;   // 16384
 // float32 rows of 16 elements per lane are too wide to double-buffer.
-using BwdPlansF32 = PlanList<Plan<4, 1, 1, 8>,             //   256
+using BwdPlansF32 = PlanList<SegPlan<4, 8, 4, 1>,          //    32
+                             SegPlan<4, 16, 4, 1>,         //    64
+                             SegPlan<4, 32, 4, 1>,         //   128
+                             Plan<4, 1, 1, 8>,             //   256
                              Plan<4, 2, 1, 8>,             //   512
                              Plan<4, 4, 1, 8, false>,      //  1024
                              Plan<4, 4, 2, 4, false>,      //  2048
                              Plan<4, 4, 4, 2, false>,      //  4096
                              Plan<4, 4, 8, 1, false>,      //  8192
                              Plan<4, 4, 16, 1, false>>;    // 16384
-using BwdPlansScalar = PlanList<Plan<1, 1, 1, 8>,   //    64
+using BwdPlansScalar = PlanList<SegPlan<1, 8, 4, 1>,   //     8
+                                SegPlan<1, 16, 4, 1>,  //    16
+                                SegPlan<1, 32, 4, 1>,  //    32
+                                Plan<1, 1, 1, 8>,   //    64
                                 Plan<1, 4, 1, 8>,   //   256
                                 Plan<1, 4, 4, 2>,   //  1024
                                 Plan<1, 4, 16, 1>,  //  4096
@@ -104,14 +213,14 @@ using BwdPlansScalar = PlanList<Plan<1, 1, 1, 8>,   //    64
 template <class T, class W, class VecPlans>
 hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
                         hipStream_t s) {
-    auto f = [&]<class P>() { return launch_fwd_op<T, W, P>(op, a, cus, s); };
+    auto f = [&]<class P>() { return launch_fwd_any<T, W, P>(op, a, cus, s); };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(FwdPlansScalar{}, a.H, f);
 }
 
 template <class T, class W, class VecPlans>
 int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
-    auto f = [&]<class P>() { return bwd_grid<T, W, P>(N, H, cus); };
+    auto f = [&]<class P>() { return bwd_grid_any<T, W, P>(N, H, cus); };
     return vec ? pick_plan_int(VecPlans{}, H, f)
                : pick_plan_int(BwdPlansScalar{}, H, f);
 }
@@ -120,7 +229,7 @@ template <class T, class W, class VecPlans>
 hipError_t launch_bwd_t(bool ln, bool fused, const BwdArgs &a, bool vec, int P,
                         bool colsum, int cus, void *dg, void *db, hipStream_t s) {
     auto f = [&]<class Pl>() {
-        return launch_bwd_plan<T, W, Pl>(ln, fused, a, P, colsum, cus, dg, db, s);
+        return launch_bwd_any<T, W, Pl>(ln, fused, a, P, colsum, cus, dg, db, s);
     };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(BwdPlansScalar{}, a.H, f);

@@ -1,0 +1,270 @@
+// Short rows: several rows per wavefront.
+//
+// For rows of at most SEG*VEC elements a wave is cut into 64/SEG segments of
+// SEG lanes (SEG = 8, 16 or 32); segment s owns one row and lane sl of it
+// holds the chunk of VEC elements starting at sl*VEC.  All lanes of a wave
+// stay busy on rows far shorter than the wave's 64*VEC-element reach, and a
+// wave moves 64 chunks per access instead of H/VEC.
+//
+// Addressing.  A buffer resource must be wave-uniform, so it covers the
+// wave's whole group of rows [row0, row0 + n): it starts at row row0 and ends
+// at the last row's H-th element.  Lane offsets are s*ld + sl*VEC elements;
+// a chunk at or past H gets an offset beyond every group's range, so it
+// loads as 0 and its store is dropped, and rows of the group at or past N
+// fall beyond the resource's end the same way.  The host uses these kernels
+// only when (64/SEG)*ld*sizeof(T) < 2^31 for every row tensor, so offsets fit
+// in 32 bits.
+//
+// Statistics are the row-per-wave kernels' (two-pass over register values,
+// LayerNorm shifted by the row's first element), with sums over a segment
+// instead of a wave.
+#pragma once
+
+#include "rn_kernels.h"
+
+namespace rn {
+
+// Sum over aligned groups of SEG lanes; every lane of a group receives the
+// group's sum, with the same bits in each lane (the steps pair lanes
+// symmetrically, as in wave_sum).  All 64 lanes must be active.
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+    static_assert(SEG == 8 || SEG == 16 || SEG == 32, "segments of 8, 16 or 32 lanes");
+    v += dpp<DPP_QUAD_XOR1>(v);
+    v += dpp<DPP_QUAD_XOR2>(v);
+    v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (SEG >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+    if constexpr (SEG >= 32) v += swizzle_xor16(v);
+    return v;
+}
+
+// The value lane `src` holds, fetched by every lane (ds_bpermute).
+__device__ __forceinline__ float lane_pull(float v, int src) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+constexpr uint32_t kOffOOB = 0x80000000u;   // beyond every group's range
+
+// Resource over rows [row0, row0 + n) (n >= 1) of a tensor with row stride ld.
+template <class T>
+__device__ __forceinline__ rsrc_t group_rsrc(const void *base, int64_t row0, int n,
+                                             int64_t ld, int H) {
+    const T *p = (const T *)base + row0 * ld;
+    return make_rsrc(p, (uint32_t)(((int64_t)(n - 1) * ld + H) * (int64_t)sizeof(T)));
+}
+
+// Byte offset of lane (seg, sl)'s chunk, or kOffOOB when the chunk is past H.
+template <class T, int VEC>
+__device__ __forceinline__ uint32_t seg_off(int seg, int sl, int64_t ld, bool valid) {
+    return valid ? (uint32_t)(((int64_t)seg * ld + sl * VEC) * (int64_t)sizeof(T)) : kOffOOB;
+}
+
+// Forward.  Wave w of workgroup b owns IT consecutive groups of 64/SEG rows
+// starting at row ((b*WPG + w)*IT)*(64/SEG); all IT groups are requested
+// before the first is reduced.  One workgroup per WPG*IT groups (not
+// persistent): the dispatcher keeps every CU fed.
+template <class T, class W, int VEC, int SEG, int WPG, int IT, int OP>
+__global__ __launch_bounds__(64 * WPG) void fwd_seg_kernel(const FwdArgs a) {
+    constexpr int RPW = 64 / SEG;
+    using Raw = RawChunk<T, VEC>;
+    using RawW = RawChunk<W, VEC>;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id_uniform();
+    const int seg = lane / SEG, sl = lane % SEG;
+    const int H = a.H;
+    const int64_t N = a.N;
+    const bool valid = sl * VEC < H;
+    const int64_t wrow = ((int64_t)blockIdx.x * WPG + wave) * (IT * RPW);
+    if (wrow >= N) return;   // wave-uniform; no barriers below
+
+    RawW g, bt;
+    const uint32_t poff = valid ? (uint32_t)(sl * VEC * (int)sizeof(W)) : kOffOOB;
+    g.template bload<0>(row_rsrc((const W *)a.gamma, H), poff);
+    if constexpr (OP == OP_LN) {
+        if (a.beta != nullptr) bt.template bload<0>(row_rsrc((const W *)a.beta, H), poff);
+        else bt.zero();
+    }
+
+    Raw cx[IT], cr[(OP == OP_FUSED) ? IT : 1];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int64_t row0 = wrow + (int64_t)i * RPW;
+        if (row0 < N) {
+            const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
+            cx[i].template bload<RN_LOAD_AUX>(group_rsrc<T>(a.x, row0, n, a.ldx, H),
+                                              seg_off<T, VEC>(seg, sl, a.ldx, valid));
+            if constexpr (OP == OP_FUSED)
+                cr[i].template bload<RN_LOAD_AUX>(group_rsrc<T>(a.res, row0, n, a.ldr, H),
+                                                  seg_off<T, VEC>(seg, sl, a.ldr, valid));
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int64_t row0 = wrow + (int64_t)i * RPW;
+        if (row0 >= N) break;
+        const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
+        float v[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            v[k] = cx[i].get(k);
+            if constexpr (OP == OP_FUSED) v[k] += cr[i].get(k);
+        }
+        // h goes out before y; every element of this lane is already loaded,
+        // so h may alias x or the residual.
+        if constexpr (OP == OP_FUSED)
+            bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.h, row0, n, a.ldh, H),
+                              seg_off<T, VEC>(seg, sl, a.ldh, valid), v);
+
+        float mean = 0.0f, var;
+        if constexpr (OP == OP_LN) {
+            const float pivot = lane_pull(v[0], seg * SEG);   // the row's first element
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                v[k] = valid ? v[k] - pivot : 0.0f;
+                s += v[k];
+            }
+            const float ms = seg_sum<SEG>(s) * a.inv_H;
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                v[k] = valid ? v[k] - ms : 0.0f;   // x - mean
+                q = __builtin_fmaf(v[k], v[k], q);
+            }
+            var = seg_sum<SEG>(q) * a.inv_H;
+            mean = pivot + ms;
+        } else {
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) q = __builtin_fmaf(v[k], v[k], q);
+            var = seg_sum<SEG>(q) * a.inv_H;
+        }
+        const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
+
+        float out[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            if constexpr (OP == OP_LN)
+                out[k] = __builtin_fmaf(v[k] * rstd, g.get(k), bt.get(k));
+            else
+                out[k] = (v[k] * rstd) * g.get(k);
+        }
+        bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.y, row0, n, a.ldy, H),
+                          seg_off<T, VEC>(seg, sl, a.ldy, valid), out);
+        if (sl == 0 && seg < n) {
+            if constexpr (OP == OP_LN) {
+                if (a.mean) a.mean[row0 + seg] = mean;
+            }
+            if (a.rstd) a.rstd[row0 + seg] = rstd;
+        }
+    }
+}
+
+// Backward kernel 1.  Persistent: wave w of workgroup b takes row groups
+// b*WPG + w, += gridDim.x*WPG, each of 64/SEG rows; every lane accumulates
+// dy*x_hat (and dy) for its VEC columns over all its rows.  At the end the
+// WPG*(64/SEG) segments of the workgroup are added column-wise through LDS,
+// in segment order, into ONE float32 partial row (two for LayerNorm), as in
+// bwd1_kernel.  ADD: the fused add+RMSNorm variant (a.add added to dx, a.dx2
+// a second copy).
+template <class T, class W, int VEC, int SEG, int WPG, bool LN, bool ADD>
+__global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
+    static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
+    constexpr int RPW = 64 / SEG;
+    constexpr int SPAN = SEG * VEC;
+    constexpr int SLOTS = WPG * RPW;
+    using Raw = RawChunk<T, VEC>;
+    __shared__ float acc[SLOTS * SPAN];
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id_uniform();
+    const int seg = lane / SEG, sl = lane % SEG;
+    const int H = a.H;
+    const int64_t N = a.N;
+    const bool valid = sl * VEC < H;
+
+    RawChunk<W, VEC> g;
+    g.template bload<0>(row_rsrc((const W *)a.gamma, H),
+                        valid ? (uint32_t)(sl * VEC * (int)sizeof(W)) : kOffOOB);
+    float adg[VEC], adb[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) adg[k] = adb[k] = 0.0f;
+    const T *addb = (const T *)a.add;
+    const bool has_add = ADD && addb != nullptr;
+
+    const int64_t gstep = (int64_t)gridDim.x * WPG;
+    for (int64_t gi = (int64_t)blockIdx.x * WPG + wave; gi * RPW < N; gi += gstep) {
+        const int64_t row0 = gi * RPW;
+        const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
+        Raw cx, cdy, cad;
+        cx.template bload<RN_LOAD_AUX>(group_rsrc<T>(a.x, row0, n, a.ldx, H),
+                                       seg_off<T, VEC>(seg, sl, a.ldx, valid));
+        cdy.template bload<RN_LOAD_AUX>(group_rsrc<T>(a.dy, row0, n, a.lddy, H),
+                                        seg_off<T, VEC>(seg, sl, a.lddy, valid));
+        if constexpr (ADD) {
+            if (has_add)
+                cad.template bload<RN_LOAD_AUX>(group_rsrc<T>(addb, row0, n, a.ldadd, H),
+                                                seg_off<T, VEC>(seg, sl, a.ldadd, valid));
+            else
+                cad.zero();
+        }
+        const bool live = seg < n;
+        const float mu = (LN && live) ? a.mean[row0 + seg] : 0.0f;
+        const float s = live ? a.rstd[row0 + seg] : 0.0f;
+
+        // Masked elements and rows past N have dy = 0 and add nothing.
+        float sg = 0.0f, sgx = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float dyv = cdy.get(k);
+            const float xhat = (cx.get(k) - mu) * s;
+            const float gv = dyv * g.get(k);
+            adg[k] = __builtin_fmaf(dyv, xhat, adg[k]);
+            if constexpr (LN) adb[k] += dyv;
+            sg += gv;
+            sgx = __builtin_fmaf(gv, xhat, sgx);
+        }
+        if constexpr (LN) sg = seg_sum<SEG>(sg);
+        sgx = seg_sum<SEG>(sgx);
+        const float c1 = LN ? sg * a.inv_H : 0.0f;
+        const float c2 = sgx * a.inv_H;
+        float dx[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float xhat = (cx.get(k) - mu) * s;
+            float t = cdy.get(k) * g.get(k);
+            if constexpr (LN) t -= c1;
+            dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
+            if constexpr (ADD) dx[k] += cad.get(k);
+        }
+        bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.dx, row0, n, a.lddx, H),
+                          seg_off<T, VEC>(seg, sl, a.lddx, valid), dx);
+        if constexpr (ADD) {
+            if (a.dx2 != nullptr)
+                bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.dx2, row0, n, a.lddx2, H),
+                                  seg_off<T, VEC>(seg, sl, a.lddx2, valid), dx);
+        }
+    }
+
+    // Partial rows: slot (wave, seg) parks its accumulators, then each
+    // thread adds one column over the slots in order.
+    const int slot = wave * RPW + seg;
+#pragma unroll
+    for (int p = 0; p < (LN ? 2 : 1); ++p) {
+        const float *src = p == 0 ? adg : adb;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[slot * SPAN + sl * VEC + k] = src[k];
+        __syncthreads();
+        float *dst = a.part + ((int64_t)p * gridDim.x + blockIdx.x) * H;
+        for (int col = threadIdx.x; col < H; col += 64 * WPG) {
+            float t = acc[col];
+#pragma unroll 8
+            for (int j = 1; j < SLOTS; ++j) t += acc[j * SPAN + col];
+            dst[col] = t;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace rn

@@ -38,6 +38,10 @@ shapes and test lists describe them):
                        activations and float32 gamma, beta, dgamma, dbeta;
                        distributions as step_bf16_32768x1024
   f16_32768x1024       the same in IEEE binary16 throughout
+  rows_bf16_1048576x128  short rows (a normalization over a 128-wide head
+                       dimension of 2^20 token-head rows): LayerNorm and
+                       RMSNorm fwd+bwd, bf16, x, dy ~ N(0,1),
+                       gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1), eps 1e-5
   bwd_bf16_32768x1024, bwd_bf16_16384x2048  (tall-narrow)
   bwd_bf16_512x16384,  bwd_bf16_2048x16384  (wide)
                        LayerNorm and RMSNorm fwd+bwd, bf16; x, dy ~ N(0,1),
@@ -95,6 +99,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("f16_32768x1024", 1008, 32768, 1024, "f16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1),
                  residual=(0.0, 1.0), dh=(0.0, 1.0)),
+        Workload("rows_bf16_1048576x128", 1009, 1 << 20, 128, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         Workload("bwd_bf16_16384x2048", 1004, 16384, 2048, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         Workload("bwd_bf16_512x16384", 1005, 512, 16384, "bf16", 1e-5,

@@ -269,6 +269,36 @@ def test_shapes_all_ops(orc, storage, H):
     check_fused_bwd(orc, arr, dtype, 1e-6)
 
 
+# Short rows, several per wave: every segment width (8, 16, 32 lanes) on the
+# 16-byte path and the element-wise path, ragged in N against the rows a
+# workgroup holds.
+SHORT = [8, 16, 24, 32, 40, 56, 96, 136, 200, 256, 5, 7, 17, 31, 33, 63]
+
+
+@pytest.mark.parametrize("storage", ["bf16", "f32", "f16/f32"])
+@pytest.mark.parametrize("H", SHORT)
+def test_short_rows(orc, storage, H):
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(300 + H, 333, H, dtype, wdtype=wdt or None)
+    check_ln_fwd(orc, arr, dtype, 1e-5)
+    check_rms_fwd(orc, arr, dtype, 1e-5)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
+    check_fused_bwd(orc, arr, dtype, 1e-6)
+
+
+def test_qk_norm_bf16_1048576x128(orc):
+    """Head-dimension rows (a million rows of 128): sampled rows against the
+    oracle, parameter gradients over all rows."""
+    w = synth.WORKLOADS["rows_bf16_1048576x128"]
+    arr = synth.generate(w)
+    rows = sample_rows(w.N, k=200)
+    check_ln_fwd(orc, arr, "bf16", w.eps, rows=rows)
+    check_rms_fwd(orc, arr, "bf16", w.eps, rows=rows)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=True, rows=rows)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=False, rows=rows)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_small_variance_rows(orc, dtype):
     # fp32 rows with |mean|/sigma = 50 and constant rows
@@ -283,13 +313,15 @@ def test_small_variance_rows(orc, dtype):
     assert np.all(orc.decode(host(y), dtype) == orc.decode(arr["beta"], dtype)[None, :])
 
 
+@pytest.mark.parametrize("H", [1024, 128, 40, 24])
 @pytest.mark.parametrize("pad", [24, 3])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_strided_rows_and_canaries(orc, dtype, pad):
+def test_strided_rows_and_canaries(orc, dtype, pad, H):
     """Row strides > H (pad 24 keeps 16-byte rows, pad 3 forces the
     element-wise path): the padding between rows and a guard row after the
-    last row stay untouched, and results match the oracle."""
-    N, H = 33, 1024
+    last row stay untouched, and results match the oracle.  Short rows run
+    several rows per wave, addressed through one range per row group."""
+    N = 33
     arr = synth.custom(11, N, H, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     SENT = -7.0
