@@ -305,6 +305,20 @@ __device__ __forceinline__ void wave_sum2(float &a, float &b) {
     b = lane_value(b, 0) + lane_value(b, 32);
 }
 
+// Sum over aligned groups of SEG lanes (8, 16 or 32): the first steps of
+// wave_sum; every lane of a group receives the group's sum, with the same
+// bits in each lane.  All 64 lanes must be active.
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+    static_assert(SEG == 8 || SEG == 16 || SEG == 32, "segments of 8, 16 or 32 lanes");
+    v += dpp<DPP_QUAD_XOR1>(v);
+    v += dpp<DPP_QUAD_XOR2>(v);
+    v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (SEG >= 16) v += dpp<DPP_ROW_MIRROR>(v);
+    if constexpr (SEG >= 32) v += swizzle_xor16(v);
+    return v;
+}
+
 __device__ __forceinline__ int wave_id_uniform() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

@@ -112,10 +112,23 @@ __device__ __forceinline__ void store_row(rsrc_t r, const Layout<VEC, CPL, TW> &
 }
 
 // ----------------------------------------------------------------- forward --
-// 1024-thread forward workgroups ask for 8 waves per SIMD (<= 64 VGPRs), so
-// that two rows' workgroups share a CU.
+// Workgroups ask for 8 waves per SIMD (<= 64 VGPRs) where that costs no
+// spills: 1024-thread forward workgroups, so that two rows' workgroups
+// share a CU, and single-wave rows of up to 16 two-byte elements per lane
+// (LayerNorm there would otherwise take 70 registers and 7 waves).
+#ifndef RN_FWD_MINW8
+#define RN_FWD_MINW8 1
+#endif
 template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF>
-__global__ __launch_bounds__(64 * TW * RT, (TW * RT == 16 && !PF) ? 8 : 1)
+constexpr int fwd_min_waves() {
+    return ((TW * RT == 16 && !PF) ||
+            (RN_FWD_MINW8 && sizeof(T) == 2 && TW == 1 && VEC * CPL <= 16))
+               ? 8
+               : 1;
+}
+
+template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF>
+__global__ __launch_bounds__(64 * TW * RT, (fwd_min_waves<T, W, VEC, CPL, TW, RT, OP, PF>()))
 void fwd_kernel(const FwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
     using Raw = RawChunk<T, VEC>;
@@ -509,16 +522,20 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
 }
 
 // Kernel 2: column sums of the partial rows.  A workgroup of 1024 threads
-// owns COLS columns; its lanes form (1024 / COLS) row slots, slot j adding
-// the contiguous block of rows [j*R, (j+1)*R) (R = ceil(P / slots)) in
-// increasing order with up to 32 loads in flight, after which the slot sums
-// are added in slot order.  blockIdx.y picks dgamma (0) or dbeta (1).
-// Narrow tiles spread short rows over more CUs; wide rows use 64 columns
-// (256-byte segments per partial row).
+// owns COLS columns; its lanes form SLOTS = 1024/COLS row slots, slot j
+// adding the contiguous block of rows [j*R, (j+1)*R) (R = ceil(P / SLOTS))
+// in increasing order with up to 32 loads in flight.  The slot sums meet in
+// LDS, and each column's SLOTS values are then added by one segment of
+// SLOTS lanes with the fixed segment-sum tree.  blockIdx.y picks dgamma (0)
+// or dbeta (1).  Narrow tiles spread short rows over more CUs; wide rows
+// use 64 columns (256-byte segments per partial row).
 template <class T, int COLS>
 __global__ __launch_bounds__(1024) void bwd2_kernel(const float *part, int P,
                                                    int H, T *dgamma, T *dbeta) {
     constexpr int SLOTS = 1024 / COLS;
+    static_assert(SLOTS == 8 || SLOTS == 16 || SLOTS == 32, "column tile");
+    constexpr int CPW = 64 / SLOTS;   // columns folded per wave
+    static_assert(COLS == 16 * CPW, "16 waves fold the tile");
     __shared__ float red[SLOTS][COLS];
     const int cl = threadIdx.x % COLS;
     const int slot = threadIdx.x / COLS;
@@ -540,16 +557,18 @@ __global__ __launch_bounds__(1024) void bwd2_kernel(const float *part, int P,
     }
     red[slot][cl] = s;
     __syncthreads();
-    if (slot == 0 && col < H) {
-        float t = red[0][cl];
-        for (int j = 1; j < SLOTS; ++j) t += red[j][cl];
-        store_one(blockIdx.y == 0 ? dgamma + col : dbeta + col, t);
-    }
+    const int lane = threadIdx.x & 63;
+    const int fc = (threadIdx.x >> 6) * CPW + lane / SLOTS;   // column folded
+    const float t = seg_sum<SLOTS>(red[lane % SLOTS][fc]);
+    const int gcol = blockIdx.x * COLS + fc;
+    if (lane % SLOTS == 0 && gcol < H)
+        store_one(blockIdx.y == 0 ? dgamma + gcol : dbeta + gcol, t);
 }
 
 #ifndef RN_K2_WIDE_H
 #define RN_K2_WIDE_H 4096   // rows at least this long use 64-column tiles
 #endif
+
 
 template <class T>
 hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void *db,

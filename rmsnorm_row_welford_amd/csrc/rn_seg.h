@@ -24,20 +24,6 @@
 
 namespace rn {
 
-// Sum over aligned groups of SEG lanes; every lane of a group receives the
-// group's sum, with the same bits in each lane (the steps pair lanes
-// symmetrically, as in wave_sum).  All 64 lanes must be active.
-template <int SEG>
-__device__ __forceinline__ float seg_sum(float v) {
-    static_assert(SEG == 8 || SEG == 16 || SEG == 32, "segments of 8, 16 or 32 lanes");
-    v += dpp<DPP_QUAD_XOR1>(v);
-    v += dpp<DPP_QUAD_XOR2>(v);
-    v += dpp<DPP_ROW_HALF_MIRROR>(v);
-    if constexpr (SEG >= 16) v += dpp<DPP_ROW_MIRROR>(v);
-    if constexpr (SEG >= 32) v += swizzle_xor16(v);
-    return v;
-}
-
 // The value lane `src` holds, fetched by every lane (ds_bpermute).
 __device__ __forceinline__ float lane_pull(float v, int src) {
     return __builtin_bit_cast(
@@ -247,8 +233,11 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
         }
     }
 
-    // Partial rows: slot (wave, seg) parks its accumulators, then each
-    // thread adds one column over the slots in order.
+    // Partial rows: slot (wave, seg) parks its accumulators in LDS; then
+    // each column's SLOTS values are added by one segment of SLOTS lanes
+    // with the fixed segment-sum tree (64/SLOTS columns per wave and pass).
+    constexpr int CPW = 64 / SLOTS;
+    static_assert(SLOTS == 8 || SLOTS == 16 || SLOTS == 32, "slot count");
     const int slot = wave * RPW + seg;
 #pragma unroll
     for (int p = 0; p < (LN ? 2 : 1); ++p) {
@@ -257,11 +246,11 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
         for (int k = 0; k < VEC; ++k) acc[slot * SPAN + sl * VEC + k] = src[k];
         __syncthreads();
         float *dst = a.part + ((int64_t)p * gridDim.x + blockIdx.x) * H;
-        for (int col = threadIdx.x; col < H; col += 64 * WPG) {
-            float t = acc[col];
-#pragma unroll 8
-            for (int j = 1; j < SLOTS; ++j) t += acc[j * SPAN + col];
-            dst[col] = t;
+        for (int c0 = wave * CPW; c0 < H; c0 += WPG * CPW) {   // wave-uniform
+            const int fc = c0 + lane / SLOTS;
+            const float v = fc < H ? acc[(lane % SLOTS) * SPAN + fc] : 0.0f;
+            const float t = seg_sum<SLOTS>(v);
+            if (lane % SLOTS == 0 && fc < H) dst[fc] = t;
         }
         __syncthreads();
     }
