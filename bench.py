@@ -25,8 +25,8 @@ Outside the step, per_op also times (same protocol, same shape):
   fused_add_rms_bwd        the fused op's backward: dx from dy, the stored h,
                            the saved rstd and a residual-stream gradient dh_in
   fused_add_rms_fwd_inplace  the fused forward writing h over the residual
-  unfused_add_rms          the unfused comparison: torch.add (h = x + r, one
-                           launch) then rms_fwd on h, 5 N H e bytes in all
+  unfused_add_rms          the unfused comparison: the library's add kernel
+                           (h = x + r) then rms_fwd on h, 5 N H e bytes
 """
 import argparse
 import json
@@ -148,8 +148,7 @@ class Sets:
             rn.fused_add_rms_fwd(t["x"], t["r_in"], g, FUSED_EPS, y=t["y4"],
                                  h=t["r_in"], rstd=t["rstd4"])
         elif op == "unfused_add_rms":
-            import torch
-            torch.add(t["x"], t["r"], out=t["h5"])
+            rn.add(t["x"], t["r"], out=t["h5"])
             rn.rms_fwd(t["h5"], g, FUSED_EPS, y=t["y5"], rstd=t["rstd5"])
         else:
             raise ValueError(op)

@@ -192,6 +192,15 @@ const char *rn_status_str(int status);
  * that calibrates hardware byte counters).  Buffers must not overlap. */
 int rn_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+/* Benchmark helper, not part of the normalization: out = a + b over n
+ * elements of the activation type of `dtype` (float32 add, rounded to the
+ * storage type), the first launch of the unfused add-then-RMSNorm
+ * comparison ("Write Triton Fused Add Rmsnorm Kernel", Required reasoning
+ * process, the traffic comparison).  out may be exactly a or b; any other
+ * overlap is RN_EOVERLAP. */
+int rn_add(const void *a, const void *b, void *out, int64_t n, int dtype,
+           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

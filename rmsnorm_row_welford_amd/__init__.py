@@ -43,6 +43,7 @@ SIGNATURES = {
     "rn_max_hidden": ([_I, _I], _I64),
     "rn_status_str": ([_I], ctypes.c_char_p),
     "rn_copy": ([_P, _P, _SZ, _P], _I),
+    "rn_add": ([_P, _P, _P, _I64, _I, _P], _I),
 }
 
 _lib = None
@@ -306,3 +307,19 @@ def copy(src, dst, nbytes=None, stream=None):
     """Device-to-device byte copy with the library's streaming copy kernel."""
     n = src.numel() * src.element_size() if nbytes is None else nbytes
     _check("rn_copy", lib().rn_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
+
+
+def add(a, b, out=None, stream=None):
+    """out = a + b (element-wise, float32 add rounded to the storage type)
+    with the library's streaming add kernel; a benchmark helper."""
+    import torch
+    if a.shape != b.shape or a.dtype != b.dtype:
+        raise ValueError("a and b must match in shape and dtype")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    if out is None:
+        out = torch.empty_like(a)
+    code = _code_of(a.dtype, a.dtype)
+    _check("rn_add", lib().rn_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), code,
+                                  _stream(stream)))
+    return out

@@ -405,3 +405,19 @@ extern "C" int rn_copy(const void *src, void *dst, size_t bytes,
     if (overlaps(a, b)) return RN_EOVERLAP;
     return hip_status(launch_copy(src, dst, bytes, stream));
 }
+
+extern "C" int rn_add(const void *a, const void *b, void *out, int64_t n, int dtype,
+                      hipStream_t stream) {
+    if (!dtype_ok(dtype)) return RN_EDTYPE;
+    if (n < 0) return RN_EINVAL;
+    if (n == 0) return RN_OK;
+    if (!a || !b || !out) return RN_EINVAL;
+    const size_t e = elem_size(dtype);
+    for (const void *p : {a, b, (const void *)out})
+        if (!aligned(p, e)) return RN_EINVAL;
+    const Span sa = span1d(a, n, e), sb = span1d(b, n, e), so = span1d(out, n, e);
+    if ((out != a && overlaps(so, sa)) || (out != b && overlaps(so, sb)))
+        return RN_EOVERLAP;
+    const int elem = dtype == RN_F32 ? 0 : (dtype == RN_BF16 || dtype == RN_BF16_F32W) ? 1 : 2;
+    return hip_status(launch_add(elem, a, b, out, n, stream));
+}

@@ -102,4 +102,8 @@ inline bool bwd_use_colsum(int64_t N, int H, int e, int P, bool ln, int cus) {
 hipError_t launch_copy(const void *src, void *dst, size_t bytes,
                        hipStream_t s);
 
+// out = a + b over n elements; elem: 0 float32, 1 bfloat16, 2 binary16.
+hipError_t launch_add(int elem, const void *a, const void *b, void *out, int64_t n,
+                      hipStream_t s);
+
 }  // namespace rn

@@ -230,3 +230,13 @@ def test_mixed_param_backward_checks(L):
     assert ln_bwd(L, dt=BF16_F32W, db=DG + 2048) == EOVERLAP
     assert fused_bwd(L, dt=F16_F32W, dg=DG + 2) == EINVAL
     assert fused_bwd(L, dt=F16_F32W, dx=G + 2048) == EOVERLAP
+
+
+def test_add_argument_errors(L):
+    assert L.rn_add(X, Y, H_, 0, BF16, S) == OK
+    assert L.rn_add(X, Y, H_, -1, BF16, S) == EINVAL
+    assert L.rn_add(None, Y, H_, 8, BF16, S) == EINVAL
+    assert L.rn_add(X, Y, H_, 8, 9, S) == EDTYPE
+    assert L.rn_add(X + 1, Y, H_, 8, BF16, S) == EINVAL
+    assert L.rn_add(X, Y, X + 4, 8, BF16, S) == EOVERLAP
+    assert L.rn_add(X, Y, Y + 4, 8, F32, S) == EOVERLAP

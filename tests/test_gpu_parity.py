@@ -479,6 +479,67 @@ def test_many_short_rows(orc):
     check_bwd(orc, arr, "bf16", 1e-5, layernorm=True, rows=rows)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("n,off", [(1000003, 0), (4096, 0), (777, 1)])
+def test_add_helper(orc, dtype, n, off):
+    """The unfused baseline's add: RNE(a + b) bit-exact, on the 16-byte path
+    with a tail and element by element (offset views)."""
+    arr = synth.custom(18, 1, n + off, dtype)
+    a = to_dev(arr["x"], dtype)[0, off:]
+    b = to_dev(arr["residual"], dtype)[0, off:]
+    out = rn.add(a, b)
+    torch.cuda.synchronize()
+    want = orc.encode(orc.decode(arr["x"][0, off:], dtype) +
+                      orc.decode(arr["residual"][0, off:], dtype), dtype)
+    assert np.array_equal(host(out), want)
+    rn.add(a, b, out=a)      # in place over a
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), want)
+
+
+@pytest.mark.parametrize("N,H", [(64, 4096), (1, 8192), (333, 128)])
+def test_graph_capture_replays(N, H):
+    """The entry points enqueue only kernels on the caller's stream, so a HIP
+    graph can capture them: fused forward + fused backward + LayerNorm
+    forward/backward captured once and replayed four times, with eager work
+    and synchronizations between replays; every replay must reproduce the
+    eager results bit for bit."""
+    arr = synth.custom(19, N, H, "bf16")
+    x, r, g, b, dy, dh = (to_dev(arr[k]) for k in ("x", "residual", "gamma", "beta",
+                                                   "dy", "dh"))
+    bf = torch.bfloat16
+    y, hh, dx, dx2, y2 = (torch.empty((N, H), dtype=bf, device=DEV) for _ in range(5))
+    rstd, mean, rstd2 = (torch.empty(N, dtype=torch.float32, device=DEV) for _ in range(3))
+    dg, dg2, db2 = (torch.empty(H, dtype=bf, device=DEV) for _ in range(3))
+    ws = torch.empty(max(1, rn.workspace_bytes(N, H, bf, True)), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        rn.fused_add_rms_fwd(x, r, g, 1e-6, y=y, h=hh, rstd=rstd)
+        rn.fused_add_rms_bwd(dy, hh, g, rstd, 1e-6, dh_in=dh, dx=dx, dgamma=dg,
+                             workspace=ws)
+        rn.ln_fwd(x, g, b, 1e-5, y=y2, mean=mean, rstd=rstd2)
+        rn.ln_bwd(dy, x, g, mean, rstd2, 1e-5, dx=dx2, dgamma=dg2, dbeta=db2,
+                  workspace=ws)
+
+    outs = (y, hh, rstd, dx, dg, y2, mean, rstd2, dx2, dg2, db2)
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, w_ in zip(outs, want):
+            assert torch.equal(t, w_), f"replay {rep} differs from eager"
+
+
 def test_unsupported_sizes():
     g = torch.ones(16385, dtype=torch.bfloat16, device=DEV)
     x = torch.ones((2, 16385), dtype=torch.bfloat16, device=DEV)
