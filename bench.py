@@ -27,6 +27,11 @@ Outside the step, per_op also times (same protocol, same shape):
   fused_add_rms_fwd_inplace  the fused forward writing h over the residual
   unfused_add_rms          the unfused comparison: the library's add kernel
                            (h = x + r) then rms_fwd on h, 5 N H e bytes
+
+decode (not in the step): the latency regime of a few rows (N = 1, 16, 64
+at H = 4096, bf16, data in cache): 50 back-to-back calls captured in one HIP
+graph and replayed, GPU time per call (launch gaps included, host overhead
+excluded).
 """
 import argparse
 import json
@@ -215,6 +220,46 @@ def time_op_swept(sets, op, K, sweep):
     return float(np.median([a.elapsed_time(b) for a, b in ms])) * 1e3
 
 
+def decode_latency(rn, dev, H=4096, Ns=(1, 16, 64), K=50, reps=5):
+    """us per call of the forward ops at decode-size N, from graph replays."""
+    import torch
+    bf = torch.bfloat16
+    out = {}
+    for N in Ns:
+        x = torch.randn(N, H, device=dev).to(bf)
+        r = torch.randn(N, H, device=dev).to(bf)
+        g = (1 + 0.1 * torch.randn(H, device=dev)).to(bf)
+        y, h = torch.empty_like(x), torch.empty_like(x)
+        rstd = torch.empty(N, dtype=torch.float32, device=dev)
+        ops = {
+            "rms_fwd": lambda: rn.rms_fwd(x, g, 1e-6, y=y, rstd=rstd),
+            "ln_fwd": lambda: rn.ln_fwd(x, g, None, 1e-6, y=y, rstd=rstd,
+                                        save_stats=False),
+            "fused_add_rms_fwd": lambda: rn.fused_add_rms_fwd(x, r, g, 1e-6, y=y,
+                                                              h=h, rstd=rstd),
+        }
+        for name, f in ops.items():
+            f()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(K):
+                    f()
+            graph.replay()
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[f"{name}:{N}x{H}"] = round(e0.elapsed_time(e1) * 1e3 / (reps * K), 3)
+            del graph
+    return out
+
+
 def copy_ceiling(rn, dev, nbytes=1 << 30, reps=5):
     """Streaming copy bandwidth over rotating buffers (read + write bytes)."""
     import torch
@@ -293,6 +338,8 @@ def main():
     ap.add_argument("--only", default=None, help="comma list of step ops")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the ops timed outside the step")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-size latency table")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -350,6 +397,11 @@ def main():
 
     del sets
     torch.cuda.empty_cache()
+    decode = None
+    if not (args.no_decode or args.only):
+        decode = decode_latency(rn, dev)
+        for k, v in decode.items():
+            log(f"decode {k:28s} {v:7.2f} us per call (graph replay)")
     copy_gbs = copy_ceiling(rn, dev)
     log(f"copy ceiling {copy_gbs:.0f} GB/s ({100 * copy_gbs / PEAK_GBS:.1f}% of peak)")
 
@@ -380,6 +432,7 @@ def main():
         "pct_peak": round(100.0 * value / PEAK_GBS, 2),
         "per_op": per_op,
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "decode_us_per_call": decode,
         "wall_ms_per_step": round(wall_ms, 5),
         "roofline": roof,
     }

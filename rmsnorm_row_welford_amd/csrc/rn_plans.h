@@ -15,16 +15,18 @@
 namespace rn {
 
 // ------------------------------------------------ several rows per wave --
-// Rows of at most SEG*VEC elements: SEG lanes per row, 64/SEG rows per wave,
-// WPG waves per workgroup, IT row groups per wave in the forward.  Row
-// strides too large for 32-bit group offsets fall back to one row per wave.
-template <int VEC_, int SEG_, int WPG_, int IT_>
+// Rows of at most SEG*VEC*CPL elements: SEG lanes per row (64: a whole
+// wave), 64/SEG rows per wave, CPL chunks per lane, WPG waves per
+// workgroup, IT row groups of a wave in flight in the forward (the backward
+// forms take CPL = 1, SEG <= 32).  Row strides too large for 32-bit group
+// offsets fall back to one row per wave.
+template <int VEC_, int SEG_, int WPG_, int IT_, int CPL_ = 1>
 struct SegPlan {
-    static constexpr int VEC = VEC_, SEG = SEG_, WPG = WPG_, IT = IT_;
+    static constexpr int VEC = VEC_, SEG = SEG_, WPG = WPG_, IT = IT_, CPL = CPL_;
     static constexpr int RPW = 64 / SEG_;
-    static constexpr int SPAN = SEG_ * VEC_;
+    static constexpr int SPAN = SEG_ * VEC_ * CPL_;
     static constexpr int THREADS = 64 * WPG_;
-    using Fallback = Plan<VEC_, 1, 1, 4, false>;
+    using Fallback = Plan<VEC_, CPL_, 1, 4, false>;
 };
 
 inline bool seg_fits(int rpw, int e, std::initializer_list<int64_t> lds) {
@@ -37,7 +39,7 @@ template <class T, class W, class P, int OP>
 hipError_t launch_fwd_seg(const FwdArgs &a, hipStream_t s) {
     constexpr int rows = P::WPG * P::RPW * P::IT;
     const int64_t grid = (a.N + rows - 1) / rows;
-    hipLaunchKernelGGL((fwd_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, P::IT, OP>),
+    hipLaunchKernelGGL((fwd_seg_kernel<T, W, P::VEC, P::SEG, P::CPL, P::WPG, P::IT, OP>),
                        dim3((unsigned)grid), dim3(P::THREADS), 0, s, a);
     return hipGetLastError();
 }
@@ -128,12 +130,17 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 // row lengths can be overridden at build time (-DRN_FWD_BF16_1024=... etc.)
 // to sweep team shapes.
 // Forward plans that run one workgroup per row group (several fit per CU)
-// do not prefetch (PF = false): the registers would go unused.
+// do not prefetch (PF = false): the registers would go unused.  Rows of
+// 1-4 KiB run one row per wave with two rows of each wave in flight (a
+// whole-wave SegPlan; four 4 KiB rows need too many registers, so one).
+#ifndef RN_FWD_BF16_512
+#define RN_FWD_BF16_512 SegPlan<8, 64, 4, 2, 1>
+#endif
 #ifndef RN_FWD_BF16_1024
-#define RN_FWD_BF16_1024 Plan<8, 2, 1, 4, false>
+#define RN_FWD_BF16_1024 SegPlan<8, 64, 4, 2, 2>
 #endif
 #ifndef RN_FWD_BF16_2048
-#define RN_FWD_BF16_2048 Plan<8, 4, 1, 4, false>
+#define RN_FWD_BF16_2048 SegPlan<8, 64, 4, 1, 4>
 #endif
 #ifndef RN_FWD_BF16_4096
 #define RN_FWD_BF16_4096 Plan<8, 2, 4, 1, false>
@@ -155,18 +162,18 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 using FwdPlans2B = PlanList<SegPlan<8, 8, 4, 2>,          //    64
                             SegPlan<8, 16, 4, 2>,         //   128
                             SegPlan<8, 32, 4, 2>,         //   256
-                            Plan<8, 1, 1, 4, false>,      //   512
-                              RN_FWD_BF16_1024,            //  1024
-                              RN_FWD_BF16_2048,            //  2048
-                              RN_FWD_BF16_4096,            //  4096
-                              Plan<8, 2, 8, 1, false>,     //  8192
-                              RN_FWD_BF16_16384>;          // 16384
+                            RN_FWD_BF16_512,              //   512
+                            RN_FWD_BF16_1024,             //  1024
+                            RN_FWD_BF16_2048,             //  2048
+                            RN_FWD_BF16_4096,             //  4096
+                            Plan<8, 2, 8, 1, false>,      //  8192
+                            RN_FWD_BF16_16384>;           // 16384
 using FwdPlansF32 = PlanList<SegPlan<4, 8, 4, 2>,         //    32
                              SegPlan<4, 16, 4, 2>,        //    64
                              SegPlan<4, 32, 4, 2>,        //   128
-                             Plan<4, 1, 1, 4, false>,      //   256
-                             Plan<4, 2, 1, 4, false>,      //   512
-                             Plan<4, 4, 1, 4, false>,      //  1024
+                             SegPlan<4, 64, 4, 2, 1>,     //   256
+                             SegPlan<4, 64, 4, 2, 2>,     //   512
+                             SegPlan<4, 64, 4, 1, 4>,     //  1024
                              Plan<4, 4, 2, 2, false>,      //  2048
                              Plan<4, 4, 4, 1, false>,      //  4096
                              Plan<4, 4, 8, 1, false>,      //  8192

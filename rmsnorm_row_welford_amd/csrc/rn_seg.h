@@ -1,10 +1,12 @@
 // Short rows: several rows per wavefront.
 //
-// For rows of at most SEG*VEC elements a wave is cut into 64/SEG segments of
-// SEG lanes (SEG = 8, 16 or 32); segment s owns one row and lane sl of it
-// holds the chunk of VEC elements starting at sl*VEC.  All lanes of a wave
-// stay busy on rows far shorter than the wave's 64*VEC-element reach, and a
-// wave moves 64 chunks per access instead of H/VEC.
+// For rows of at most SEG*VEC*CPL elements a wave is cut into 64/SEG
+// segments of SEG lanes (SEG = 8, 16, 32 or 64); segment s owns one row and
+// lane sl of it holds the CPL chunks of VEC elements starting at
+// (c*SEG + sl)*VEC.  All lanes of a wave stay busy on rows far shorter than
+// the wave's 64*VEC-element reach, and a wave moves 64 chunks per access
+// instead of H/VEC.  With SEG = 64 this is one row per wave, as in
+// fwd_kernel, but with IT rows of each wave in flight at once.
 //
 // Addressing.  A buffer resource must be wave-uniform, so it covers the
 // wave's whole group of rows [row0, row0 + n): it starts at row row0 and ends
@@ -46,13 +48,22 @@ __device__ __forceinline__ uint32_t seg_off(int seg, int sl, int64_t ld, bool va
     return valid ? (uint32_t)(((int64_t)seg * ld + sl * VEC) * (int64_t)sizeof(T)) : kOffOOB;
 }
 
+// Sum over a segment; a whole-wave segment uses the wave sum.
+template <int SEG>
+__device__ __forceinline__ float segment_sum(float v) {
+    if constexpr (SEG == 64) return wave_sum(v);
+    else return seg_sum<SEG>(v);
+}
+
 // Forward.  Wave w of workgroup b owns IT consecutive groups of 64/SEG rows
 // starting at row ((b*WPG + w)*IT)*(64/SEG); all IT groups are requested
 // before the first is reduced.  One workgroup per WPG*IT groups (not
 // persistent): the dispatcher keeps every CU fed.
-template <class T, class W, int VEC, int SEG, int WPG, int IT, int OP>
-__global__ __launch_bounds__(64 * WPG) void fwd_seg_kernel(const FwdArgs a) {
+template <class T, class W, int VEC, int SEG, int CPL, int WPG, int IT, int OP>
+__global__ __launch_bounds__(64 * WPG, (sizeof(T) == 2 && sizeof(W) == 2 && VEC * CPL <= 16) ? 8 : 1)
+void fwd_seg_kernel(const FwdArgs a) {
     constexpr int RPW = 64 / SEG;
+    constexpr int E = VEC * CPL;
     using Raw = RawChunk<T, VEC>;
     using RawW = RawChunk<W, VEC>;
     const int lane = threadIdx.x & 63;
@@ -60,29 +71,44 @@ __global__ __launch_bounds__(64 * WPG) void fwd_seg_kernel(const FwdArgs a) {
     const int seg = lane / SEG, sl = lane % SEG;
     const int H = a.H;
     const int64_t N = a.N;
-    const bool valid = sl * VEC < H;
+    bool valid[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) valid[c] = (c * SEG + sl) * VEC < H;
     const int64_t wrow = ((int64_t)blockIdx.x * WPG + wave) * (IT * RPW);
     if (wrow >= N) return;   // wave-uniform; no barriers below
 
-    RawW g, bt;
-    const uint32_t poff = valid ? (uint32_t)(sl * VEC * (int)sizeof(W)) : kOffOOB;
-    g.template bload<0>(row_rsrc((const W *)a.gamma, H), poff);
-    if constexpr (OP == OP_LN) {
-        if (a.beta != nullptr) bt.template bload<0>(row_rsrc((const W *)a.beta, H), poff);
-        else bt.zero();
+    RawW g[CPL], bt[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const uint32_t poff =
+            valid[c] ? (uint32_t)((c * SEG + sl) * VEC * (int)sizeof(W)) : kOffOOB;
+        g[c].template bload<0>(row_rsrc((const W *)a.gamma, H), poff);
+        if constexpr (OP == OP_LN) {
+            if (a.beta != nullptr)
+                bt[c].template bload<0>(row_rsrc((const W *)a.beta, H), poff);
+            else
+                bt[c].zero();
+        }
     }
 
-    Raw cx[IT], cr[(OP == OP_FUSED) ? IT : 1];
+    Raw cx[IT][CPL], cr[(OP == OP_FUSED) ? IT : 1][CPL];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int64_t row0 = wrow + (int64_t)i * RPW;
         if (row0 < N) {
             const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
-            cx[i].template bload<RN_LOAD_AUX>(group_rsrc<T>(a.x, row0, n, a.ldx, H),
-                                              seg_off<T, VEC>(seg, sl, a.ldx, valid));
-            if constexpr (OP == OP_FUSED)
-                cr[i].template bload<RN_LOAD_AUX>(group_rsrc<T>(a.res, row0, n, a.ldr, H),
-                                                  seg_off<T, VEC>(seg, sl, a.ldr, valid));
+            const rsrc_t rx = group_rsrc<T>(a.x, row0, n, a.ldx, H);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                cx[i][c].template bload<RN_LOAD_AUX>(
+                    rx, seg_off<T, VEC>(seg, c * SEG + sl, a.ldx, valid[c]));
+            if constexpr (OP == OP_FUSED) {
+                const rsrc_t rr = group_rsrc<T>(a.res, row0, n, a.ldr, H);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    cr[i][c].template bload<RN_LOAD_AUX>(
+                        rr, seg_off<T, VEC>(seg, c * SEG + sl, a.ldr, valid[c]));
+            }
         }
     }
 
@@ -91,54 +117,76 @@ __global__ __launch_bounds__(64 * WPG) void fwd_seg_kernel(const FwdArgs a) {
         const int64_t row0 = wrow + (int64_t)i * RPW;
         if (row0 >= N) break;
         const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
-        float v[VEC];
+        float v[E];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            v[k] = cx[i].get(k);
-            if constexpr (OP == OP_FUSED) v[k] += cr[i].get(k);
-        }
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                v[c * VEC + k] = cx[i][c].get(k);
+                if constexpr (OP == OP_FUSED) v[c * VEC + k] += cr[i][c].get(k);
+            }
         // h goes out before y; every element of this lane is already loaded,
         // so h may alias x or the residual.
-        if constexpr (OP == OP_FUSED)
-            bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.h, row0, n, a.ldh, H),
-                              seg_off<T, VEC>(seg, sl, a.ldh, valid), v);
+        if constexpr (OP == OP_FUSED) {
+            const rsrc_t rh = group_rsrc<T>(a.h, row0, n, a.ldh, H);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                bstore_chunk<VEC>((T *)nullptr, rh,
+                                  seg_off<T, VEC>(seg, c * SEG + sl, a.ldh, valid[c]),
+                                  v + c * VEC);
+        }
 
         float mean = 0.0f, var;
         if constexpr (OP == OP_LN) {
-            const float pivot = lane_pull(v[0], seg * SEG);   // the row's first element
+            float pivot;   // the row's first element
+            if constexpr (SEG == 64) pivot = lane_value(v[0], 0);
+            else pivot = lane_pull(v[0], seg * SEG);
             float s = 0.0f;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                v[k] = valid ? v[k] - pivot : 0.0f;
-                s += v[k];
-            }
-            const float ms = seg_sum<SEG>(s) * a.inv_H;
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    float &u = v[c * VEC + k];
+                    u = valid[c] ? u - pivot : 0.0f;
+                    s += u;
+                }
+            const float ms = segment_sum<SEG>(s) * a.inv_H;
             float q = 0.0f;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                v[k] = valid ? v[k] - ms : 0.0f;   // x - mean
-                q = __builtin_fmaf(v[k], v[k], q);
-            }
-            var = seg_sum<SEG>(q) * a.inv_H;
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    float &u = v[c * VEC + k];
+                    u = valid[c] ? u - ms : 0.0f;   // x - mean
+                    q = __builtin_fmaf(u, u, q);
+                }
+            var = segment_sum<SEG>(q) * a.inv_H;
             mean = pivot + ms;
         } else {
             float q = 0.0f;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) q = __builtin_fmaf(v[k], v[k], q);
-            var = seg_sum<SEG>(q) * a.inv_H;
+            for (int e = 0; e < E; ++e) q = __builtin_fmaf(v[e], v[e], q);
+            var = segment_sum<SEG>(q) * a.inv_H;
         }
         const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
 
-        float out[VEC];
+        float out[E];
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            if constexpr (OP == OP_LN)
-                out[k] = __builtin_fmaf(v[k] * rstd, g.get(k), bt.get(k));
-            else
-                out[k] = (v[k] * rstd) * g.get(k);
-        }
-        bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.y, row0, n, a.ldy, H),
-                          seg_off<T, VEC>(seg, sl, a.ldy, valid), out);
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const int e = c * VEC + k;
+                if constexpr (OP == OP_LN)
+                    out[e] = __builtin_fmaf(v[e] * rstd, g[c].get(k), bt[c].get(k));
+                else
+                    out[e] = (v[e] * rstd) * g[c].get(k);
+            }
+        const rsrc_t ry = group_rsrc<T>(a.y, row0, n, a.ldy, H);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            bstore_chunk<VEC>((T *)nullptr, ry,
+                              seg_off<T, VEC>(seg, c * SEG + sl, a.ldy, valid[c]),
+                              out + c * VEC);
         if (sl == 0 && seg < n) {
             if constexpr (OP == OP_LN) {
                 if (a.mean) a.mean[row0 + seg] = mean;
