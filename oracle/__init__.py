@@ -248,7 +248,10 @@ def default() -> Oracle:
 
 
 def __getattr__(name):
-    # module-level shortcuts: oracle.ln_fwd(...) etc. use the default build
-    if name.startswith("_"):
+    # module-level shortcuts: oracle.ln_fwd(...) etc. use the default build.
+    # Submodule names fall through to the import system (the first
+    # `from oracle import build` in a fresh tree runs before liboracle.so
+    # exists, so it must not try to load it).
+    if name.startswith("_") or name in ("build",):
         raise AttributeError(name)
     return getattr(default(), name)
