@@ -28,6 +28,12 @@ Outside the step, per_op also times (same protocol, same shape):
   unfused_add_rms          the unfused comparison: the library's add kernel
                            (h = x + r) then rms_fwd on h, 5 N H e bytes
 
+shapes (not in the step): every op at the other workload shapes (16384x2048,
+512x16384, 2048x16384 forward and backward; 8192x1024 forward without a
+bias; the fused forward at 32768x4096), each with enough rotating copies
+that its data comes from HBM.  --shapes-only NAME[,NAME] (or all) times just
+those and prints their table.
+
 decode (not in the step): the latency regime of a few rows (N = 1, 16, 64
 at H = 4096, bf16, data in cache): 50 back-to-back calls captured in one HIP
 graph and replayed, GPU time per call (launch gaps included, host overhead
@@ -49,16 +55,30 @@ WORKLOAD = "step_bf16_32768x1024"
 FUSED_EPS = 1e-6
 OPS = ("ln_fwd", "rms_fwd", "fused_add_rms_fwd", "ln_bwd", "rms_bwd")
 EXTRA_OPS = ("fused_add_rms_bwd", "fused_add_rms_fwd_inplace", "unfused_add_rms")
+# The other workload shapes of the normalization pages' test and benchmark
+# lists, timed op by op outside the step (same cold protocol): tall-narrow
+# and wide backward shapes (with the forwards at those shapes), the
+# bias-free forward with half its rows constant, and the fused forward at
+# (B=16, T=2048, H=4096).
+NORM_OPS = ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd")
+SHAPES = (
+    ("bwd_bf16_16384x2048", NORM_OPS),
+    ("bwd_bf16_512x16384", NORM_OPS),
+    ("bwd_bf16_2048x16384", NORM_OPS),
+    ("fwd_bf16_8192x1024", ("ln_fwd", "rms_fwd")),
+    ("fused_bf16_32768x4096", ("fused_add_rms_fwd",)),
+)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(N, H, e):
-    """Algorithmic HBM bytes of each op: every tensor read or written once."""
+def alg_bytes(N, H, e, beta=True):
+    """Algorithmic HBM bytes of each op: every tensor read or written once
+    (beta=False: LayerNorm without a bias)."""
     return {
-        "ln_fwd": 2 * N * H * e + 2 * H * e + 8 * N,          # x,y,gamma,beta,mean,rstd
+        "ln_fwd": 2 * N * H * e + (2 if beta else 1) * H * e + 8 * N,  # x,y,gamma,beta,stats
         "rms_fwd": 2 * N * H * e + H * e + 4 * N,             # x,y,gamma,rstd
         "fused_add_rms_fwd": 4 * N * H * e + H * e + 4 * N,   # x,r,h,y,gamma,rstd
         "ln_bwd": 3 * N * H * e + 3 * H * e + 8 * N,          # dy,x,dx,gamma,dg,db,stats
@@ -86,49 +106,72 @@ def counters_traffic(op, shape_tag):
     return d.get("traffic_bytes_per_launch")
 
 
-class Sets:
-    """M copies of the step's tensors on the GPU, and the five ops bound to
-    one copy each."""
+# what each op reads (inputs) and writes (outputs), by tensor key
+_OP_INPUTS = {
+    "ln_fwd": ("x",), "rms_fwd": ("x",), "fused_add_rms_fwd": ("x", "r"),
+    "ln_bwd": ("x", "dy"), "rms_bwd": ("x", "dy"),
+    "fused_add_rms_bwd": ("x", "r", "dy", "dh"),
+    "fused_add_rms_fwd_inplace": ("x", "r_in"), "unfused_add_rms": ("x", "r"),
+}
+_OP_ROWS_OUT = {
+    "ln_fwd": ("y",), "rms_fwd": ("y2",), "fused_add_rms_fwd": ("y3", "h"),
+    "ln_bwd": ("dx",), "rms_bwd": ("dx2",), "fused_add_rms_bwd": ("dx3",),
+    "fused_add_rms_fwd_inplace": ("y4",), "unfused_add_rms": ("y5", "h5"),
+}
+_OP_STATS_OUT = {
+    "ln_fwd": ("mean", "rstd"), "rms_fwd": ("rstd2",), "fused_add_rms_fwd": ("rstd3",),
+    "fused_add_rms_fwd_inplace": ("rstd4",), "unfused_add_rms": ("rstd5",),
+}
+# the forward whose saved statistics (and h) a backward op reads
+_BWD_NEEDS_FWD = {"ln_bwd": "ln_fwd", "rms_bwd": "rms_fwd",
+                  "fused_add_rms_bwd": "fused_add_rms_fwd"}
 
-    def __init__(self, rn, arr, eps, M, dev, extras=False):
+
+class Sets:
+    """M copies of the tensors the given ops touch, on the GPU, and the ops
+    bound to one copy each.  The forwards whose saved statistics a backward
+    op reads run once per copy at set-up."""
+
+    def __init__(self, rn, arr, eps, M, dev, ops):
         import torch
         self.rn, self.eps, self.M = rn, eps, M
         bf = torch.bfloat16
         N, H = arr["x"].shape
+        ops = list(ops)
+        pre = [_BWD_NEEDS_FWD[o] for o in ops if o in _BWD_NEEDS_FWD]
+        every = list(dict.fromkeys(pre + ops))
 
         def to_dev(a):
             return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
 
-        x0, r0, dy0 = to_dev(arr["x"]), to_dev(arr["residual"]), to_dev(arr["dy"])
-        self.g, self.b = to_dev(arr["gamma"]), to_dev(arr["beta"])
-        ws_ln = rn.workspace_bytes(N, H, bf, True)
-        ws_rms = rn.workspace_bytes(N, H, bf, False)
+        src = {"x": "x", "r": "residual", "r_in": "residual", "dy": "dy", "dh": "dy"}
+        need_in = {k for o in every for k in _OP_INPUTS[o]}
+        dev_src = {name: to_dev(arr[name]) for name in {src[k] for k in need_in}}
+        base = {k: dev_src[src[k]] for k in need_in}
+        self.g = to_dev(arr["gamma"])
+        self.b = to_dev(arr["beta"]) if "beta" in arr else None
+        ws = {}
+        if "ln_bwd" in ops:
+            ws["ws_ln"] = rn.workspace_bytes(N, H, bf, True)
+        if "rms_bwd" in ops or "fused_add_rms_bwd" in ops:
+            ws["ws_rms"] = rn.workspace_bytes(N, H, bf, False)
         self.s = []
         for _ in range(M):
-            t = {"x": x0.clone(), "r": r0.clone(), "dy": dy0.clone()}
-            for k in ("y", "y2", "y3", "h", "dx", "dx2"):
-                t[k] = torch.empty((N, H), dtype=bf, device=dev)
-            for k in ("mean", "rstd", "rstd2", "rstd3"):
-                t[k] = torch.empty(N, dtype=torch.float32, device=dev)
-            for k in ("dg", "db", "dg2"):
-                t[k] = torch.empty(H, dtype=bf, device=dev)
-            t["ws_ln"] = torch.empty(ws_ln, dtype=torch.uint8, device=dev)
-            t["ws_rms"] = torch.empty(ws_rms, dtype=torch.uint8, device=dev)
-            self.s.append(t)
-        if extras:
-            for t in self.s:
-                t["dh"] = dy0.clone()
-                t["r_in"] = r0.clone()
-                for k in ("y4", "y5", "h5", "dx3"):
+            t = {k: base[k].clone() for k in need_in}
+            for o in every:
+                for k in _OP_ROWS_OUT[o]:
                     t[k] = torch.empty((N, H), dtype=bf, device=dev)
-                for k in ("rstd4", "rstd5"):
+                for k in _OP_STATS_OUT.get(o, ()):
                     t[k] = torch.empty(N, dtype=torch.float32, device=dev)
-                t["dg3"] = torch.empty(H, dtype=bf, device=dev)
-        del x0, r0, dy0
-        for i in range(M):       # saved statistics for the backward ops
-            self.run("ln_fwd", i)
-            self.run("rms_fwd", i)
-            self.run("fused_add_rms_fwd", i)
+            for k in ("dg", "db", "dg2", "dg3"):
+                t[k] = torch.empty(H, dtype=bf, device=dev)
+            for k, nb in ws.items():
+                t[k] = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.s.append(t)
+        del base, dev_src
+        for i in range(M):       # saved statistics (and h) for the backward ops
+            for o in dict.fromkeys(pre):
+                self.run(o, i)
 
     def run(self, op, i):
         rn, t, g, b, eps = self.rn, self.s[i % self.M], self.g, self.b, self.eps
@@ -202,6 +245,33 @@ def time_op(sets, op, K, reps=3):
     return float(np.median(out)), out
 
 
+def time_op_graph(sets, op, K, reps=5):
+    """us per launch of one op with the host out of the loop: K launches
+    over the rotating sets captured once in a HIP graph, the graph replayed
+    `reps` times between two events (kernels and the gaps between them
+    only, no per-call host overhead)."""
+    import torch
+    for i in range(sets.M):
+        sets.run(op, i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(K):
+            sets.run(op, i)
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / (reps * K)
+
+
 def time_op_swept(sets, op, K, sweep):
     """Isolated protocol: read sweep of 512 MiB, then events around one op."""
     import torch
@@ -218,6 +288,37 @@ def time_op_swept(sets, op, K, sweep):
             ms.append((e0, e1))
     torch.cuda.synchronize()
     return float(np.median([a.elapsed_time(b) for a, b in ms])) * 1e3
+
+
+def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24):
+    """Per-op times at the other workload shapes: for each, enough rotating
+    copies that consecutive launches touch data last used about `cold_bytes`
+    of traffic earlier (so it comes from HBM), K launches back to back."""
+    import torch
+    from rmsnorm_row_welford_amd import synth
+    out = {}
+    for name, ops in SHAPES:
+        if names is not None and name not in names:
+            continue
+        w = synth.WORKLOADS[name]
+        arr = synth.generate(w)
+        N, H = w.N, w.H
+        nb = alg_bytes(N, H, 2, beta="beta" in arr)
+        per_launch = min(nb[o] for o in ops)
+        M = int(min(32, max(3, -(-cold_bytes // per_launch) + 1)))
+        sets = Sets(rn, arr, w.eps, M, dev, ops)
+        row = {"N": N, "H": H, "sets": M}
+        for k in ops:
+            us, _ = time_op(sets, k, max(K, 2 * M))
+            gbs = nb[k] / (us * 1e-6) / 1e9
+            row[k] = {"us": round(us, 3), "alg_bytes": nb[k], "GBps": round(gbs, 1),
+                      "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+            log(f"{name:24s} {k:18s} {us:8.2f} us  {gbs:7.0f} GB/s  "
+                f"{100 * gbs / PEAK_GBS:5.1f}% of peak")
+        out[name] = row
+        del sets, arr
+        torch.cuda.empty_cache()
+    return out
 
 
 def decode_latency(rn, dev, H=4096, Ns=(1, 16, 64), K=50, reps=5):
@@ -340,6 +441,11 @@ def main():
                     help="skip the ops timed outside the step")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-size latency table")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the per-op table at the other workload shapes")
+    ap.add_argument("--shapes-only", default=None,
+                    help="comma list of shape workloads (or 'all'): time only "
+                         "those, print their table as the JSON line, no step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -357,6 +463,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.shapes_only:
+        names = None if args.shapes_only == "all" else args.shapes_only.split(",")
+        print(json.dumps({"shapes": time_shapes(rn, dev, names)}), flush=True)
+        return
     w = synth.WORKLOADS[WORKLOAD]
     N, H = w.N, w.H
     t0 = time.time()
@@ -364,7 +474,7 @@ def main():
     log(f"inputs generated in {time.time() - t0:.1f}s")
     ops = list(OPS) if not args.only else args.only.split(",")
     extras = [] if (args.no_extras or args.only) else list(EXTRA_OPS)
-    sets = Sets(rn, arr, w.eps, args.sets, dev, extras=bool(extras))
+    sets = Sets(rn, arr, w.eps, args.sets, dev, ops + extras)
     nbytes = alg_bytes(N, H, 2)
 
     step_ms, wall_ms = time_steps(sets, ops, args.steps, args.warmup)
@@ -402,6 +512,9 @@ def main():
         decode = decode_latency(rn, dev)
         for k, v in decode.items():
             log(f"decode {k:28s} {v:7.2f} us per call (graph replay)")
+    shapes = None
+    if not (args.no_shapes or args.only):
+        shapes = time_shapes(rn, dev)
     copy_gbs = copy_ceiling(rn, dev)
     log(f"copy ceiling {copy_gbs:.0f} GB/s ({100 * copy_gbs / PEAK_GBS:.1f}% of peak)")
 
@@ -433,6 +546,7 @@ def main():
         "per_op": per_op,
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "decode_us_per_call": decode,
+        "shapes": shapes,
         "wall_ms_per_step": round(wall_ms, 5),
         "roofline": roof,
     }

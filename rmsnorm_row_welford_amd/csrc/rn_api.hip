@@ -263,7 +263,8 @@ extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
         if (P < 0) continue;
         any = true;
         if (bwd_use_colsum(N, (int)H, e, P, is_layernorm != 0, cus)) continue;
-        const size_t b = (size_t)P * (size_t)H * sizeof(float) * (is_layernorm ? 2 : 1);
+        const size_t b = (size_t)partial_stride(P) * (size_t)H * sizeof(float) *
+                         (is_layernorm ? 2 : 1);
         if (b > need) need = b;
     }
     if (!any) return RN_EUNSUPPORTED;
@@ -334,7 +335,8 @@ static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
     const int P = N == 0 ? 0 : partial_rows(dtype, N, H, vec, cus);
     if (P < 0) return RN_EUNSUPPORTED;
     const bool colsum = bwd_use_colsum(N, (int)H, (int)e, P, ln, cus);
-    const size_t need = colsum ? 0 : (size_t)P * (size_t)H * sizeof(float) * (ln ? 2 : 1);
+    const size_t need =
+        colsum ? 0 : (size_t)partial_stride(P) * (size_t)H * sizeof(float) * (ln ? 2 : 1);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RN_EWORKSPACE;
 
     BwdArgs a{};

@@ -29,7 +29,9 @@ struct FwdArgs {
 };
 
 // Arguments of one backward call.  `part` is the float32 partial-row
-// workspace: rows [0, P) hold dgamma partials, rows [P, 2P) dbeta (LN).
+// workspace: P partial rows of dgamma, then (LN) P of dbeta at
+// part + partial_stride(P) * H; short rows store each set column-major,
+// long rows row-major (partial_colmajor in rn_kernels.h).
 // Fused add+RMSNorm backward extras: `add` (NULL = none) is added to dx,
 // and `dx2` (NULL = none) receives a second copy of dx.
 struct BwdArgs {
@@ -47,6 +49,11 @@ struct BwdArgs {
     int H;
     float inv_H;
 };
+
+// Column stride of the partial-row workspace: the P float32 partial rows of
+// one parameter are stored column by column, each column padded to a
+// multiple of 8 slots.
+__host__ __device__ inline int partial_stride(int P) { return (P + 7) & ~7; }
 
 // Largest H each path supports: 16-byte vector path, element-wise path.
 constexpr int kMaxHidden = 16384;

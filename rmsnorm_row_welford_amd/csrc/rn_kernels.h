@@ -330,6 +330,39 @@ void fwd_kernel(const FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------- partial-row layout --
+// Rows of up to RN_PART_COLMAJOR_MAX_H elements store the P float32 partial
+// rows of a parameter column-major: the P values of column j are
+// contiguous, at part[j * Pp + slot] (Pp = partial_stride(P)), so kernel 2
+// reads a column with a few 16-byte loads and one wavefront reduces it.
+// Workgroup b writes slot slot_of(b): the workgroups that share an XCD
+// (b mod 8, as the dispatcher deals them out) take adjacent slots, so each
+// column's cache line is filled from one L2; slots no workgroup owns are
+// skipped.  Longer rows keep the partial rows row-major (part[slot * H + j],
+// slot = b): a workgroup's scattered column-major stores would touch more
+// lines than an L2 can merge, while kernel 2 finds enough columns to spread
+// over the CUs.  The dbeta partials follow at part + Pp * H.
+#ifndef RN_PART_COLMAJOR_MAX_H
+#define RN_PART_COLMAJOR_MAX_H 4096
+#endif
+__host__ __device__ inline bool partial_colmajor(int H) {
+    return H <= RN_PART_COLMAJOR_MAX_H;
+}
+__device__ __forceinline__ int slot_of(int b, int P) {
+    return (b & 7) * (partial_stride(P) >> 3) + (b >> 3);
+}
+// Does column-major slot s hold a workgroup's partial row?
+__device__ __forceinline__ bool slot_used(int s, int P) {
+    const int per = partial_stride(P) >> 3;
+    const int x = s / per, j = s - x * per;
+    return j < ((P - x + 7) >> 3);
+}
+// Where workgroup `b` of `P` writes column `col` of its partial row.
+__device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
+    return partial_colmajor(H) ? (int64_t)col * partial_stride(P) + slot_of(b, P)
+                               : (int64_t)b * H + col;
+}
+
 // ---------------------------------------------------------------- backward --
 // ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
 // kernel only writes dx (the column-sum strategy computes the parameter
@@ -491,13 +524,28 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     if constexpr (!ACC) {
         return;
     } else if constexpr (RT == 1) {
-        float *pg = a.part + (int64_t)blockIdx.x * H;
-        float *pb = a.part + ((int64_t)gridDim.x + blockIdx.x) * H;
+        float *pb = a.part + (int64_t)partial_stride(gridDim.x) * H;
+        if (partial_colmajor(H)) {
+            const int Pp = partial_stride(gridDim.x);
+            const int slot = slot_of(blockIdx.x, gridDim.x);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            if (!L.valid(c)) continue;
-            store_f32s<VEC>(pg + L.off(c), adg + c * VEC);
-            if constexpr (LN) store_f32s<VEC>(pb + L.off(c), adb + c * VEC);
+            for (int c = 0; c < CPL; ++c) {
+                if (!L.valid(c)) continue;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const int64_t o = (int64_t)(L.off(c) + k) * Pp + slot;
+                    a.part[o] = adg[c * VEC + k];
+                    if constexpr (LN) pb[o] = adb[c * VEC + k];
+                }
+            }
+        } else {
+            const int64_t o = (int64_t)blockIdx.x * H;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                if (!L.valid(c)) continue;
+                store_f32s<VEC>(a.part + o + L.off(c), adg + c * VEC);
+                if constexpr (LN) store_f32s<VEC>(pb + o + L.off(c), adb + c * VEC);
+            }
         }
     } else {
         float *accbuf = (float *)acc_lds;
@@ -509,29 +557,60 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
             for (int c = 0; c < CPL; ++c)
                 if (L.valid(c)) store_f32s<VEC>(accbuf + team * H + L.off(c), acc + c * VEC);
             __syncthreads();
-            float *dst = a.part + ((int64_t)p * gridDim.x + blockIdx.x) * H;
+            float *dst = a.part + (int64_t)p * partial_stride(gridDim.x) * H;
             for (int col = threadIdx.x; col < H; col += 64 * TW * RT) {
                 float t = accbuf[col];
 #pragma unroll
                 for (int tm = 1; tm < RT; ++tm) t += accbuf[tm * H + col];
-                dst[col] = t;
+                dst[partial_index(blockIdx.x, gridDim.x, H, col)] = t;
             }
             if (p + 1 < NV) __syncthreads();
         }
     }
 }
 
-// Kernel 2: column sums of the partial rows.  A workgroup of 1024 threads
-// owns COLS columns; its lanes form SLOTS = 1024/COLS row slots, slot j
-// adding the contiguous block of rows [j*R, (j+1)*R) (R = ceil(P / SLOTS))
-// in increasing order with up to 32 loads in flight.  The slot sums meet in
-// LDS, and each column's SLOTS values are then added by one segment of
-// SLOTS lanes with the fixed segment-sum tree.  blockIdx.y picks dgamma (0)
-// or dbeta (1).  Narrow tiles spread short rows over more CUs; wide rows
-// use 64 columns (256-byte segments per partial row).
+// Kernel 2: column sums of the partial rows, in a fixed order, rounded to
+// the parameter type.  blockIdx.y picks dgamma (0) or dbeta (1).
+//
+// Column-major partials: one wavefront per column (CPW consecutive columns
+// per wavefront, four wavefronts per workgroup).  Lane l adds the column's
+// slots [4l, 4l+4), [4l+256, ...), ... in increasing order (slots no
+// workgroup owns count as 0), then the lanes are added by the fixed wave64
+// tree.
+template <class T, int CPW>
+__global__ __launch_bounds__(256) void bwd2_cols_kernel(const float *part, int P, int H,
+                                                       T *dgamma, T *dbeta) {
+    const int Pp = partial_stride(P);
+    const int lane = threadIdx.x & 63;
+    const int col0 = (blockIdx.x * 4 + wave_id_uniform()) * CPW;
+    const float *base = part + (int64_t)blockIdx.y * Pp * H;
+    T *dst = blockIdx.y == 0 ? dgamma : dbeta;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int col = col0 + i;
+        if (col >= H) break;   // wave-uniform
+        const float *src = base + (int64_t)col * Pp;
+        float s = 0.0f;
+        for (int q = lane * 4; q < Pp; q += 256) {
+            const f32x4 v = *(const f32x4 *)(src + q);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (slot_used(q + k, P)) s += v[k];
+        }
+        s = wave_sum(s);
+        if (lane == 0) store_one(dst + col, s);
+    }
+}
+
+// Row-major partials: a workgroup of 1024 threads owns COLS columns; its
+// lanes form SLOTS = 1024/COLS row slots, slot j adding the contiguous
+// block of partial rows [j*R, (j+1)*R) (R = ceil(P / SLOTS)) in increasing
+// order with up to 32 loads in flight.  The slot sums meet in LDS, and each
+// column's SLOTS values are then added by one segment of SLOTS lanes with
+// the fixed segment-sum tree.
 template <class T, int COLS>
-__global__ __launch_bounds__(1024) void bwd2_kernel(const float *part, int P,
-                                                   int H, T *dgamma, T *dbeta) {
+__global__ __launch_bounds__(1024) void bwd2_rows_kernel(const float *part, int P,
+                                                        int H, T *dgamma, T *dbeta) {
     constexpr int SLOTS = 1024 / COLS;
     static_assert(SLOTS == 8 || SLOTS == 16 || SLOTS == 32, "column tile");
     constexpr int CPW = 64 / SLOTS;   // columns folded per wave
@@ -545,7 +624,7 @@ __global__ __launch_bounds__(1024) void bwd2_kernel(const float *part, int P,
     const int p1 = p0 + R < P ? p0 + R : P;
     float s = 0.0f;
     if (col < H) {
-        const float *base = part + (int64_t)blockIdx.y * P * H + col;
+        const float *base = part + (int64_t)blockIdx.y * partial_stride(P) * H + col;
         for (int p = p0; p < p1; p += 32) {
             float v[32];
 #pragma unroll
@@ -565,20 +644,16 @@ __global__ __launch_bounds__(1024) void bwd2_kernel(const float *part, int P,
         store_one(blockIdx.y == 0 ? dgamma + gcol : dbeta + gcol, t);
 }
 
-#ifndef RN_K2_WIDE_H
-#define RN_K2_WIDE_H 4096   // rows at least this long use 64-column tiles
-#endif
-
-
 template <class T>
 hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void *db,
                        hipStream_t s) {
-    if (H >= RN_K2_WIDE_H)
-        hipLaunchKernelGGL((bwd2_kernel<T, 64>), dim3((H + 63) / 64, ln ? 2 : 1),
-                           dim3(1024), 0, s, part, P, H, (T *)dg, (T *)db);
+    const unsigned np = ln ? 2 : 1;
+    if (partial_colmajor(H))
+        hipLaunchKernelGGL((bwd2_cols_kernel<T, 1>), dim3((H + 3) / 4, np), dim3(256), 0,
+                           s, part, P, H, (T *)dg, (T *)db);
     else
-        hipLaunchKernelGGL((bwd2_kernel<T, 32>), dim3((H + 31) / 32, ln ? 2 : 1),
-                           dim3(1024), 0, s, part, P, H, (T *)dg, (T *)db);
+        hipLaunchKernelGGL((bwd2_rows_kernel<T, 64>), dim3((H + 63) / 64, np), dim3(1024),
+                           0, s, part, P, H, (T *)dg, (T *)db);
     return hipGetLastError();
 }
 
@@ -648,9 +723,12 @@ __global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, W *dg
 
 // ------------------------------------------------------------------ plans --
 // A plan is <VEC, CPL, TW, RT>; rows up to 64*TW*VEC*CPL elements.
-template <int VEC_, int CPL_, int TW_, int RT_, bool PF_ = true>
+// PER_CU > 0 caps the persistent backward grid at that many workgroups per
+// CU (0: as many as are resident at once).
+template <int VEC_, int CPL_, int TW_, int RT_, bool PF_ = true, int PER_CU_ = 0>
 struct Plan {
     static constexpr int VEC = VEC_, CPL = CPL_, TW = TW_, RT = RT_;
+    static constexpr int PER_CU = PER_CU_;
     static constexpr bool PF = PF_;   // prefetch the next row into registers
     static constexpr int SPAN = 64 * TW_ * VEC_ * CPL_;
     static constexpr int THREADS = 64 * TW_ * RT_;
@@ -732,8 +810,8 @@ template <class T, class W, class P>
 inline int bwd_grid(int64_t N, int H, int cus) {
     const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
     constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true>;
-    const int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU
-                                         : resident_per_cu<k>(P::THREADS, lds);
+    int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU : resident_per_cu<k>(P::THREADS, lds);
+    if (P::PER_CU > 0 && per_cu > P::PER_CU) per_cu = P::PER_CU;
     return persistent_grid<P>(N, cus, per_cu, P::TW > 1 ? RN_BWD_MIN_ROWS_WIDE : 1);
 }
 

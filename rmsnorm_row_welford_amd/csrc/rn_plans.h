@@ -148,8 +148,10 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 #ifndef RN_FWD_BF16_16384
 #define RN_FWD_BF16_16384 Plan<8, 2, 16, 1>
 #endif
+// One 8-wave workgroup per CU: with two, the waves that a CU's arbitration
+// serves last leave a long tail of a few rows in flight.
 #ifndef RN_BWD_BF16_1024
-#define RN_BWD_BF16_1024 Plan<8, 2, 1, 8>
+#define RN_BWD_BF16_1024 Plan<8, 2, 1, 8, true, 1>
 #endif
 #ifndef RN_BWD_BF16_2048
 #define RN_BWD_BF16_2048 Plan<8, 2, 2, 4>

@@ -293,12 +293,13 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[slot * SPAN + sl * VEC + k] = src[k];
         __syncthreads();
-        float *dst = a.part + ((int64_t)p * gridDim.x + blockIdx.x) * H;
+        float *dst = a.part + (int64_t)p * partial_stride(gridDim.x) * H;
         for (int c0 = wave * CPW; c0 < H; c0 += WPG * CPW) {   // wave-uniform
             const int fc = c0 + lane / SLOTS;
             const float v = fc < H ? acc[(lane % SLOTS) * SPAN + fc] : 0.0f;
             const float t = seg_sum<SLOTS>(v);
-            if (lane % SLOTS == 0 && fc < H) dst[fc] = t;
+            if (lane % SLOTS == 0 && fc < H)
+                dst[partial_index(blockIdx.x, gridDim.x, H, fc)] = t;
         }
         __syncthreads();
     }
