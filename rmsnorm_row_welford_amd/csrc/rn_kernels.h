@@ -369,8 +369,12 @@ __device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
 // gradients separately).  ADD (RMSNorm only): the fused add+RMSNorm
 // backward, where x is the stored h, a.add (if set) is added to dx and
 // a.dx2 (if set) receives the same values as dx.
+// KEEP (plans that run one workgroup of at most 8 waves per CU, which
+// leaves each wave 256 registers): gamma is widened once for the whole
+// loop and the float32 x_hat and g of a row are kept from the sums to the
+// dx pass; otherwise only the packed chunks are kept and widened again.
 template <class T, class W, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC,
-          bool ADD = false>
+          bool ADD = false, bool KEEP = false>
 __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     using Lay = Layout<VEC, CPL, TW>;
@@ -387,8 +391,16 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     const int H = a.H;
     const Lay L(wit * 64 + lane, H);
 
+    static_assert(!KEEP || TW * RT <= 8, "KEEP needs 256 registers per wave");
     RawChunk<W, VEC> g[CPL];
     load_raw_row<0>(row_rsrc((const W *)a.gamma, H), L, g);
+    float gf[KEEP ? E : 1];
+    if constexpr (KEEP) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) gf[c * VEC + k] = g[c].get(k);
+    }
     float adg[ACC ? E : 1], adb[(ACC && LN) ? E : 1];
     if constexpr (ACC) {
 #pragma unroll
@@ -445,6 +457,7 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
 
         // Masked elements have dy = 0, so they add nothing below.
         float sg = 0.0f, sgx = 0.0f;
+        float kx[KEEP ? E : 1], kg[KEEP ? E : 1];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -452,7 +465,11 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
                 const int e = c * VEC + k;
                 const float dyv = cdy[c].get(k);
                 const float xhat = (cx[c].get(k) - cmu) * cs;
-                const float gv = dyv * g[c].get(k);
+                const float gv = dyv * (KEEP ? gf[e] : g[c].get(k));
+                if constexpr (KEEP) {
+                    kx[e] = xhat;
+                    kg[e] = gv;
+                }
                 if constexpr (ACC) {
                     adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
                     if constexpr (LN) adb[e] += dyv;
@@ -481,18 +498,21 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
         const float c1 = LN ? sg * a.inv_H : 0.0f;
         const float c2 = sgx * a.inv_H;
         if (active) {
+            if constexpr (!KEEP) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                opaque(cx[c].v);
-                opaque(cdy[c].v);
+                for (int c = 0; c < CPL; ++c) {
+                    opaque(cx[c].v);
+                    opaque(cdy[c].v);
+                }
             }
             float dx[E];
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
-                    const float xhat = (cx[c].get(k) - cmu) * cs;
-                    float t = cdy[c].get(k) * g[c].get(k);
+                    const int e = c * VEC + k;
+                    const float xhat = KEEP ? kx[e] : (cx[c].get(k) - cmu) * cs;
+                    float t = KEEP ? kg[e] : cdy[c].get(k) * g[c].get(k);
                     if constexpr (LN) t -= c1;
                     dx[c * VEC + k] = __builtin_fmaf(-xhat, c2, t) * cs;
                     if constexpr (ADD) {
@@ -729,6 +749,8 @@ template <int VEC_, int CPL_, int TW_, int RT_, bool PF_ = true, int PER_CU_ = 0
 struct Plan {
     static constexpr int VEC = VEC_, CPL = CPL_, TW = TW_, RT = RT_;
     static constexpr int PER_CU = PER_CU_;
+    // one workgroup of at most 8 waves per CU: room to keep float copies
+    static constexpr bool KEEP = PER_CU_ == 1 && TW_ * RT_ <= 8;
     static constexpr bool PF = PF_;   // prefetch the next row into registers
     static constexpr int SPAN = 64 * TW_ * VEC_ * CPL_;
     static constexpr int THREADS = 64 * TW_ * RT_;
@@ -809,7 +831,8 @@ hipError_t launch_fwd_op(int op, const FwdArgs &a, int cus, hipStream_t s) {
 template <class T, class W, class P>
 inline int bwd_grid(int64_t N, int H, int cus) {
     const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
-    constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true>;
+    constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true,
+                                   false, P::KEEP>;
     int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU : resident_per_cu<k>(P::THREADS, lds);
     if (P::PER_CU > 0 && per_cu > P::PER_CU) per_cu = P::PER_CU;
     return persistent_grid<P>(N, cus, per_cu, P::TW > 1 ? RN_BWD_MIN_ROWS_WIDE : 1);
@@ -823,7 +846,8 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
         if (P_ > 0) {
             const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
             hipLaunchKernelGGL(
-                (bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD>),
+                (bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD,
+                             P::KEEP>),
                 dim3(P_), dim3(P::THREADS), lds, s, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
