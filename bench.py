@@ -14,9 +14,13 @@ launch reads data last touched about 1 GiB of traffic earlier, far beyond
 the 256 MB Infinity Cache and 32 MB of L2.  The K timed steps run back to
 back between two HIP events on the launch stream (ms_per_step = elapsed/K).
 The per-op table times K launches of one op back to back over the rotating
-sets the same way.  --sweep adds the isolated protocol (a 512 MiB read sweep
-before each op, events around the op alone), which also pays each op's
-launch latency.
+sets, captured once in a HIP graph and replayed, each replay between two
+events on the launch stream (median of 5): kernel time plus the gaps
+between launches, without the per-call Python/ctypes overhead that would
+otherwise exceed the kernel time of the small shapes; "us_eager" is the
+same K launches issued one by one from Python.  --sweep adds the isolated
+protocol (a 512 MiB read sweep before each op, events around the op alone),
+which also pays each op's launch latency.
 
 value = the step's algorithmic HBM bytes / ms_per_step.  Prints ONE JSON line
 on stdout (diagnostics go to stderr).  One GPU only.
@@ -247,9 +251,9 @@ def time_op(sets, op, K, reps=3):
 
 def time_op_graph(sets, op, K, reps=5):
     """us per launch of one op with the host out of the loop: K launches
-    over the rotating sets captured once in a HIP graph, the graph replayed
-    `reps` times between two events (kernels and the gaps between them
-    only, no per-call host overhead)."""
+    over the rotating sets captured once in a HIP graph; each of `reps`
+    replays is timed between two events on the launch stream (kernels and
+    the gaps between them, no per-call host overhead); the median."""
     import torch
     for i in range(sets.M):
         sets.run(op, i)
@@ -261,15 +265,17 @@ def time_op_graph(sets, op, K, reps=5):
     graph.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    out = []
     for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / K)
     del graph
-    return e0.elapsed_time(e1) * 1e3 / (reps * K)
+    return float(np.median(out))
 
 
 def time_op_swept(sets, op, K, sweep):
@@ -309,9 +315,11 @@ def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24):
         sets = Sets(rn, arr, w.eps, M, dev, ops)
         row = {"N": N, "H": H, "sets": M}
         for k in ops:
-            us, _ = time_op(sets, k, max(K, 2 * M))
+            us = time_op_graph(sets, k, max(K, 2 * M))
+            us_eager, _ = time_op(sets, k, max(K, 2 * M))
             gbs = nb[k] / (us * 1e-6) / 1e9
-            row[k] = {"us": round(us, 3), "alg_bytes": nb[k], "GBps": round(gbs, 1),
+            row[k] = {"us": round(us, 3), "us_eager": round(us_eager, 3),
+                      "alg_bytes": nb[k], "GBps": round(gbs, 1),
                       "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
             log(f"{name:24s} {k:18s} {us:8.2f} us  {gbs:7.0f} GB/s  "
                 f"{100 * gbs / PEAK_GBS:5.1f}% of peak")
@@ -486,10 +494,12 @@ def main():
     per_op = {}
     K = max(12, 2 * args.sets)
     for k in ops + extras:
-        us, reps = time_op(sets, k, K)
+        us = time_op_graph(sets, k, K)
+        us_eager, _ = time_op(sets, k, K)
         gbs = nbytes[k] / (us * 1e-6) / 1e9
-        per_op[k] = {"us": round(us, 3), "alg_bytes": nbytes[k],
-                     "GBps": round(gbs, 1), "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
+        per_op[k] = {"us": round(us, 3), "us_eager": round(us_eager, 3),
+                     "alg_bytes": nbytes[k], "GBps": round(gbs, 1),
+                     "pct_peak": round(100 * gbs / PEAK_GBS, 2)}
         if k in extras:
             per_op[k]["in_step"] = False
         log(f"{k:18s} {us:8.2f} us  {gbs:7.0f} GB/s  {100 * gbs / PEAK_GBS:5.1f}% of peak")

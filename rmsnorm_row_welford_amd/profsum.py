@@ -33,17 +33,21 @@ def kernel_source_digest() -> str:
 
 
 def kernel_table(db: str):
+    """Per kernel and launch shape (one template serves several row shapes,
+    told apart by their grid): calls, average/min/max duration, share."""
     c = sqlite3.connect(db)
     rows = list(c.execute(
-        "select name, count(*), avg(duration), min(duration), max(duration), "
-        "sum(duration) from kernels group by name order by sum(duration) desc"))
-    tot = sum(r[5] for r in rows) or 1
-    out = [f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
-           f"{'max_us':>9s} {'pct':>6s}"]
-    for name, n, avg, mn, mx, s in rows:
+        "select name, grid_x / workgroup_x, grid_y, workgroup_x, count(*), "
+        "avg(duration), min(duration), max(duration), sum(duration) from kernels "
+        "group by name, grid_x, grid_y, workgroup_x order by sum(duration) desc"))
+    tot = sum(r[8] for r in rows) or 1
+    out = [f"{'kernel':90s} {'grid':>11s} {'wg':>5s} {'calls':>6s} {'avg_us':>9s} "
+           f"{'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for name, gx, gy, wx, n, avg, mn, mx, s in rows:
         short = name if len(name) <= 90 else name[:87] + "..."
-        out.append(f"{short:90s} {n:6d} {avg / 1e3:9.3f} {mn / 1e3:9.3f} "
-                   f"{mx / 1e3:9.3f} {100 * s / tot:6.2f}")
+        grid = f"{gx}x{gy}"
+        out.append(f"{short:90s} {grid:>11s} {wx:5d} {n:6d} {avg / 1e3:9.3f} "
+                   f"{mn / 1e3:9.3f} {mx / 1e3:9.3f} {100 * s / tot:6.2f}")
     return out
 
 
