@@ -27,7 +27,9 @@
  * to nearest even; fp16 overflow gives infinity) at the store.
  *
  * eps.  Added INSIDE the square root: rstd = 1 / sqrt(var + eps).  It must be
- * finite and > 0.
+ * a finite, positive, normal float (>= FLT_MIN, about 1.2e-38); anything
+ * else is RN_EINVAL.  rstd comes from the hardware reciprocal square root
+ * (within about 1 ulp of the exact value).
  *
  * Status.  Every function returns RN_OK (0) or a negative RN_E* code.  All
  * argument checks run before anything is enqueued: a non-zero return means

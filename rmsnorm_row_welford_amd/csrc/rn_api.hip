@@ -1,6 +1,7 @@
 // C-ABI entry points of librownorm.so: argument validation, overlap checks,
 // plan inputs (vectorizability, CU count) and kernel launches.  All checks
 // run before anything is enqueued.
+#include <float.h>
 #include <math.h>
 #include <initializer_list>
 #include <mutex>
@@ -109,8 +110,10 @@ int check_ld(int64_t ld, int64_t N, int64_t H) {
     if (N > 0 && ld > ((int64_t)1 << 58) / (N > 0 ? N : 1)) return RN_EINVAL;
     return RN_OK;
 }
+// eps must be a finite, positive, normal float (the kernels' reciprocal
+// square root of var + eps is then always taken of a normal number).
 int check_eps(float eps) {
-    if (!(eps > 0.0f) || !isfinite(eps)) return RN_EINVAL;
+    if (!(eps >= FLT_MIN) || !isfinite(eps)) return RN_EINVAL;
     return RN_OK;
 }
 

@@ -55,6 +55,11 @@ __device__ __forceinline__ unsigned pack_f16(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
 }
 
+// 1/sqrt(v) for a normal v > 0 (var + eps; eps is a positive normal float):
+// one v_rsq_f32 (about 1 ulp) instead of a correctly rounded square root and
+// an IEEE division, a chain of some 30 dependent instructions on every row.
+__device__ __forceinline__ float rsqrt_pos(float v) { return __builtin_amdgcn_rsqf(v); }
+
 // ------------------------------------------------------------ chunk I/O --
 // Load VEC consecutive elements at p (aligned to VEC elements) as float32.
 // NT selects the non-temporal hint for data read exactly once.

@@ -127,7 +127,10 @@ constexpr int fwd_min_waves() {
                : 1;
 }
 
-template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF>
+// FULL: H equals the plan's span, so every chunk is inside the row and
+// LayerNorm needs no masking selects.
+template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF,
+          bool FULL = false>
 __global__ __launch_bounds__(64 * TW * RT, (fwd_min_waves<T, W, VEC, CPL, TW, RT, OP, PF>()))
 void fwd_kernel(const FwdArgs a) {
     using Lay = Layout<VEC, CPL, TW>;
@@ -235,7 +238,7 @@ void fwd_kernel(const FwdArgs a) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     float &u = v[c * VEC + k];
-                    u = L.valid(c) ? u - pivot : 0.0f;
+                    u = (FULL || L.valid(c)) ? u - pivot : 0.0f;
                     s += u;
                 }
             float ms;   // mean of the shifted row
@@ -246,7 +249,7 @@ void fwd_kernel(const FwdArgs a) {
                 for (int c = 0; c < CPL; ++c)
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
-                        const float d = L.valid(c) ? v[c * VEC + k] - ms : 0.0f;
+                        const float d = (FULL || L.valid(c)) ? v[c * VEC + k] - ms : 0.0f;
                         q = __builtin_fmaf(d, d, q);
                     }
                 var = wave_sum(q) * a.inv_H;
@@ -257,7 +260,7 @@ void fwd_kernel(const FwdArgs a) {
                 for (int c = 0; c < CPL; ++c)
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
-                        const float d = L.valid(c) ? v[c * VEC + k] - mw : 0.0f;
+                        const float d = (FULL || L.valid(c)) ? v[c * VEC + k] - mw : 0.0f;
                         q = __builtin_fmaf(d, d, q);
                     }
                 q = wave_sum(q);
@@ -300,7 +303,7 @@ void fwd_kernel(const FwdArgs a) {
             }
             var = q * a.inv_H;
         }
-        const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
+        const float rstd = rsqrt_pos(var + a.eps);
 
         if (active) {
             float out[E];
@@ -804,9 +807,9 @@ inline int persistent_grid(int64_t N, int cus, int per_cu, int min_rows) {
 // finish, which streams better than a persistent loop.  When only one fits
 // (1024-thread rows), a persistent grid of one workgroup per CU whose teams
 // prefetch their next row.
-template <class T, class W, class P, int OP>
-hipError_t launch_fwd_plan(const FwdArgs &a, int cus, hipStream_t s) {
-    constexpr auto k = fwd_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, OP, P::PF>;
+template <class T, class W, class P, int OP, bool FULL>
+hipError_t launch_fwd_kernel(const FwdArgs &a, int cus, hipStream_t s) {
+    constexpr auto k = fwd_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, OP, P::PF, FULL>;
     const int resident = resident_per_cu<k>(P::THREADS, 0);
     const int per_cu = RN_FWD_PER_CU > 0 ? RN_FWD_PER_CU
                        : resident >= 2   ? (1 << 20)
@@ -814,6 +817,14 @@ hipError_t launch_fwd_plan(const FwdArgs &a, int cus, hipStream_t s) {
     const int grid = persistent_grid<P>(a.N, cus, per_cu, 1);
     hipLaunchKernelGGL(k, dim3(grid), dim3(P::THREADS), 0, s, a);
     return hipGetLastError();
+}
+
+template <class T, class W, class P, int OP>
+hipError_t launch_fwd_plan(const FwdArgs &a, int cus, hipStream_t s) {
+    // LayerNorm rows that fill the span exactly need no masking selects
+    if constexpr (OP == OP_LN)
+        if (a.H == P::SPAN) return launch_fwd_kernel<T, W, P, OP, true>(a, cus, s);
+    return launch_fwd_kernel<T, W, P, OP, false>(a, cus, s);
 }
 
 template <class T, class W, class P>

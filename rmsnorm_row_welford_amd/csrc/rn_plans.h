@@ -39,6 +39,15 @@ template <class T, class W, class P, int OP>
 hipError_t launch_fwd_seg(const FwdArgs &a, hipStream_t s) {
     constexpr int rows = P::WPG * P::RPW * P::IT;
     const int64_t grid = (a.N + rows - 1) / rows;
+    // LayerNorm rows that fill the span exactly need no masking selects
+    if constexpr (OP == OP_LN) {
+        if (a.H == P::SPAN) {
+            hipLaunchKernelGGL(
+                (fwd_seg_kernel<T, W, P::VEC, P::SEG, P::CPL, P::WPG, P::IT, OP, true>),
+                dim3((unsigned)grid), dim3(P::THREADS), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((fwd_seg_kernel<T, W, P::VEC, P::SEG, P::CPL, P::WPG, P::IT, OP>),
                        dim3((unsigned)grid), dim3(P::THREADS), 0, s, a);
     return hipGetLastError();

@@ -58,8 +58,11 @@ __device__ __forceinline__ float segment_sum(float v) {
 // Forward.  Wave w of workgroup b owns IT consecutive groups of 64/SEG rows
 // starting at row ((b*WPG + w)*IT)*(64/SEG); all IT groups are requested
 // before the first is reduced.  One workgroup per WPG*IT groups (not
-// persistent): the dispatcher keeps every CU fed.
-template <class T, class W, int VEC, int SEG, int CPL, int WPG, int IT, int OP>
+// persistent): the dispatcher keeps every CU fed.  FULL: H equals the
+// plan's span, so every chunk is inside the row and LayerNorm needs no
+// masking selects.
+template <class T, class W, int VEC, int SEG, int CPL, int WPG, int IT, int OP,
+          bool FULL = false>
 __global__ __launch_bounds__(64 * WPG, (sizeof(T) == 2 && sizeof(W) == 2 && VEC * CPL <= 16) ? 8 : 1)
 void fwd_seg_kernel(const FwdArgs a) {
     constexpr int RPW = 64 / SEG;
@@ -73,7 +76,7 @@ void fwd_seg_kernel(const FwdArgs a) {
     const int64_t N = a.N;
     bool valid[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) valid[c] = (c * SEG + sl) * VEC < H;
+    for (int c = 0; c < CPL; ++c) valid[c] = FULL || (c * SEG + sl) * VEC < H;
     const int64_t wrow = ((int64_t)blockIdx.x * WPG + wave) * (IT * RPW);
     if (wrow >= N) return;   // wave-uniform; no barriers below
 
@@ -168,7 +171,7 @@ void fwd_seg_kernel(const FwdArgs a) {
             for (int e = 0; e < E; ++e) q = __builtin_fmaf(v[e], v[e], q);
             var = segment_sum<SEG>(q) * a.inv_H;
         }
-        const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
+        const float rstd = rsqrt_pos(var + a.eps);
 
         float out[E];
 #pragma unroll

@@ -78,6 +78,7 @@ def ln_fwd(L, x=X, ldx=1024, g=G, b=B, y=Y, ldy=1024, m=M, r=R, N=8,
 @pytest.mark.parametrize("kw,want", [
     (dict(eps=0.0), EINVAL), (dict(eps=-1e-5), EINVAL),
     (dict(eps=float("nan")), EINVAL), (dict(eps=float("inf")), EINVAL),
+    (dict(eps=1e-40), EINVAL),               # subnormal in binary32
     (dict(dt=7), EDTYPE), (dict(H=0), EINVAL), (dict(N=-1), EINVAL),
     (dict(H=16385, ldx=16385, ldy=16385), EUNSUP),
     (dict(ldx=1000), EINVAL), (dict(ldy=1023), EINVAL),
