@@ -34,9 +34,11 @@ Outside the step, per_op also times (same protocol, same shape):
 
 shapes (not in the step): every op at the other workload shapes (16384x2048,
 512x16384, 2048x16384 forward and backward; 8192x1024 forward without a
-bias; the fused forward at 32768x4096), each with enough rotating copies
-that its data comes from HBM.  --shapes-only NAME[,NAME] (or all) times just
-those and prints their table.
+bias; the fused forward at 32768x4096), the other storage pairs at
+32768x1024 (binary16 throughout; bf16 with float32 parameters: all six
+ops) and short rows (1048576x128 forward and backward), each with enough
+rotating copies that its data comes from HBM.  --shapes-only NAME[,NAME]
+(or all) times just those and prints their table.
 
 decode (not in the step): the latency regime of a few rows (N = 1, 16, 64
 at H = 4096, bf16, data in cache): 50 back-to-back calls captured in one HIP
@@ -64,13 +66,21 @@ EXTRA_OPS = ("fused_add_rms_bwd", "fused_add_rms_fwd_inplace", "unfused_add_rms"
 # and wide backward shapes (with the forwards at those shapes), the
 # bias-free forward with half its rows constant, and the fused forward at
 # (B=16, T=2048, H=4096).
+# Beyond those: the other storage pairs at the headline shape (IEEE
+# binary16 throughout; bf16 activations with float32 gamma/beta and their
+# gradients) and short rows (2^20 rows of 128: a normalization over a head
+# dimension), each for every op they have a workload for.
 NORM_OPS = ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd")
+ALL_OPS = NORM_OPS + ("fused_add_rms_fwd", "fused_add_rms_bwd")
 SHAPES = (
     ("bwd_bf16_16384x2048", NORM_OPS),
     ("bwd_bf16_512x16384", NORM_OPS),
     ("bwd_bf16_2048x16384", NORM_OPS),
     ("fwd_bf16_8192x1024", ("ln_fwd", "rms_fwd")),
     ("fused_bf16_32768x4096", ("fused_add_rms_fwd",)),
+    ("f16_32768x1024", ALL_OPS),
+    ("mixed_bf16_f32w_32768x1024", ALL_OPS),
+    ("rows_bf16_1048576x128", NORM_OPS),
 )
 
 
@@ -78,20 +88,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(N, H, e, beta=True):
-    """Algorithmic HBM bytes of each op: every tensor read or written once
-    (beta=False: LayerNorm without a bias)."""
+def alg_bytes(N, H, e, beta=True, ep=None):
+    """Algorithmic HBM bytes of each op: every tensor read or written once.
+    e: bytes per activation element; ep: per parameter element (gamma, beta
+    and their gradients; default e); beta=False: LayerNorm without a bias."""
+    ep = e if ep is None else ep
     return {
-        "ln_fwd": 2 * N * H * e + (2 if beta else 1) * H * e + 8 * N,  # x,y,gamma,beta,stats
-        "rms_fwd": 2 * N * H * e + H * e + 4 * N,             # x,y,gamma,rstd
-        "fused_add_rms_fwd": 4 * N * H * e + H * e + 4 * N,   # x,r,h,y,gamma,rstd
-        "ln_bwd": 3 * N * H * e + 3 * H * e + 8 * N,          # dy,x,dx,gamma,dg,db,stats
-        "rms_bwd": 3 * N * H * e + 2 * H * e + 4 * N,         # dy,x,dx,gamma,dg,rstd
-        "fused_add_rms_bwd": 4 * N * H * e + 2 * H * e + 4 * N,  # dy,h,dh_in,dx,gamma,dg,rstd
-        "fused_add_rms_fwd_inplace": 4 * N * H * e + H * e + 4 * N,
+        "ln_fwd": 2 * N * H * e + (2 if beta else 1) * H * ep + 8 * N,  # x,y,gamma,beta,stats
+        "rms_fwd": 2 * N * H * e + H * ep + 4 * N,             # x,y,gamma,rstd
+        "fused_add_rms_fwd": 4 * N * H * e + H * ep + 4 * N,   # x,r,h,y,gamma,rstd
+        "ln_bwd": 3 * N * H * e + 3 * H * ep + 8 * N,          # dy,x,dx,gamma,dg,db,stats
+        "rms_bwd": 3 * N * H * e + 2 * H * ep + 4 * N,         # dy,x,dx,gamma,dg,rstd
+        "fused_add_rms_bwd": 4 * N * H * e + 2 * H * ep + 4 * N,  # dy,h,dh_in,dx,gamma,dg,rstd
+        "fused_add_rms_fwd_inplace": 4 * N * H * e + H * ep + 4 * N,
         # add: x, r read, h written; rms_fwd: h read, y written
-        "unfused_add_rms": 5 * N * H * e + H * e + 4 * N,
+        "unfused_add_rms": 5 * N * H * e + H * ep + 4 * N,
     }
+
+
+_TORCH_DT = {"bf16": "bfloat16", "f16": "float16", "f32": "float32"}
+_ESIZE = {"bf16": 2, "f16": 2, "f32": 4}
 
 
 def counters_traffic(op, shape_tag):
@@ -136,29 +152,32 @@ class Sets:
     bound to one copy each.  The forwards whose saved statistics a backward
     op reads run once per copy at set-up."""
 
-    def __init__(self, rn, arr, eps, M, dev, ops):
+    def __init__(self, rn, arr, eps, M, dev, ops, dtype="bf16", wdtype=None):
         import torch
         self.rn, self.eps, self.M = rn, eps, M
-        bf = torch.bfloat16
+        bf = getattr(torch, _TORCH_DT[dtype])
+        wt = getattr(torch, _TORCH_DT[wdtype or dtype])
         N, H = arr["x"].shape
         ops = list(ops)
         pre = [_BWD_NEEDS_FWD[o] for o in ops if o in _BWD_NEEDS_FWD]
         every = list(dict.fromkeys(pre + ops))
 
-        def to_dev(a):
-            return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
+        def to_dev(a, t=bf):
+            if a.dtype == np.uint16:      # 16-bit storage carried as bit patterns
+                return torch.from_numpy(a.view(np.int16)).view(t).to(dev)
+            return torch.from_numpy(a).to(dev)
 
         src = {"x": "x", "r": "residual", "r_in": "residual", "dy": "dy", "dh": "dy"}
         need_in = {k for o in every for k in _OP_INPUTS[o]}
         dev_src = {name: to_dev(arr[name]) for name in {src[k] for k in need_in}}
         base = {k: dev_src[src[k]] for k in need_in}
-        self.g = to_dev(arr["gamma"])
-        self.b = to_dev(arr["beta"]) if "beta" in arr else None
+        self.g = to_dev(arr["gamma"], wt)
+        self.b = to_dev(arr["beta"], wt) if "beta" in arr else None
         ws = {}
         if "ln_bwd" in ops:
-            ws["ws_ln"] = rn.workspace_bytes(N, H, bf, True)
+            ws["ws_ln"] = rn.workspace_bytes(N, H, bf, True, wt)
         if "rms_bwd" in ops or "fused_add_rms_bwd" in ops:
-            ws["ws_rms"] = rn.workspace_bytes(N, H, bf, False)
+            ws["ws_rms"] = rn.workspace_bytes(N, H, bf, False, wt)
         self.s = []
         for _ in range(M):
             t = {k: base[k].clone() for k in need_in}
@@ -168,7 +187,7 @@ class Sets:
                 for k in _OP_STATS_OUT.get(o, ()):
                     t[k] = torch.empty(N, dtype=torch.float32, device=dev)
             for k in ("dg", "db", "dg2", "dg3"):
-                t[k] = torch.empty(H, dtype=bf, device=dev)
+                t[k] = torch.empty(H, dtype=wt, device=dev)
             for k, nb in ws.items():
                 t[k] = torch.empty(nb, dtype=torch.uint8, device=dev)
             self.s.append(t)
@@ -309,11 +328,13 @@ def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24):
         w = synth.WORKLOADS[name]
         arr = synth.generate(w)
         N, H = w.N, w.H
-        nb = alg_bytes(N, H, 2, beta="beta" in arr)
+        nb = alg_bytes(N, H, _ESIZE[w.dtype], beta="beta" in arr,
+                       ep=_ESIZE[w.wdtype or w.dtype])
         per_launch = min(nb[o] for o in ops)
         M = int(min(32, max(3, -(-cold_bytes // per_launch) + 1)))
-        sets = Sets(rn, arr, w.eps, M, dev, ops)
-        row = {"N": N, "H": H, "sets": M}
+        sets = Sets(rn, arr, w.eps, M, dev, ops, w.dtype, w.wdtype)
+        row = {"N": N, "H": H, "dtype": w.dtype, "param_dtype": w.wdtype or w.dtype,
+               "sets": M}
         for k in ops:
             us = time_op_graph(sets, k, max(K, 2 * M))
             us_eager, _ = time_op(sets, k, max(K, 2 * M))
