@@ -119,6 +119,15 @@ __device__ __forceinline__ void store_row(rsrc_t r, const Layout<VEC, CPL, TW> &
 #ifndef RN_FWD_MINW8
 #define RN_FWD_MINW8 1
 #endif
+// Rows a prefetching (PF) forward team requests ahead of the one it works
+// on: three for 2-byte activations (a 16384-element row is 8 registers per
+// lane packed, so three in flight fit beside the one being reduced), one
+// for float32 (the fused op's two inputs would spill).  These plans run one
+// workgroup per CU, so the rows in flight per CU are what keeps HBM busy.
+#ifndef RN_FWD_PF_DEPTH
+#define RN_FWD_PF_DEPTH 3
+#endif
+
 template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF>
 constexpr int fwd_min_waves() {
     return ((TW * RT == 16 && !PF) ||
@@ -181,8 +190,10 @@ void fwd_kernel(const FwdArgs a) {
     // current row is reduced and written, so HBM reads stay in flight
     // across the reductions.  Without PF each row is fetched when its turn
     // comes and latency is hidden by occupancy alone.
-    Raw cur[NIN][CPL], nxt[NIN][PF ? CPL : 1];
-    float pcur = 0.0f, pnxt = 0.0f;
+    // PD rows are requested ahead (a ring of PD + 1 row buffers).
+    constexpr int PD = !PF ? 0 : sizeof(T) == 2 ? RN_FWD_PF_DEPTH : 1;
+    Raw cur[NIN][CPL], nxt[PD > 0 ? PD : 1][NIN][CPL];
+    float pcur = 0.0f, pnxt[PD > 0 ? PD : 1] = {};
     auto fetch = [&](int64_t row, auto &dst, float &piv) {
         if (row < N) {
             load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, dst[0]);
@@ -197,7 +208,12 @@ void fwd_kernel(const FwdArgs a) {
             piv = 0.0f;
         }
     };
-    if constexpr (PF) fetch((int64_t)blockIdx.x * RT + team, cur, pcur);
+    if constexpr (PD > 0) {
+        fetch((int64_t)blockIdx.x * RT + team, cur, pcur);
+#pragma unroll
+        for (int d = 0; d + 1 < PD; ++d)
+            fetch((int64_t)blockIdx.x * RT + team + (d + 1) * step, nxt[d], pnxt[d]);
+    }
 
     int parity = 0;
     for (int64_t grp = blockIdx.x; grp * RT < N; grp += gridDim.x) {
@@ -206,7 +222,7 @@ void fwd_kernel(const FwdArgs a) {
         if constexpr (TW == 1) {
             if (!active) break;
         }
-        if constexpr (PF) fetch(row + step, nxt, pnxt);
+        if constexpr (PD > 0) fetch(row + PD * step, nxt[PD - 1], pnxt[PD - 1]);
         else fetch(row, cur, pcur);
 
         float v[E];
@@ -277,17 +293,23 @@ void fwd_kernel(const FwdArgs a) {
                 var = wave_sum(__builtin_fmaf(n_lane * dm, dm, ql)) * a.inv_H;
                 parity ^= 1;
             }
-            // The float32 row is not kept across the statistics: it is
+            // Teams that run one workgroup per CU with deep prefetch keep the
+            // float32 row (x - pivot) across the statistics.  Otherwise it is
             // widened again from the packed chunks (made opaque so the
             // compiler cannot keep the first widening live), which frees E
-            // registers on the wide plans.  Same operations, same bits.
+            // registers for occupancy.  Same operations, same bits.
+            if constexpr (PD >= 2) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) opaque(cur[0][c].v);
+                for (int e = 0; e < E; ++e) v[e] -= ms;   // x - mean
+            } else {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
+                for (int c = 0; c < CPL; ++c) opaque(cur[0][c].v);
 #pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    v[c * VEC + k] = (cur[0][c].get(k) - pivot) - ms;   // x - mean
+                for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k)
+                        v[c * VEC + k] = (cur[0][c].get(k) - pivot) - ms;   // x - mean
+            }
             mean = pivot + ms;
         } else {
             float q = 0.0f;
@@ -323,12 +345,20 @@ void fwd_kernel(const FwdArgs a) {
                 if (a.rstd) a.rstd[row] = rstd;
             }
         }
-        if constexpr (PF) {
+        if constexpr (PD > 0) {
 #pragma unroll
             for (int i = 0; i < NIN; ++i)
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) cur[i][c] = nxt[i][c];
-            pcur = pnxt;
+                for (int c = 0; c < CPL; ++c) cur[i][c] = nxt[0][i][c];
+            pcur = pnxt[0];
+#pragma unroll
+            for (int d = 0; d + 1 < PD; ++d) {
+#pragma unroll
+                for (int i = 0; i < NIN; ++i)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) nxt[d][i][c] = nxt[d + 1][i][c];
+                pnxt[d] = pnxt[d + 1];
+            }
         }
     }
 }
