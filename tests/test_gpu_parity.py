@@ -240,9 +240,10 @@ def test_bwd_workloads(orc, name, op):
 # The LayerNorm page's validation list (64 ... 2049) plus tiny rows, ragged
 # tails, element-wise-path shapes and the largest rows.
 # Row lengths that fill a plan's span exactly (64 ... 16384: no masking) and
-# ragged ones (masked tails, element-wise plans).
+# ragged ones (masked tails, element-wise plans; 4097 and 6002 take the
+# row-major partial rows with a length that is not a multiple of 4).
 SHAPES = [64, 128, 256, 512, 768, 1024, 2048, 2049, 1, 2, 3, 1000, 3000, 4095,
-          4096, 8192, 12288, 16384]
+          4096, 4097, 6002, 8192, 12288, 16384]
 
 
 # storage pairs: activations[/parameters]
