@@ -190,10 +190,13 @@ void fwd_kernel(const FwdArgs a) {
     // current row is reduced and written, so HBM reads stay in flight
     // across the reductions.  Without PF each row is fetched when its turn
     // comes and latency is hidden by occupancy alone.
-    // PD rows are requested ahead (a ring of PD + 1 row buffers).
+    // PD rows are requested ahead: a ring of PD + 1 row buffers, which the
+    // loop below walks unrolled so that each buffer keeps its registers (no
+    // copies from one buffer to the next).
     constexpr int PD = !PF ? 0 : sizeof(T) == 2 ? RN_FWD_PF_DEPTH : 1;
-    Raw cur[NIN][CPL], nxt[PD > 0 ? PD : 1][NIN][CPL];
-    float pcur = 0.0f, pnxt[PD > 0 ? PD : 1] = {};
+    constexpr int NR = PD + 1;
+    Raw ring[NR][NIN][CPL];
+    float pring[NR] = {};
     auto fetch = [&](int64_t row, auto &dst, float &piv) {
         if (row < N) {
             load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, dst[0]);
@@ -208,23 +211,13 @@ void fwd_kernel(const FwdArgs a) {
             piv = 0.0f;
         }
     };
-    if constexpr (PD > 0) {
-        fetch((int64_t)blockIdx.x * RT + team, cur, pcur);
 #pragma unroll
-        for (int d = 0; d + 1 < PD; ++d)
-            fetch((int64_t)blockIdx.x * RT + team + (d + 1) * step, nxt[d], pnxt[d]);
-    }
+    for (int d = 0; d < PD; ++d)
+        fetch((int64_t)blockIdx.x * RT + team + d * step, ring[d], pring[d]);
 
     int parity = 0;
-    for (int64_t grp = blockIdx.x; grp * RT < N; grp += gridDim.x) {
-        const int64_t row = grp * RT + team;
-        const bool active = row < N;
-        if constexpr (TW == 1) {
-            if (!active) break;
-        }
-        if constexpr (PD > 0) fetch(row + PD * step, nxt[PD - 1], pnxt[PD - 1]);
-        else fetch(row, cur, pcur);
-
+    // One row of the team: statistics, y (and h), saved statistics.
+    auto process = [&](auto &cur, const float pcur, const int64_t row, const bool active) {
         float v[E];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
@@ -345,19 +338,30 @@ void fwd_kernel(const FwdArgs a) {
                 if (a.rstd) a.rstd[row] = rstd;
             }
         }
-        if constexpr (PD > 0) {
+    };
+
+    // Persistent loop over the team's rows, unrolled over the ring: the row
+    // in buffer u is worked on while buffer (u + PD) % NR receives the row
+    // PD steps ahead.
+    int64_t grp = blockIdx.x;
+    bool done = grp * RT >= N;
+    while (!done) {
 #pragma unroll
-            for (int i = 0; i < NIN; ++i)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) cur[i][c] = nxt[0][i][c];
-            pcur = pnxt[0];
-#pragma unroll
-            for (int d = 0; d + 1 < PD; ++d) {
-#pragma unroll
-                for (int i = 0; i < NIN; ++i)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) nxt[d][i][c] = nxt[d + 1][i][c];
-                pnxt[d] = pnxt[d + 1];
+        for (int u = 0; u < NR; ++u) {
+            if (!done) {
+                const int64_t row = grp * RT + team;
+                const bool active = row < N;
+                if (TW == 1 && !active) {
+                    done = true;   // wave-uniform; single-wave teams use no barrier
+                } else {
+                    if constexpr (PD > 0)
+                        fetch(row + PD * step, ring[(u + PD) % NR], pring[(u + PD) % NR]);
+                    else
+                        fetch(row, ring[u], pring[u]);
+                    process(ring[u], pring[u], row, active);
+                    grp += gridDim.x;
+                    done = grp * RT >= N;
+                }
             }
         }
     }
