@@ -479,7 +479,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the row-normalization path has no "
-              "multi-GPU part in this build; run with --gpus 1", file=sys.stderr)
+              "multi-GPU part; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

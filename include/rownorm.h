@@ -78,7 +78,7 @@ enum {
     RN_EOVERLAP = -3,      /* an output overlaps an input or another output */
     RN_EWORKSPACE = -4,    /* backward workspace missing or too small       */
     RN_EHIP = -5,          /* a HIP runtime call failed                     */
-    RN_EUNSUPPORTED = -6   /* H above the largest row this build supports   */
+    RN_EUNSUPPORTED = -6   /* H above the largest row length (rn_max_hidden) */
 };
 
 /* LayerNorm forward ("Write Triton Layernorm Kernel", Required reasoning
