@@ -448,6 +448,59 @@ def test_bitwise_deterministic(N, H):
         assert torch.equal(a, b_)
 
 
+# Tall shapes on the one-workgroup-per-CU team plans (H 1024/2048/4096:
+# 8/4/2 rows per team step; N ragged).
+@pytest.mark.parametrize("N,H", [(32771, 1024), (12293, 2048), (6151, 4096)])
+def test_workspace_contents_on_entry(orc, N, H):
+    """Whatever the workspace holds on entry (zeros, all-ones bytes, 0xFE
+    bytes, random bytes, what this call or a call of another shape left),
+    the backward gives the same bits, and they match the oracle."""
+    arr = synth.custom(31 + H, N, H, "bf16")
+    x, dy, g, dh = (to_dev(arr[k]) for k in ("x", "dy", "gamma", "dh"))
+    bf = torch.bfloat16
+    ws = torch.empty(rn.workspace_bytes(N, H, bf, True), dtype=torch.uint8, device=DEV)
+    _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+    _, rs2 = rn.rms_fwd(x, g, 1e-5)
+
+    def run():
+        dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5, workspace=ws)
+        dx2, dg2 = rn.rms_bwd(dy, x, g, rs2, 1e-5, workspace=ws)
+        dx3, _, dg3 = rn.fused_add_rms_bwd(dy, x, g, rs2, 1e-5, dh_in=dh, workspace=ws)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (dx, dg, db, dx2, dg2, dx3, dg3)]
+
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    rand = torch.randint(0, 256, (ws.numel(),), dtype=torch.uint8, generator=gen)
+    ws.zero_()
+    want = run()
+    # the first result against the oracle (LayerNorm: dx rows, dgamma, dbeta)
+    e = oracle.eps_at_boundary(1e-5)
+    xd, dyd, gd = (orc.decode(arr[k], "bf16") for k in ("x", "dy", "gamma"))
+    dx_o, dg_o, db_o, _, rstd_o = orc.ln_bwd(dyd, xd, gd, e)
+    rows = sample_rows(N)
+    tol.check_out(host(want[0])[rows], dx_o[rows], "bf16", orc, "dx",
+                  term_scale=tol.dx_term_scale(dyd[rows], gd, rstd_o[rows]))
+    tol.check_param(orc.decode(host(want[1]), "bf16"), dg_o, "dgamma")
+    tol.check_param(orc.decode(host(want[2]), "bf16"), db_o, "dbeta")
+    _, dg_r, _ = orc.rms_bwd(dyd, xd, gd, e)
+    tol.check_param(orc.decode(host(want[4]), "bf16"), dg_r, "dgamma (rms)")
+
+    states = {"reused": None, "ones": 0xFF, "fe": 0xFE, "random": rand}
+    for name, fill in states.items():
+        if isinstance(fill, int):
+            ws.fill_(fill)
+        elif fill is not None:
+            ws.copy_(fill.to(DEV))
+        got = run()
+        for a, b in zip(want, got):
+            assert torch.equal(a, b), f"workspace state {name!r} changed the result"
+    # a call of another shape on the same workspace, then this one again
+    n2 = N // 2 + 3
+    rn.rms_bwd(dy[:n2], x[:n2], g, rs2[:n2], 1e-5, workspace=ws)
+    for a, b in zip(want, run()):
+        assert torch.equal(a, b), "a call of another shape changed the result"
+
+
 @pytest.mark.parametrize("N", [0, 1, 2, 7, 255, 513])
 def test_row_counts(orc, N):
     """N = 0 (no rows: dgamma = dbeta = 0), N below the partial-row count,
@@ -500,13 +553,14 @@ def test_add_helper(orc, dtype, n, off):
     assert np.array_equal(host(a), want)
 
 
-@pytest.mark.parametrize("N,H", [(64, 4096), (1, 8192), (333, 128)])
+@pytest.mark.parametrize("N,H", [(64, 4096), (1, 8192), (333, 128), (16389, 1024)])
 def test_graph_capture_replays(N, H):
     """The entry points enqueue only kernels on the caller's stream, so a HIP
     graph can capture them: fused forward + fused backward + LayerNorm
     forward/backward captured once and replayed four times, with eager work
     and synchronizations between replays; every replay must reproduce the
-    eager results bit for bit."""
+    eager results bit for bit; (16389, 1024) is a tall ragged shape on a
+    persistent team plan."""
     arr = synth.custom(19, N, H, "bf16")
     x, r, g, b, dy, dh = (to_dev(arr[k]) for k in ("x", "residual", "gamma", "beta",
                                                    "dy", "dh"))
