@@ -146,9 +146,10 @@ void fwd_kernel(const FwdArgs a) {
     using Raw = RawChunk<T, VEC>;
     using RawW = RawChunk<W, VEC>;
     constexpr int E = Lay::E;
-    constexpr int NV = (OP == OP_LN) ? 2 : 1;
+    // values each wave posts for the cross-wave step: LayerNorm (pivot,
+    // shifted mean, M2), RMSNorm the sum of squares
+    constexpr int NV = (OP == OP_LN) ? 3 : 1;
     constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;   // row inputs: x [, residual]
-    constexpr bool PIVOT_LOAD = (OP == OP_LN) && (TW > 1);
     __shared__ float red[(TW > 1) ? 2 * RT * TW * NV : 1];
 
     const int lane = threadIdx.x & 63;
@@ -168,11 +169,13 @@ void fwd_kernel(const FwdArgs a) {
             for (int c = 0; c < CPL; ++c) bt[c].zero();
     }
 
-    // Cross-wave LayerNorm statistics: wave w holds the two-pass mean m_w and
-    // M2_w of its n_w elements.  Lane w of every wave later picks up wave w's
-    // state, and the states are combined with the parallel Welford merge in
-    // its multi-way form: mean = sum(n_w m_w)/H,
-    // M2 = sum(M2_w + n_w (m_w - mean)^2).  n_w depends only on H.
+    // Cross-wave LayerNorm statistics: wave w shifts its n_w elements by its
+    // own first element p_w and holds the two-pass mean m_w and M2_w of the
+    // shifted values.  Lane w of every wave later picks up wave w's state;
+    // the means are restated against wave 0's pivot, d_w = (p_w - p_0) + m_w,
+    // and the states are combined with the parallel Welford merge in its
+    // multi-way form: mean - p_0 = sum(n_w d_w)/H,
+    // M2 = sum(M2_w + n_w (d_w - (mean - p_0))^2).  n_w depends only on H.
     float inv_cnt = 0.0f, n_lane = 0.0f;
     if constexpr (OP == OP_LN && TW > 1) {
         const float nw = (float)Lay::wave_count(wit, H);
@@ -196,28 +199,24 @@ void fwd_kernel(const FwdArgs a) {
     constexpr int PD = !PF ? 0 : sizeof(T) == 2 ? RN_FWD_PF_DEPTH : 1;
     constexpr int NR = PD + 1;
     Raw ring[NR][NIN][CPL];
-    float pring[NR] = {};
-    auto fetch = [&](int64_t row, auto &dst, float &piv) {
+    auto fetch = [&](int64_t row, auto &dst) {
         if (row < N) {
             load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, dst[0]);
             if constexpr (OP == OP_FUSED)
                 load_raw_row<RN_LOAD_AUX>(row_rsrc(rb + row * a.ldr, H), L, dst[1]);
-            if constexpr (PIVOT_LOAD) load_chunk<1, false>(xb + row * a.ldx, &piv);
         } else {
 #pragma unroll
             for (int i = 0; i < NIN; ++i)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) dst[i][c].zero();
-            piv = 0.0f;
         }
     };
 #pragma unroll
-    for (int d = 0; d < PD; ++d)
-        fetch((int64_t)blockIdx.x * RT + team + d * step, ring[d], pring[d]);
+    for (int d = 0; d < PD; ++d) fetch((int64_t)blockIdx.x * RT + team + d * step, ring[d]);
 
     int parity = 0;
     // One row of the team: statistics, y (and h), saved statistics.
-    auto process = [&](auto &cur, const float pcur, const int64_t row, const bool active) {
+    auto process = [&](auto &cur, const int64_t row, const bool active) {
         float v[E];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
@@ -233,14 +232,13 @@ void fwd_kernel(const FwdArgs a) {
 
         float mean = 0.0f, var;
         if constexpr (OP == OP_LN) {
-            // Shift by a pivot (the row's first element) so that the sums and
-            // deviations are formed from values of the row's spread, not of
-            // its mean: with |mean| >> std the float32 rounding of the mean
-            // itself would otherwise dominate x - mean.  v becomes x - pivot
-            // on valid elements and 0 on masked ones.
-            float pivot;
-            if constexpr (TW == 1) pivot = lane_value(v[0], 0);
-            else pivot = pcur;
+            // Shift by a pivot (the first element of the row, or of the
+            // wave's part of it) so that the sums and deviations are formed
+            // from values of the row's spread, not of its mean: with
+            // |mean| >> std the float32 rounding of the mean itself would
+            // otherwise dominate x - mean.  v becomes x - pivot on valid
+            // elements and 0 on masked ones.
+            const float pivot = lane_value(v[0], 0);
             float s = 0.0f;
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
@@ -250,7 +248,7 @@ void fwd_kernel(const FwdArgs a) {
                     u = (FULL || L.valid(c)) ? u - pivot : 0.0f;
                     s += u;
                 }
-            float ms;   // mean of the shifted row
+            float ms;   // subtracted from the shifted values: they become x - mean
             if constexpr (TW == 1) {
                 ms = wave_sum(s) * a.inv_H;
                 float q = 0.0f;
@@ -262,6 +260,7 @@ void fwd_kernel(const FwdArgs a) {
                         q = __builtin_fmaf(d, d, q);
                     }
                 var = wave_sum(q) * a.inv_H;
+                mean = pivot + ms;
             } else {
                 const float mw = wave_sum(s) * inv_cnt;
                 float q = 0.0f;
@@ -273,17 +272,22 @@ void fwd_kernel(const FwdArgs a) {
                         q = __builtin_fmaf(d, d, q);
                     }
                 q = wave_sum(q);
-                float *slot = red + ((parity * RT + team) * TW) * 2;
+                float *slot = red + ((parity * RT + team) * TW) * NV;
                 if (lane == 0) {
-                    slot[2 * wit] = mw;
-                    slot[2 * wit + 1] = q;
+                    slot[NV * wit] = pivot;
+                    slot[NV * wit + 1] = mw;
+                    slot[NV * wit + 2] = q;
                 }
                 __syncthreads();
-                const float ml = lane < TW ? slot[2 * lane] : 0.0f;
-                const float ql = lane < TW ? slot[2 * lane + 1] : 0.0f;
-                ms = wave_sum(n_lane * ml) * a.inv_H;
-                const float dm = ml - ms;
+                const float p0 = slot[0];   // wave 0's pivot: the row's first element
+                const float dl = lane < TW ? (slot[NV * lane] - p0) + slot[NV * lane + 1] : 0.0f;
+                const float ql = lane < TW ? slot[NV * lane + 2] : 0.0f;
+                const float m0 = wave_sum(n_lane * dl) * a.inv_H;   // mean - p0
+                const float dm = dl - m0;
                 var = wave_sum(__builtin_fmaf(n_lane * dm, dm, ql)) * a.inv_H;
+                // this wave's shifted values minus ms are x - mean
+                ms = m0 - (pivot - p0);
+                mean = p0 + m0;
                 parity ^= 1;
             }
             // Teams that run one workgroup per CU with deep prefetch keep the
@@ -303,7 +307,6 @@ void fwd_kernel(const FwdArgs a) {
                     for (int k = 0; k < VEC; ++k)
                         v[c * VEC + k] = (cur[0][c].get(k) - pivot) - ms;   // x - mean
             }
-            mean = pivot + ms;
         } else {
             float q = 0.0f;
 #pragma unroll
@@ -355,10 +358,10 @@ void fwd_kernel(const FwdArgs a) {
                     done = true;   // wave-uniform; single-wave teams use no barrier
                 } else {
                     if constexpr (PD > 0)
-                        fetch(row + PD * step, ring[(u + PD) % NR], pring[(u + PD) % NR]);
+                        fetch(row + PD * step, ring[(u + PD) % NR]);
                     else
-                        fetch(row, ring[u], pring[u]);
-                    process(ring[u], pring[u], row, active);
+                        fetch(row, ring[u]);
+                    process(ring[u], row, active);
                     grp += gridDim.x;
                     done = grp * RT >= N;
                 }

@@ -302,10 +302,14 @@ def test_qk_norm_bf16_1048576x128(orc):
     check_bwd(orc, arr, "bf16", w.eps, layernorm=False, rows=rows)
 
 
+# Rows whose mean dwarfs their spread, on single-wave rows (1024) and on
+# rows split over 4 and 16 waves (4096, 16384), where each wave shifts by its
+# own first element and the waves' means meet relative to wave 0's.
+@pytest.mark.parametrize("H", [1024, 4096, 16384])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_small_variance_rows(orc, dtype):
-    # fp32 rows with |mean|/sigma = 50 and constant rows
-    N, H = 40, 1024
+def test_small_variance_rows(orc, dtype, H):
+    # rows with |mean|/sigma = 50, and constant rows
+    N = 40
     arr = synth.custom(5, N, H, dtype, x=(0.0, 1.0), half_shifted=(2.0, 0.04))
     check_ln_fwd(orc, arr, dtype, 1e-5)
     check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
@@ -314,6 +318,11 @@ def test_small_variance_rows(orc, dtype):
     arr2 = dict(arr, x=c)
     y, mean, rstd, _ = check_ln_fwd(orc, arr2, dtype, 1e-5)
     assert np.all(orc.decode(host(y), dtype) == orc.decode(arr["beta"], dtype)[None, :])
+    if dtype == "f32":
+        # |mean|/sigma = 2e4: x - mean formed against a float32 mean of 1000
+        # would be off by ~1e-3 relative; the pivot shift keeps it exact
+        arr3 = synth.custom(6, N, H, dtype, x=(1000.0, 0.05))
+        check_ln_fwd(orc, arr3, dtype, 1e-5)
 
 
 @pytest.mark.parametrize("H", [1024, 128, 40, 24])
