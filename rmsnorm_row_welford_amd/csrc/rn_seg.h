@@ -34,12 +34,14 @@ __device__ __forceinline__ float lane_pull(float v, int src) {
 
 constexpr uint32_t kOffOOB = 0x80000000u;   // beyond every group's range
 
-// Resource over rows [row0, row0 + n) (n >= 1) of a tensor with row stride ld.
+// Resource over rows [row0, row0 + n) of a tensor with row stride ld; for
+// n <= 0 an empty range (every access falls outside it).
 template <class T>
 __device__ __forceinline__ rsrc_t group_rsrc(const void *base, int64_t row0, int n,
                                              int64_t ld, int H) {
-    const T *p = (const T *)base + row0 * ld;
-    return make_rsrc(p, (uint32_t)(((int64_t)(n - 1) * ld + H) * (int64_t)sizeof(T)));
+    const T *p = (const T *)base + (n > 0 ? row0 : 0) * ld;
+    return make_rsrc(
+        p, n > 0 ? (uint32_t)(((int64_t)(n - 1) * ld + H) * (int64_t)sizeof(T)) : 0u);
 }
 
 // Byte offset of lane (seg, sl)'s chunk, or kOffOOB when the chunk is past H.
@@ -67,6 +69,13 @@ __global__ __launch_bounds__(64 * WPG, (sizeof(T) == 2 && sizeof(W) == 2 && VEC 
 void fwd_seg_kernel(const FwdArgs a) {
     constexpr int RPW = 64 / SEG;
     constexpr int E = VEC * CPL;
+    // The workgroup's rows are consecutive: their statistics meet in LDS and
+    // go out in one coalesced store per output, not one small store per
+    // segment (scattered 4-16 byte writes cost several times their size).
+    constexpr int WROWS = WPG * IT * RPW;
+    static_assert(WROWS <= 64, "one wave stores the workgroup's statistics");
+    constexpr int NST = (OP == OP_LN) ? 2 : 1;
+    __shared__ float stats[NST][WROWS];
     using Raw = RawChunk<T, VEC>;
     using RawW = RawChunk<W, VEC>;
     const int lane = threadIdx.x & 63;
@@ -77,8 +86,8 @@ void fwd_seg_kernel(const FwdArgs a) {
     bool valid[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) valid[c] = FULL || (c * SEG + sl) * VEC < H;
-    const int64_t wrow = ((int64_t)blockIdx.x * WPG + wave) * (IT * RPW);
-    if (wrow >= N) return;   // wave-uniform; no barriers below
+    const int64_t row_base = (int64_t)blockIdx.x * WROWS;   // the workgroup's first row
+    const int64_t wrow = row_base + (int64_t)wave * (IT * RPW);
 
     RawW g[CPL], bt[CPL];
 #pragma unroll
@@ -94,24 +103,27 @@ void fwd_seg_kernel(const FwdArgs a) {
         }
     }
 
+    // Every group's loads are issued, those of groups past N into an empty
+    // range (they return 0 and touch no memory): with no branch around them
+    // the compiler's wait before each group counts exactly the operations
+    // issued after it, instead of draining the earlier groups' stores.
     Raw cx[IT][CPL], cr[(OP == OP_FUSED) ? IT : 1][CPL];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int64_t row0 = wrow + (int64_t)i * RPW;
-        if (row0 < N) {
-            const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
-            const rsrc_t rx = group_rsrc<T>(a.x, row0, n, a.ldx, H);
+        const int64_t left = N - row0;
+        const int n = left <= 0 ? 0 : (left < RPW ? (int)left : RPW);
+        const rsrc_t rx = group_rsrc<T>(a.x, row0, n, a.ldx, H);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            cx[i][c].template bload<RN_LOAD_AUX>(
+                rx, seg_off<T, VEC>(seg, c * SEG + sl, a.ldx, valid[c]));
+        if constexpr (OP == OP_FUSED) {
+            const rsrc_t rr = group_rsrc<T>(a.res, row0, n, a.ldr, H);
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                cx[i][c].template bload<RN_LOAD_AUX>(
-                    rx, seg_off<T, VEC>(seg, c * SEG + sl, a.ldx, valid[c]));
-            if constexpr (OP == OP_FUSED) {
-                const rsrc_t rr = group_rsrc<T>(a.res, row0, n, a.ldr, H);
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    cr[i][c].template bload<RN_LOAD_AUX>(
-                        rr, seg_off<T, VEC>(seg, c * SEG + sl, a.ldr, valid[c]));
-            }
+                cr[i][c].template bload<RN_LOAD_AUX>(
+                    rr, seg_off<T, VEC>(seg, c * SEG + sl, a.ldr, valid[c]));
         }
     }
 
@@ -190,12 +202,18 @@ void fwd_seg_kernel(const FwdArgs a) {
             bstore_chunk<VEC>((T *)nullptr, ry,
                               seg_off<T, VEC>(seg, c * SEG + sl, a.ldy, valid[c]),
                               out + c * VEC);
-        if (sl == 0 && seg < n) {
-            if constexpr (OP == OP_LN) {
-                if (a.mean) a.mean[row0 + seg] = mean;
-            }
-            if (a.rstd) a.rstd[row0 + seg] = rstd;
+        if (sl == 0) {
+            const int lr = (wave * IT + i) * RPW + seg;   // row0 + seg - row_base
+            if constexpr (OP == OP_LN) stats[1][lr] = mean;
+            stats[0][lr] = rstd;
         }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < WROWS && row_base + lane < N) {
+        if constexpr (OP == OP_LN) {
+            if (a.mean) a.mean[row_base + lane] = stats[1][lane];
+        }
+        if (a.rstd) a.rstd[row_base + lane] = stats[0][lane];
     }
 }
 
