@@ -404,6 +404,15 @@ __device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
 }
 
 // ---------------------------------------------------------------- backward --
+// Rows a prefetching (PF) backward team requests ahead of the one it works
+// on.
+#ifndef RN_BWD_PF_DEPTH
+#define RN_BWD_PF_DEPTH 1
+#endif
+#ifndef RN_BWD_RING
+#define RN_BWD_RING 1
+#endif
+
 // ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
 // kernel only writes dx (the column-sum strategy computes the parameter
 // gradients separately).  ADD (RMSNorm only): the fused add+RMSNorm
@@ -458,44 +467,79 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
 
     // x and dy stay in their storage form (bf16: two per register); x_hat
     // and g are formed from them once for the sums and once more for dx.
-    // With PF the next row's chunks and statistics are requested before the
-    // current row is worked on.
-    Raw cx[CPL], cdy[CPL], nx[PF ? CPL : 1], ndy[PF ? CPL : 1];
-    Raw cad[ADD ? CPL : 1], nad[(ADD && PF) ? CPL : 1];
+    // With PF the next row is requested before the current one is worked
+    // on, in one of two loops:
+    //  - the copying loop: the row lands in a second buffer that is copied
+    //    into the first after the current row; rows past N are zero-filled
+    //    without loads;
+    //  - the ring (RING): rows are requested RN_BWD_PF_DEPTH turns ahead
+    //    into buffers walked unrolled, with no copies.  Every load and store
+    //    is issued whatever the row: rows past N (and an absent residual
+    //    gradient) use empty ranges, which load 0 and store nothing, so the
+    //    compiler's wait before each row counts exactly what was issued
+    //    after that row's loads.
+    // The ring pays on multi-wave teams that keep float copies (1.5 us at
+    // 16384 x 2048); on single-wave teams and 16-wave teams the per-row range
+    // set-up costs more than it saves (and 16-wave teams would spill).
+    // RN_BWD_RING: 0 the copying loop everywhere, 1 the ring on multi-wave
+    // teams that keep float copies, 2 the ring on every prefetching plan.
+    constexpr bool RING = PF && (RN_BWD_RING == 2 || (RN_BWD_RING == 1 && KEEP && TW > 1));
+    constexpr int PD = RING ? RN_BWD_PF_DEPTH : (PF ? 1 : 0);
+    constexpr int NR = PD + 1;
+    struct Buf {
+        Raw x[CPL], dy[CPL], ad[ADD ? CPL : 1];
+        float mu, s;
+    };
+    Buf ring[RING ? NR : 1];   // the copying loop uses cur and nxt instead
+    Buf cur, nxt;
     const T *addb = (const T *)a.add;
     const bool has_add = ADD && addb != nullptr;
-    float cmu = 0.0f, cs = 0.0f, nmu = 0.0f, ns = 0.0f;
-    auto fetch = [&](int64_t row, auto &x_, auto &dy_, auto &ad_, float &mu_, float &s_) {
-        if (row < N) {
-            load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, x_);
-            load_raw_row<RN_LOAD_AUX>(row_rsrc(dyb + row * a.lddy, H), L, dy_);
-            if constexpr (ADD) {
-                if (has_add) load_raw_row<RN_LOAD_AUX>(row_rsrc(addb + row * a.ldadd, H), L, ad_);
-            }
-            mu_ = LN ? a.mean[row] : 0.0f;
-            s_ = a.rstd[row];
-        } else {
+    auto fetch = [&](int64_t row, Buf &b) {
+        if constexpr (!RING) {
+            // the copying loop: rows past N are zero-filled without loads
+            // (the statistics go through locals: stores to either member
+            // from two branches would keep the buffer in scratch)
+            float mu = 0.0f, sv = 0.0f;
+            if (row < N) {
+                load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, b.x);
+                load_raw_row<RN_LOAD_AUX>(row_rsrc(dyb + row * a.lddy, H), L, b.dy);
+                if constexpr (ADD) {
+                    if (has_add)
+                        load_raw_row<RN_LOAD_AUX>(row_rsrc(addb + row * a.ldadd, H), L, b.ad);
+                }
+                if constexpr (LN) mu = a.mean[row];
+                sv = a.rstd[row];
+            } else {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                x_[c].zero();
-                dy_[c].zero();
+                for (int c = 0; c < CPL; ++c) {
+                    b.x[c].zero();
+                    b.dy[c].zero();
+                }
             }
-            mu_ = s_ = 0.0f;
+            b.mu = mu;
+            b.s = sv;
+            return;
         }
+        const bool in = row < N;
+        const int64_t r = in ? row : 0;
+        const uint32_t nb = in ? (uint32_t)H * (uint32_t)sizeof(T) : 0u;
+        load_raw_row<RN_LOAD_AUX>(make_rsrc(xb + r * a.ldx, nb), L, b.x);
+        load_raw_row<RN_LOAD_AUX>(make_rsrc(dyb + r * a.lddy, nb), L, b.dy);
+        if constexpr (ADD)
+            load_raw_row<RN_LOAD_AUX>(
+                make_rsrc(has_add ? addb + r * a.ldadd : xb, has_add ? nb : 0u), L, b.ad);
+        b.mu = LN ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  make_rsrc(a.mean + r, in ? 4u : 0u), 0, 0, 0))
+                  : 0.0f;
+        b.s = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.rstd + r, in ? 4u : 0u), 0, 0, 0));
     };
-    if constexpr (PF) fetch((int64_t)blockIdx.x * RT + team, cx, cdy, cad, cmu, cs);
 
     int parity = 0;
-    for (int64_t grp = blockIdx.x; grp * RT < N; grp += gridDim.x) {
-        const int64_t row = grp * RT + team;
-        const bool active = row < N;
-        if constexpr (TW == 1) {
-            if (!active) break;
-        }
-        if constexpr (PF) fetch(row + step, nx, ndy, nad, nmu, ns);
-        else fetch(row, cx, cdy, cad, cmu, cs);
-
-        // Masked elements have dy = 0, so they add nothing below.
+    // One row of the team: dx, and its terms added to the accumulators.
+    // Rows past N hold zeros: they add nothing and store nothing.
+    auto process = [&](Buf &b, const int64_t row, const bool active) {
+        const float cmu = b.mu, cs = b.s;
         float sg = 0.0f, sgx = 0.0f;
         float kx[KEEP ? E : 1], kg[KEEP ? E : 1];
 #pragma unroll
@@ -503,8 +547,8 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
                 const int e = c * VEC + k;
-                const float dyv = cdy[c].get(k);
-                const float xhat = (cx[c].get(k) - cmu) * cs;
+                const float dyv = b.dy[c].get(k);
+                const float xhat = (b.x[c].get(k) - cmu) * cs;
                 const float gv = dyv * (KEEP ? gf[e] : g[c].get(k));
                 if constexpr (KEEP) {
                     kx[e] = xhat;
@@ -537,43 +581,103 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
         }
         const float c1 = LN ? sg * a.inv_H : 0.0f;
         const float c2 = sgx * a.inv_H;
-        if (active) {
-            if constexpr (!KEEP) {
+        if constexpr (!KEEP) {
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    opaque(cx[c].v);
-                    opaque(cdy[c].v);
+            for (int c = 0; c < CPL; ++c) {
+                opaque(b.x[c].v);
+                opaque(b.dy[c].v);
+            }
+        }
+        float dx[E];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const int e = c * VEC + k;
+                const float xhat = KEEP ? kx[e] : (b.x[c].get(k) - cmu) * cs;
+                float t = KEEP ? kg[e] : b.dy[c].get(k) * g[c].get(k);
+                if constexpr (LN) t -= c1;
+                dx[e] = __builtin_fmaf(-xhat, c2, t) * cs;
+                if constexpr (ADD) {
+                    if (has_add) dx[e] += b.ad[c].get(k);
                 }
             }
-            float dx[E];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const int e = c * VEC + k;
-                    const float xhat = KEEP ? kx[e] : (cx[c].get(k) - cmu) * cs;
-                    float t = KEEP ? kg[e] : cdy[c].get(k) * g[c].get(k);
-                    if constexpr (LN) t -= c1;
-                    dx[c * VEC + k] = __builtin_fmaf(-xhat, c2, t) * cs;
-                    if constexpr (ADD) {
-                        if (has_add) dx[c * VEC + k] += cad[c].get(k);
-                    }
-                }
+        if constexpr (RING) {
+            const int64_t r = active ? row : 0;
+            const uint32_t ob = active ? (uint32_t)H * (uint32_t)sizeof(T) : 0u;
+            store_row<T>(make_rsrc((T *)a.dx + r * a.lddx, ob), L, dx);
+            if constexpr (ADD) {
+                const bool two = a.dx2 != nullptr;
+                store_row<T>(
+                    make_rsrc(two ? (T *)a.dx2 + r * a.lddx2 : (T *)a.dx, two ? ob : 0u), L, dx);
+            }
+        } else if (active) {
             store_row<T>(row_rsrc((T *)a.dx + row * a.lddx, H), L, dx);
             if constexpr (ADD) {
                 if (a.dx2 != nullptr)
                     store_row<T>(row_rsrc((T *)a.dx2 + row * a.lddx2, H), L, dx);
             }
         }
-        if constexpr (PF) {
+    };
+
+    int64_t grp = blockIdx.x;
+    if constexpr (RING) {
+        // The workgroup's K row groups.
+        const int64_t ngrp = (N + RT - 1) / RT;
+        const int64_t K = ngrp > (int64_t)blockIdx.x
+                              ? (ngrp - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x
+                              : 0;
+        // Whole turns of the ring in a loop with no exit inside, then the
+        // remaining K mod NR groups.  Each prefetch is followed by a row's
+        // stores into an empty range (nothing is written), so the loop is
+        // entered with the same sequence of outstanding memory operations
+        // as it repeats with and the compiler's waits at its head need not
+        // drain the rows in flight.
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                cx[c] = nx[c];
-                cdy[c] = ndy[c];
-                if constexpr (ADD) cad[c] = nad[c];
+        for (int d = 0; d < PD; ++d) {
+            fetch(grp * RT + team + d * step, ring[d]);
+            float z[E] = {};
+            store_row<T>(make_rsrc(a.dx, 0u), L, z);
+            if constexpr (ADD) store_row<T>(make_rsrc(a.dx, 0u), L, z);
+        }
+        auto slot = [&](const int u) {
+            const int64_t row = grp * RT + team;
+            fetch(row + PD * step, ring[(u + PD) % NR]);
+            process(ring[u], row, row < N);
+            grp += gridDim.x;
+        };
+        for (int64_t k = K / NR; k > 0; --k) {
+#pragma unroll
+            for (int u = 0; u < NR; ++u) slot(u);
+        }
+        const int rem = (int)(K % NR);
+#pragma unroll
+        for (int u = 0; u + 1 < NR; ++u)
+            if (u < rem) slot(u);
+    } else {
+        // One buffer, or with PF two: the next row is requested before the
+        // current one is worked on and then copied into its place.
+        // Single-wave teams leave the loop at their first row past N.
+        if constexpr (PF) fetch(grp * RT + team, cur);
+        for (; grp * RT < N; grp += gridDim.x) {
+            const int64_t row = grp * RT + team;
+            const bool active = row < N;
+            if constexpr (TW == 1) {
+                if (!active) break;
             }
-            cmu = nmu;
-            cs = ns;
+            if constexpr (PF) fetch(row + step, nxt);
+            else fetch(row, cur);
+            process(cur, row, active);
+            if constexpr (PF) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    cur.x[c] = nxt.x[c];
+                    cur.dy[c] = nxt.dy[c];
+                    if constexpr (ADD) cur.ad[c] = nxt.ad[c];
+                }
+                cur.mu = nxt.mu;
+                cur.s = nxt.s;
+            }
         }
     }
 
