@@ -28,7 +28,8 @@ def kernel_source_digest() -> str:
     for the kernels they were taken on."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
-        h.update(open(p, "rb").read())
+        if os.path.isfile(p) and p.endswith((".h", ".hip")):
+            h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
