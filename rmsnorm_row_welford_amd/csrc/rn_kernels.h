@@ -749,20 +749,26 @@ __global__ __launch_bounds__(256) void bwd2_cols_kernel(const float *part, int P
     const int col0 = (blockIdx.x * 4 + wave_id_uniform()) * CPW;
     const float *base = part + (int64_t)blockIdx.y * Pp * H;
     T *dst = blockIdx.y == 0 ? dgamma : dbeta;
+    // all CPW columns' loads are issued before any is summed
+    float s[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int col = col0 + i;
-        if (col >= H) break;   // wave-uniform
-        const float *src = base + (int64_t)col * Pp;
-        float s = 0.0f;
-        for (int q = lane * 4; q < Pp; q += 256) {
-            const f32x4 v = *(const f32x4 *)(src + q);
+    for (int i = 0; i < CPW; ++i) s[i] = 0.0f;
+    for (int q = lane * 4; q < Pp; q += 256) {
+        f32x4 v[CPW];
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            v[i] = col0 + i < H ? *(const f32x4 *)(base + (int64_t)(col0 + i) * Pp + q)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                if (slot_used(q + k, P)) s += v[k];
-        }
-        s = wave_sum(s);
-        if (lane == 0) store_one(dst + col, s);
+                if (slot_used(q + k, P)) s[i] += v[i][k];
+    }
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const float t = wave_sum(s[i]);
+        if (lane == 0 && col0 + i < H) store_one(dst + col0 + i, t);
     }
 }
 
@@ -808,13 +814,18 @@ __global__ __launch_bounds__(1024) void bwd2_rows_kernel(const float *part, int 
         store_one(blockIdx.y == 0 ? dgamma + gcol : dbeta + gcol, t);
 }
 
+// Columns per wavefront of kernel 2 on column-major partial rows.
+#ifndef RN_BWD2_CPW
+#define RN_BWD2_CPW 1
+#endif
 template <class T>
 hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void *db,
                        hipStream_t s) {
     const unsigned np = ln ? 2 : 1;
     if (partial_colmajor(H))
-        hipLaunchKernelGGL((bwd2_cols_kernel<T, 1>), dim3((H + 3) / 4, np), dim3(256), 0,
-                           s, part, P, H, (T *)dg, (T *)db);
+        hipLaunchKernelGGL((bwd2_cols_kernel<T, RN_BWD2_CPW>),
+                           dim3((H + 4 * RN_BWD2_CPW - 1) / (4 * RN_BWD2_CPW), np), dim3(256),
+                           0, s, part, P, H, (T *)dg, (T *)db);
     else
         hipLaunchKernelGGL((bwd2_rows_kernel<T, 64>), dim3((H + 63) / 64, np), dim3(1024),
                            0, s, part, P, H, (T *)dg, (T *)db);

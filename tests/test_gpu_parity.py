@@ -458,8 +458,9 @@ def test_bitwise_deterministic(N, H):
 
 
 # Tall shapes on the one-workgroup-per-CU team plans (H 1024/2048/4096:
-# 8/4/2 rows per team step; N ragged).
-@pytest.mark.parametrize("N,H", [(32771, 1024), (12293, 2048), (6151, 4096)])
+# 8/4/2 rows per team step; N ragged), and wide rows.
+@pytest.mark.parametrize("N,H", [(32771, 1024), (12293, 2048), (6151, 4096),
+                                 (1000, 16384)])
 def test_workspace_contents_on_entry(orc, N, H):
     """Whatever the workspace holds on entry (zeros, all-ones bytes, 0xFE
     bytes, random bytes, what this call or a call of another shape left),
@@ -467,7 +468,8 @@ def test_workspace_contents_on_entry(orc, N, H):
     arr = synth.custom(31 + H, N, H, "bf16")
     x, dy, g, dh = (to_dev(arr[k]) for k in ("x", "dy", "gamma", "dh"))
     bf = torch.bfloat16
-    ws = torch.empty(rn.workspace_bytes(N, H, bf, True), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(rn.workspace_bytes(N, H, bf, True),
+                         rn.workspace_bytes(N, H, bf, False)), dtype=torch.uint8, device=DEV)
     _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
     _, rs2 = rn.rms_fwd(x, g, 1e-5)
 
@@ -508,6 +510,37 @@ def test_workspace_contents_on_entry(orc, N, H):
     rn.rms_bwd(dy[:n2], x[:n2], g, rs2[:n2], 1e-5, workspace=ws)
     for a, b in zip(want, run()):
         assert torch.equal(a, b), "a call of another shape changed the result"
+
+
+# Wide rows at ragged row counts: row lengths that leave the last 2048-column
+# blocks empty (9000, 12288), fp16, and fp32 parameters.
+WIDE = [(1001, 16384, "bf16"), (37, 9000, "bf16"), (300, 12288, "f16"),
+        (513, 16384, "bf16/f32")]
+
+
+@pytest.mark.parametrize("N,H,storage", WIDE)
+def test_wide_rows(orc, N, H, storage):
+    """LN, RMS and fused backward against the oracle, and bit for bit the
+    same run to run."""
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(60 + N, N, H, dtype, wdtype=wdt or None)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
+    check_fused_bwd(orc, arr, dtype, 1e-5)
+    x, dy, g, dh = (to_dev(arr[k], dtype) for k in ("x", "dy", "gamma", "dh"))
+
+    def run():
+        _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+        _, rs2 = rn.rms_fwd(x, g, 1e-5)
+        dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5)
+        dx2, dg2 = rn.rms_bwd(dy, x, g, rs2, 1e-5)
+        dx3, dr3, dg3 = rn.fused_add_rms_bwd(dy, x, g, rs2, 1e-5, dh_in=dh,
+                                             write_dres=True)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (dx, dg, db, dx2, dg2, dx3, dr3, dg3)]
+
+    for a_, b_ in zip(run(), run()):
+        assert torch.equal(a_, b_), "not reproducible run to run"
 
 
 @pytest.mark.parametrize("N", [0, 1, 2, 7, 255, 513])
@@ -562,14 +595,15 @@ def test_add_helper(orc, dtype, n, off):
     assert np.array_equal(host(a), want)
 
 
-@pytest.mark.parametrize("N,H", [(64, 4096), (1, 8192), (333, 128), (16389, 1024)])
+@pytest.mark.parametrize("N,H", [(64, 4096), (1, 8192), (333, 128), (16389, 1024),
+                                 (300, 16384)])
 def test_graph_capture_replays(N, H):
     """The entry points enqueue only kernels on the caller's stream, so a HIP
     graph can capture them: fused forward + fused backward + LayerNorm
     forward/backward captured once and replayed four times, with eager work
     and synchronizations between replays; every replay must reproduce the
     eager results bit for bit; (16389, 1024) is a tall ragged shape on a
-    persistent team plan."""
+    persistent team plan, (300, 16384) a wide one."""
     arr = synth.custom(19, N, H, "bf16")
     x, r, g, b, dy, dh = (to_dev(arr[k]) for k in ("x", "residual", "gamma", "beta",
                                                    "dy", "dh"))
@@ -577,8 +611,10 @@ def test_graph_capture_replays(N, H):
     y, hh, dx, dx2, y2 = (torch.empty((N, H), dtype=bf, device=DEV) for _ in range(5))
     rstd, mean, rstd2 = (torch.empty(N, dtype=torch.float32, device=DEV) for _ in range(3))
     dg, dg2, db2 = (torch.empty(H, dtype=bf, device=DEV) for _ in range(3))
-    ws = torch.empty(max(1, rn.workspace_bytes(N, H, bf, True)), dtype=torch.uint8,
-                     device=DEV)
+    # one workspace for both backward ops (LayerNorm may need none where
+    # RMSNorm needs partial rows)
+    ws = torch.empty(max(1, rn.workspace_bytes(N, H, bf, True),
+                         rn.workspace_bytes(N, H, bf, False)), dtype=torch.uint8, device=DEV)
 
     def step():
         rn.fused_add_rms_fwd(x, r, g, 1e-6, y=y, h=hh, rstd=rstd)
