@@ -127,6 +127,12 @@ __device__ __forceinline__ void store_row(rsrc_t r, const Layout<VEC, CPL, TW> &
 #ifndef RN_FWD_PF_DEPTH
 #define RN_FWD_PF_DEPTH 3
 #endif
+// Prefetching teams walk their ring with every load and store issued (rows
+// past N into empty ranges), so that the compiler's waits at the loop head
+// count exactly the operations issued after each one (see fwd_kernel).
+#ifndef RN_FWD_RING
+#define RN_FWD_RING 1
+#endif
 
 template <class T, class W, int VEC, int CPL, int TW, int RT, int OP, bool PF>
 constexpr int fwd_min_waves() {
@@ -199,8 +205,22 @@ void fwd_kernel(const FwdArgs a) {
     constexpr int PD = !PF ? 0 : sizeof(T) == 2 ? RN_FWD_PF_DEPTH : 1;
     constexpr int NR = PD + 1;
     Raw ring[NR][NIN][CPL];
+    // URING: the ring's loads and stores are all issued, with no branch
+    // around them; a row past N is read from and written to an empty range
+    // (loads return 0, stores are dropped).  Branches around memory
+    // operations make the compiler's wait-count analysis merge paths with
+    // different outstanding operations, and at the loop head it then waits
+    // for every load and store in flight, the prefetched rows included.
+    constexpr bool URING = RN_FWD_RING && PD > 0;
     auto fetch = [&](int64_t row, auto &dst) {
-        if (row < N) {
+        if constexpr (URING) {
+            const bool in = row < N;
+            const int64_t r = in ? row : 0;
+            const uint32_t nb = in ? (uint32_t)H * (uint32_t)sizeof(T) : 0u;
+            load_raw_row<RN_LOAD_AUX>(make_rsrc(xb + r * a.ldx, nb), L, dst[0]);
+            if constexpr (OP == OP_FUSED)
+                load_raw_row<RN_LOAD_AUX>(make_rsrc(rb + r * a.ldr, nb), L, dst[1]);
+        } else if (row < N) {
             load_raw_row<RN_LOAD_AUX>(row_rsrc(xb + row * a.ldx, H), L, dst[0]);
             if constexpr (OP == OP_FUSED)
                 load_raw_row<RN_LOAD_AUX>(row_rsrc(rb + row * a.ldr, H), L, dst[1]);
@@ -211,12 +231,12 @@ void fwd_kernel(const FwdArgs a) {
                 for (int c = 0; c < CPL; ++c) dst[i][c].zero();
         }
     };
-#pragma unroll
-    for (int d = 0; d < PD; ++d) fetch((int64_t)blockIdx.x * RT + team + d * step, ring[d]);
-
     int parity = 0;
     // One row of the team: statistics, y (and h), saved statistics.
     auto process = [&](auto &cur, const int64_t row, const bool active) {
+        // URING: an inactive row's stores go to empty ranges
+        const uint32_t ob = active ? (uint32_t)H * (uint32_t)sizeof(T) : 0u;
+        const int64_t rr = active ? row : 0;
         float v[E];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
@@ -227,8 +247,10 @@ void fwd_kernel(const FwdArgs a) {
             }
         // h is written back in the same pass, before y; every element of
         // this lane was loaded before, so h may alias x or the residual.
-        if constexpr (OP == OP_FUSED)
-            if (active) store_row<T>(row_rsrc((T *)a.h + row * a.ldh, H), L, v);
+        if constexpr (OP == OP_FUSED) {
+            if constexpr (URING) store_row<T>(make_rsrc((T *)a.h + rr * a.ldh, ob), L, v);
+            else if (active) store_row<T>(row_rsrc((T *)a.h + row * a.ldh, H), L, v);
+        }
 
         float mean = 0.0f, var;
         if constexpr (OP == OP_LN) {
@@ -323,7 +345,7 @@ void fwd_kernel(const FwdArgs a) {
         }
         const float rstd = rsqrt_pos(var + a.eps);
 
-        if (active) {
+        if (URING || active) {
             float out[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -333,12 +355,28 @@ void fwd_kernel(const FwdArgs a) {
                 else
                     out[e] = (v[e] * rstd) * ge;
             }
-            store_row<T>(row_rsrc((T *)a.y + row * a.ldy, H), L, out);
-            if (wit == 0 && lane == 0) {
-                if constexpr (OP == OP_LN) {
-                    if (a.mean) a.mean[row] = mean;
+            if constexpr (URING) {
+                store_row<T>(make_rsrc((T *)a.y + rr * a.ldy, ob), L, out);
+                // the row's statistics: lane 0 of wave 0 stores them, every
+                // other lane falls past a 4-byte range (no branch)
+                const int so = (wit == 0 && lane == 0) ? 0 : 4;
+                if constexpr (OP == OP_LN)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(mean),
+                        make_rsrc(a.mean ? a.mean + rr : a.rstd, (active && a.mean) ? 4u : 0u),
+                        so, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(rstd),
+                    make_rsrc(a.rstd ? a.rstd + rr : a.mean, (active && a.rstd) ? 4u : 0u), so,
+                    0, 0);
+            } else {
+                store_row<T>(row_rsrc((T *)a.y + row * a.ldy, H), L, out);
+                if (wit == 0 && lane == 0) {
+                    if constexpr (OP == OP_LN) {
+                        if (a.mean) a.mean[row] = mean;
+                    }
+                    if (a.rstd) a.rstd[row] = rstd;
                 }
-                if (a.rstd) a.rstd[row] = rstd;
             }
         }
     };
@@ -347,23 +385,61 @@ void fwd_kernel(const FwdArgs a) {
     // in buffer u is worked on while buffer (u + PD) % NR receives the row
     // PD steps ahead.
     int64_t grp = blockIdx.x;
-    bool done = grp * RT >= N;
-    while (!done) {
+    if constexpr (URING) {
+        // The workgroup's K row groups: whole turns of the ring in a loop
+        // with no exit inside, then the remaining K mod NR groups.  Each
+        // prefetch before the loop is followed by a row's stores into an
+        // empty range (nothing is written), so the loop is entered with the
+        // same sequence of outstanding memory operations as it repeats with.
+        const int64_t ngrp = (N + RT - 1) / RT;
+        const int64_t K = ngrp > (int64_t)blockIdx.x
+                              ? (ngrp - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x
+                              : 0;
 #pragma unroll
-        for (int u = 0; u < NR; ++u) {
-            if (!done) {
-                const int64_t row = grp * RT + team;
-                const bool active = row < N;
-                if (TW == 1 && !active) {
-                    done = true;   // wave-uniform; single-wave teams use no barrier
-                } else {
-                    if constexpr (PD > 0)
-                        fetch(row + PD * step, ring[(u + PD) % NR]);
-                    else
-                        fetch(row, ring[u]);
-                    process(ring[u], row, active);
-                    grp += gridDim.x;
-                    done = grp * RT >= N;
+        for (int d = 0; d < PD; ++d) {
+            fetch(grp * RT + team + d * step, ring[d]);
+            float z[E] = {};
+            const rsrc_t none = make_rsrc(a.y, 0u);
+            if constexpr (OP == OP_FUSED) store_row<T>(none, L, z);
+            store_row<T>(none, L, z);
+            if constexpr (OP == OP_LN) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+        }
+        auto slot = [&](const int u) {
+            const int64_t row = grp * RT + team;
+            fetch(row + PD * step, ring[(u + PD) % NR]);
+            process(ring[u], row, row < N);
+            grp += gridDim.x;
+        };
+        for (int64_t k = K / NR; k > 0; --k) {
+#pragma unroll
+            for (int u = 0; u < NR; ++u) slot(u);
+        }
+        const int rem = (int)(K % NR);
+#pragma unroll
+        for (int u = 0; u + 1 < NR; ++u)
+            if (u < rem) slot(u);
+    } else {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) fetch(grp * RT + team + d * step, ring[d]);
+        bool done = grp * RT >= N;
+        while (!done) {
+#pragma unroll
+            for (int u = 0; u < NR; ++u) {
+                if (!done) {
+                    const int64_t row = grp * RT + team;
+                    const bool active = row < N;
+                    if (TW == 1 && !active) {
+                        done = true;   // wave-uniform; single-wave teams use no barrier
+                    } else {
+                        if constexpr (PD > 0)
+                            fetch(row + PD * step, ring[(u + PD) % NR]);
+                        else
+                            fetch(row, ring[u]);
+                        process(ring[u], row, active);
+                        grp += gridDim.x;
+                        done = grp * RT >= N;
+                    }
                 }
             }
         }
