@@ -488,6 +488,10 @@ __device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
 #ifndef RN_BWD_RING
 #define RN_BWD_RING 1
 #endif
+// Largest one-per-CU workgroup (in waves) whose teams keep float32 copies.
+#ifndef RN_BWD_KEEP_MAXW
+#define RN_BWD_KEEP_MAXW 8
+#endif
 
 // ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
 // kernel only writes dx (the column-sum strategy computes the parameter
@@ -516,7 +520,7 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     const int H = a.H;
     const Lay L(wit * 64 + lane, H);
 
-    static_assert(!KEEP || TW * RT <= 8, "KEEP needs 256 registers per wave");
+    static_assert(!KEEP || TW * RT <= RN_BWD_KEEP_MAXW, "KEEP needs the registers of few waves");
     RawChunk<W, VEC> g[CPL];
     load_raw_row<0>(row_rsrc((const W *)a.gamma, H), L, g);
     float gf[KEEP ? E : 1];
@@ -981,7 +985,7 @@ struct Plan {
     static constexpr int VEC = VEC_, CPL = CPL_, TW = TW_, RT = RT_;
     static constexpr int PER_CU = PER_CU_;
     // one workgroup of at most 8 waves per CU: room to keep float copies
-    static constexpr bool KEEP = PER_CU_ == 1 && TW_ * RT_ <= 8;
+    static constexpr bool KEEP = PER_CU_ == 1 && TW_ * RT_ <= RN_BWD_KEEP_MAXW;
     static constexpr bool PF = PF_;   // prefetch the next row into registers
     static constexpr int SPAN = 64 * TW_ * VEC_ * CPL_;
     static constexpr int THREADS = 64 * TW_ * RT_;

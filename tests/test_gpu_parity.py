@@ -669,3 +669,35 @@ def test_workspace_errors():
     # the workspace does not grow with N past the partial-row cap
     assert rn.workspace_bytes(10 ** 6, H, torch.bfloat16, True) == \
         rn.workspace_bytes(10 ** 7, H, torch.bfloat16, True)
+
+
+# Forward with some or all saved statistics omitted (null mean / rstd): y
+# and h do not depend on which statistics are stored, and a statistic that
+# is stored is the same either way.  The shapes cover every forward plan
+# family: several rows per wave, a row per wave, 4- and 8-wave teams, and
+# the persistent 16-wave plan with partial ring turns (N below, between and
+# above multiples of the grid).
+STATLESS = [(1000, 128), (257, 1024), (129, 2048), (70, 4096), (33, 8192),
+            (7, 16384), (300, 16384), (1029, 16384)]
+
+
+@pytest.mark.parametrize("N,H", STATLESS)
+def test_forward_without_stats(N, H):
+    arr = synth.custom(90 + N, N, H, "bf16")
+    x, g, b, r = (to_dev(arr[k]) for k in ("x", "gamma", "beta", "residual"))
+    y1, m1, s1 = rn.ln_fwd(x, g, b, 1e-5)
+    y0, m0, s0 = rn.ln_fwd(x, g, b, 1e-5, save_stats=False)
+    assert m0 is None and s0 is None
+    assert torch.equal(y0, y1)
+    ym, mm, sm = rn.ln_fwd(x, g, b, 1e-5, mean=torch.empty_like(m1), save_stats=False)
+    assert sm is None and torch.equal(ym, y1) and torch.equal(mm, m1)
+    ys, ms, ss = rn.ln_fwd(x, g, b, 1e-5, rstd=torch.empty_like(s1), save_stats=False)
+    assert ms is None and torch.equal(ys, y1) and torch.equal(ss, s1)
+
+    y1, s1 = rn.rms_fwd(x, g, 1e-5)
+    y0, s0 = rn.rms_fwd(x, g, 1e-5, save_stats=False)
+    assert s0 is None and torch.equal(y0, y1)
+
+    y1, h1, s1 = rn.fused_add_rms_fwd(x, r, g, 1e-5)
+    y0, h0, s0 = rn.fused_add_rms_fwd(x, r, g, 1e-5, save_stats=False)
+    assert s0 is None and torch.equal(y0, y1) and torch.equal(h0, h1)
