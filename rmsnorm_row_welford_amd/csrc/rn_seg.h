@@ -284,13 +284,18 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
         sgx = seg_sum<SEG>(sgx);
         const float c1 = LN ? sg * a.inv_H : 0.0f;
         const float c2 = sgx * a.inv_H;
+        const float k2 = -c2 * s, k1 = -c1 * s;   // as in bwd1_kernel
         float dx[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const float xhat = (cx.get(k) - mu) * s;
             float t = cdy.get(k) * g.get(k);
-            if constexpr (LN) t -= c1;
-            dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
+            if constexpr (LN && RN_BWD_FOLD) {
+                dx[k] = __builtin_fmaf(t, s, __builtin_fmaf(xhat, k2, k1));
+            } else {
+                if constexpr (LN) t -= c1;
+                dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
+            }
             if constexpr (ADD) dx[k] += cad.get(k);
         }
         bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.dx, row0, n, a.lddx, H),

@@ -325,14 +325,20 @@ def test_small_variance_rows(orc, dtype, H):
         check_ln_fwd(orc, arr3, dtype, 1e-5)
 
 
-@pytest.mark.parametrize("H", [1024, 128, 40, 24])
-@pytest.mark.parametrize("pad", [24, 3])
+# (H, pad): every plan family; the element-wise path (pad 3) ends at 8192
+STRIDED = [(H, pad) for H in (1024, 128, 40, 24, 4096) for pad in (24, 3)] + \
+          [(8192, 24), (16384, 24), (16384, 40)]
+
+
+@pytest.mark.parametrize("H,pad", STRIDED)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_strided_rows_and_canaries(orc, dtype, pad, H):
-    """Row strides > H (pad 24 keeps 16-byte rows, pad 3 forces the
+    """Row strides > H (pad 24 or 40 keeps 16-byte rows, pad 3 forces the
     element-wise path): the padding between rows and a guard row after the
     last row stay untouched, and results match the oracle.  Short rows run
-    several rows per wave, addressed through one range per row group."""
+    several rows per wave, addressed through one range per row group; 16384
+    runs the persistent plan, whose ring reads rows past N from empty
+    ranges."""
     N = 33
     arr = synth.custom(11, N, H, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
