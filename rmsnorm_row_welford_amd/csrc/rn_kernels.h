@@ -194,10 +194,9 @@ void fwd_kernel(const FwdArgs a) {
     const int64_t N = a.N;
     const int64_t step = (int64_t)gridDim.x * RT;
 
-    // Software pipeline (PF): the raw chunks of the team's NEXT row (and, for
-    // multi-wave LayerNorm, its pivot element) are requested before the
-    // current row is reduced and written, so HBM reads stay in flight
-    // across the reductions.  Without PF each row is fetched when its turn
+    // Software pipeline (PF): the raw chunks of the team's next rows are
+    // requested before the current row is reduced and written, so HBM reads
+    // stay in flight across the reductions.  Without PF each row is fetched when its turn
     // comes and latency is hidden by occupancy alone.
     // PD rows are requested ahead: a ring of PD + 1 row buffers, which the
     // loop below walks unrolled so that each buffer keeps its registers (no
