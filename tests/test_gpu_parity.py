@@ -526,10 +526,23 @@ WIDE = [(1001, 16384, "bf16"), (37, 9000, "bf16"), (300, 12288, "f16"),
 
 @pytest.mark.parametrize("N,H,storage", WIDE)
 def test_wide_rows(orc, N, H, storage):
-    """LN, RMS and fused backward against the oracle, and bit for bit the
-    same run to run."""
+    """LN, RMS and fused forward and backward against the oracle, and bit for
+    bit the same run to run.  On the persistent 16384 plan, 1001 and 513
+    rows give each workgroup 2-4 rows: whole turns of its prefetch ring and
+    every remainder."""
     dtype, _, wdt = storage.partition("/")
     arr = synth.custom(60 + N, N, H, dtype, wdtype=wdt or None)
+    check_ln_fwd(orc, arr, dtype, 1e-5)
+    check_rms_fwd(orc, arr, dtype, 1e-5)
+    xf, rf, gf = (to_dev(arr[k], dtype) for k in ("x", "residual", "gamma"))
+    yf, hf, rsf = rn.fused_add_rms_fwd(xf, rf, gf, 1e-5)
+    torch.cuda.synchronize()
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(
+        orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype),
+        dec(orc, arr, "gamma", dtype), oracle.eps_at_boundary(1e-5))
+    assert np.array_equal(host(hf), orc.encode(h_o, dtype)), "h not RNE(x + r)"
+    tol.check_out(host(yf), y_o, dtype, orc, "fused y")
+    tol.check_rstd(host(rsf), r_o, "fused rstd")
     check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
     check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
     check_fused_bwd(orc, arr, dtype, 1e-5)
