@@ -521,15 +521,15 @@ def test_workspace_contents_on_entry(orc, N, H):
 # Wide rows at ragged row counts: row lengths that leave the last 2048-column
 # blocks empty (9000, 12288), fp16, and fp32 parameters.
 WIDE = [(1001, 16384, "bf16"), (37, 9000, "bf16"), (300, 12288, "f16"),
-        (513, 16384, "bf16/f32")]
+        (513, 16384, "bf16/f32"), (600, 16384, "f32")]
 
 
 @pytest.mark.parametrize("N,H,storage", WIDE)
 def test_wide_rows(orc, N, H, storage):
     """LN, RMS and fused forward and backward against the oracle, and bit for
-    bit the same run to run.  On the persistent 16384 plan, 1001 and 513
-    rows give each workgroup 2-4 rows: whole turns of its prefetch ring and
-    every remainder."""
+    bit the same run to run.  On the persistent 16384 plan, 1001, 600 and
+    513 rows give each workgroup 2-4 rows: whole turns of its prefetch ring
+    (four buffers for 2-byte rows, two for float32) and every remainder."""
     dtype, _, wdt = storage.partition("/")
     arr = synth.custom(60 + N, N, H, dtype, wdtype=wdt or None)
     check_ln_fwd(orc, arr, dtype, 1e-5)
