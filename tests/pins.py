@@ -12,8 +12,9 @@ What each check leans on (never the oracle's own formula retyped):
   (tests/golden/closed_forms.txt), central finite differences of
   L = sum(dy * y), exact backward invariants, torch's binary64 CPU
   layer_norm / rms_norm and autograd (an independent library routine),
-  and for the codec: exact rational rounding against the enumerated set of
-  all bfloat16 values, plus torch's own float32 -> bfloat16 cast.
+  and for the codecs: exact rational rounding against the enumerated set of
+  all bfloat16 / binary16 values (binary32: against the three binary32
+  neighbours of each input), plus torch's and numpy's own casts.
 """
 import math
 import os
@@ -599,6 +600,68 @@ def check_f16_encode_vs_torch(orc):
     assert bad.size == 0, f"{bad.size} mismatches, e.g. {f[bad[:3]]}"
 
 
+def _exact_round_f32(v: float):
+    """Reference RNE to binary32 by exact rational comparison: the answer is
+    one of the binary32 neighbours of a nearby candidate (three consecutive
+    binary32 values around it), chosen by exact distance, ties to the even
+    significand; at or beyond FLT_MAX + half an ulp (2^103) it overflows."""
+    fmax = float(np.finfo(np.float32).max)
+    if v == 0.0:
+        return np.float32(v)
+    if Fraction(abs(v)) >= Fraction(fmax) + Fraction(2) ** 103:
+        return np.float32(np.inf if v > 0 else -np.inf)
+    with np.errstate(over="ignore"):
+        c = np.float32(min(max(v, -fmax), fmax))
+    with np.errstate(over="ignore"):
+        cands = {np.nextafter(c, np.float32(-np.inf)), c,
+                 np.nextafter(c, np.float32(np.inf))}
+    cands = [k for k in cands if np.isfinite(k)]
+    fv = Fraction(v)
+    best = None
+    for k in cands:
+        key = (abs(Fraction(float(k)) - fv), int(np.array(k).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, k)
+    r = best[1]
+    if r == 0:   # rounded to zero: the sign follows the input
+        return np.float32(-0.0) if v < 0 else np.float32(0.0)
+    return r
+
+
+def check_f32_encode(orc):
+    """binary64 -> binary32 (the expected value of every float32 output and of
+    the bit-exact float32 h): exact rational rounding to the nearest binary32
+    value, ties to even, on random values over the whole exponent range,
+    exact midpoints between neighbours (and one binary64 step either side),
+    subnormals and the subnormal/normal boundary, overflow, signed zeros;
+    then numpy's float64 -> float32 cast on a million random values."""
+    rng = _rng(29)
+    tests = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-46, 39, 2000))
+    u = rng.integers(1, 0x7F7FFFFF, 600, dtype=np.uint64).astype(np.uint32)
+    for f in u.view(np.float32):
+        nb = np.nextafter(f, np.float32(np.inf))
+        mid = (float(f) + float(nb)) / 2.0        # exact in binary64
+        tests += [mid, -mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)]
+    tiny = 2.0 ** -149
+    fmax = float(np.finfo(np.float32).max)
+    tests += [0.0, -0.0, tiny, tiny / 2, tiny * 0.75, tiny * 1.5, -tiny * 2.5,
+              tiny * 3.5, 2.0 ** -126, 2.0 ** -126 * (1 - 2 ** -24),
+              2.0 ** -126 - tiny / 2, fmax, -fmax, fmax + 2.0 ** 103,
+              np.nextafter(fmax + 2.0 ** 103, 0), 1e39, -1e39, 1.0 + 2 ** -24,
+              1.0 + 3 * 2 ** -24, 1.0 - 2 ** -25, 1.0 + 2 ** -52]
+    tests = np.array(tests, dtype=np.float64)
+    got = orc.f32_encode(tests)
+    for v, g in zip(tests, got):
+        want = _exact_round_f32(float(v))
+        same = (np.array(g).view(np.uint32) == np.array(want).view(np.uint32))
+        assert same, f"f32({v!r}) = {g!r}, want {want!r}"
+    w = rng.standard_normal(1 << 20) * 10.0 ** rng.integers(-45, 38, 1 << 20)
+    with np.errstate(over="ignore"):
+        want = w.astype(np.float32)
+    bad = np.nonzero(orc.f32_encode(w).view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, f"{bad.size} mismatches vs numpy, e.g. {w[bad[:3]]}"
+
+
 ALL_CHECKS = [
     check_ln_moments, check_ln_scale_law, check_ln_affine, check_rms_moments,
     check_rms_scale_law, check_rms_equals_ln_zero_mean, check_fused,
@@ -607,4 +670,5 @@ ALL_CHECKS = [
     check_bwd_invariants,
     check_bwd_against_torch, check_special_cases, check_bf16_codec,
     check_bf16_encode_vs_torch, check_f16_codec, check_f16_encode_vs_torch,
+    check_f32_encode,
 ]

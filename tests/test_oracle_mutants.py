@@ -66,6 +66,11 @@ MUTANTS = [
     ("f16_no_overflow_to_inf", "if (rv > 65504.0)", "if (rv > 1e300)"),
     ("f16_decode_subnormal_scale", "v = ldexp((double)fr, -24);",
      "v = ldexp((double)fr, -25);"),
+    ("f32_truncates", "out[i] = (float)in[i];",
+     "{ out[i] = (float)in[i]; if (fabs((double)out[i]) > fabs(in[i])) "
+     "out[i] = nextafterf(out[i], 0.0f); }"),
+    ("f32_flushes_subnormals", "out[i] = (float)in[i];",
+     "out[i] = fabs(in[i]) < 0x1p-126 ? 0.0f : (float)in[i];"),
 ]
 
 
