@@ -37,3 +37,24 @@ def pytest_collection_modifyitems(config, items):
 def orc():
     import oracle
     return oracle.default()
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Print what every parity check recorded (elements, largest ulp
+    distance, elements that passed only through the cancellation floor,
+    largest relative error); with RN_PARITY_STATS=<path> also write it as
+    JSON."""
+    try:
+        import tolerance
+    except Exception:
+        return
+    if not tolerance.STATS:
+        return
+    terminalreporter.section("parity statistics")
+    for line in tolerance.summary_lines():
+        terminalreporter.write_line(line)
+    path = os.environ.get("RN_PARITY_STATS")
+    if path:
+        import json
+        with open(path, "w") as f:
+            json.dump(tolerance.STATS, f, indent=1, sort_keys=True)
