@@ -1,9 +1,14 @@
 """HIP path vs the binary64 oracle, element by element, on the same seeded
 inputs (rmsnorm_row_welford_amd.synth), through the C ABI.
 
-Full-size workloads run on the GPU exactly as the benchmark launches them;
-the oracle then checks sampled rows (and, for the backward, dgamma/dbeta
-over all rows).  Smaller shapes are checked in full.  Bars: tests/tolerance.py.
+Every output element of every workload is compared, the full-size ones
+included: they run on the GPU exactly as the benchmark launches them, and
+the oracle computes every row.  Bars: tests/tolerance.py.  Each check is
+labelled with its workload; the session prints, per label, the largest ulp
+distance and how many elements passed only through the cancellation floor.
+On the workloads the pages name, RMSNorm and fused y must hold 1 ulp
+everywhere (no floor), and the floor may carry at most FLOOR_FRAC of the
+LayerNorm y and dx elements.
 """
 import numpy as np
 import pytest
@@ -42,10 +47,10 @@ def pdt(arr, dtype):
     return "f32" if arr["gamma"].dtype == np.float32 else dtype
 
 
-def sample_rows(N, k=96, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = {0, 1, N // 2, N - 1} | set(rng.choice(N, size=min(k, N), replace=False).tolist())
-    return np.array(sorted(r for r in rows if 0 <= r < N))
+# Share of LayerNorm y and dx elements that may pass only through the
+# cancellation floor on the named workloads: only |v| below about 2^-14 of
+# the row scale can need it, about 5e-5 of a normal sample.
+FLOOR_FRAC = 2e-4
 
 
 def dec(orc, arr, k, dtype):
@@ -53,49 +58,56 @@ def dec(orc, arr, k, dtype):
 
 
 # ----------------------------------------------------------------- helpers --
-def check_ln_fwd(orc, arr, dtype, eps, rows=None, use_beta=True):
+def _lab(tag, what):
+    return f"{tag}: {what}" if tag else f"edge: {what}"
+
+
+def check_ln_fwd(orc, arr, dtype, eps, use_beta=True, tag=None):
+    """tag: the workload's name for the statistics; a named workload also
+    bounds the share of floored y elements."""
     x = to_dev(arr["x"], dtype)
     g = to_dev(arr["gamma"], dtype)
     b = to_dev(arr["beta"], dtype) if (use_beta and "beta" in arr) else None
     y, mean, rstd = rn.ln_fwd(x, g, b, eps)
     torch.cuda.synchronize()
-    rows = np.arange(arr["x"].shape[0]) if rows is None else rows
-    xd = orc.decode(arr["x"][rows], dtype)
+    xd = orc.decode(arr["x"], dtype)
     e = oracle.eps_at_boundary(eps)
     bd = dec(orc, arr, "beta", dtype) if b is not None else None
     y_o, m_o, r_o = orc.ln_fwd(xd, dec(orc, arr, "gamma", dtype), bd, e)
+    del xd
     var_o = 1.0 / (r_o * r_o) - e
-    stats = tol.check_out(host(y)[rows], y_o, dtype, orc, "LN y")
-    tol.check_mean(host(mean)[rows], m_o, var_o, e, "LN mean")
-    tol.check_rstd(host(rstd)[rows], r_o, "LN rstd")
+    stats = tol.check_out(host(y), y_o, dtype, orc, _lab(tag, f"LN y {dtype}"),
+                          max_floored_frac=FLOOR_FRAC if tag else None)
+    tol.check_mean(host(mean), m_o, var_o, e, _lab(tag, "LN mean"))
+    tol.check_rstd(host(rstd), r_o, _lab(tag, "LN rstd"))
     return y, mean, rstd, stats
 
 
-def check_rms_fwd(orc, arr, dtype, eps, rows=None):
+def check_rms_fwd(orc, arr, dtype, eps, tag=None):
+    """RMSNorm y is a product (no cancellation): 1 ulp everywhere."""
     x = to_dev(arr["x"], dtype)
     g = to_dev(arr["gamma"], dtype)
     y, rstd = rn.rms_fwd(x, g, eps)
     torch.cuda.synchronize()
-    rows = np.arange(arr["x"].shape[0]) if rows is None else rows
-    xd = orc.decode(arr["x"][rows], dtype)
+    xd = orc.decode(arr["x"], dtype)
     y_o, r_o = orc.rms_fwd(xd, dec(orc, arr, "gamma", dtype),
                            oracle.eps_at_boundary(eps))
-    stats = tol.check_out(host(y)[rows], y_o, dtype, orc, "RMS y")
-    tol.check_rstd(host(rstd)[rows], r_o, "RMS rstd")
+    del xd
+    stats = tol.check_out(host(y), y_o, dtype, orc, _lab(tag, f"RMS y {dtype}"),
+                          strict=True)
+    tol.check_rstd(host(rstd), r_o, _lab(tag, "RMS rstd"))
     return y, rstd, stats
 
 
-def check_bwd(orc, arr, dtype, eps, layernorm, rows=None):
+def check_bwd(orc, arr, dtype, eps, layernorm, tag=None):
     """GPU forward (for the saved stats), GPU backward, oracle backward."""
     x = to_dev(arr["x"], dtype)
     dy = to_dev(arr["dy"], dtype)
     g = to_dev(arr["gamma"], dtype)
-    N = arr["x"].shape[0]
     e = oracle.eps_at_boundary(eps)
     xd = orc.decode(arr["x"], dtype)
     dyd = orc.decode(arr["dy"], dtype)
     gd = dec(orc, arr, "gamma", dtype)
-    rows = np.arange(N) if rows is None else rows
     if layernorm:
         _, mean, rstd = rn.ln_fwd(x, g, None, eps)
         dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, eps)
@@ -107,11 +119,15 @@ def check_bwd(orc, arr, dtype, eps, layernorm, rows=None):
         torch.cuda.synchronize()
         dx_o, dg_o, rstd_o = orc.rms_bwd(dyd, xd, gd, e)
     assert dg.dtype == TORCH_DT[pdt(arr, dtype)] and dx.dtype == TORCH_DT[dtype]
-    ts = tol.dx_term_scale(dyd[rows], gd, rstd_o[rows])
-    stats = tol.check_out(host(dx)[rows], dx_o[rows], dtype, orc, "dx", term_scale=ts)
-    rr = tol.check_param(orc.decode(host(dg), pdt(arr, dtype)), dg_o, "dgamma")
+    ts = tol.dx_term_scale(dyd, gd, rstd_o)
+    del xd, dyd
+    nm = "LN" if layernorm else "RMS"
+    stats = tol.check_out(host(dx), dx_o, dtype, orc, _lab(tag, f"{nm} dx {dtype}"),
+                          term_scale=ts, max_floored_frac=FLOOR_FRAC if tag else None)
+    rr = tol.check_param(orc.decode(host(dg), pdt(arr, dtype)), dg_o,
+                         _lab(tag, f"{nm} dgamma"))
     if layernorm:
-        tol.check_param(orc.decode(host(db), pdt(arr, dtype)), db_o, "dbeta")
+        tol.check_param(orc.decode(host(db), pdt(arr, dtype)), db_o, _lab(tag, "LN dbeta"))
     return stats, rr
 
 
@@ -128,8 +144,8 @@ def fused_bwd_oracle(orc, arr, dtype, eps, with_dh=True):
     return dx_o, dg_o, tol.dx_term_scale(dyd, gd, rs_o), h_o
 
 
-def check_fused_bwd(orc, arr, dtype, eps, rows=None, with_dh=True,
-                    write_dres=True, in_place=False):
+def check_fused_bwd(orc, arr, dtype, eps, with_dh=True, write_dres=True,
+                    in_place=False, tag=None):
     """GPU fused forward (h, rstd), GPU fused backward, oracle backward."""
     x, r, g, dy = (to_dev(arr[k], dtype) for k in ("x", "residual", "gamma", "dy"))
     _, h, rstd = rn.fused_add_rms_fwd(x, r, g, eps)
@@ -140,17 +156,17 @@ def check_fused_bwd(orc, arr, dtype, eps, rows=None, with_dh=True,
     torch.cuda.synchronize()
     if in_place:
         assert dx.data_ptr() == dh.data_ptr()
-    N = arr["x"].shape[0]
-    rows = np.arange(N) if rows is None else rows
     dx_o, dg_o, ts, h_o = fused_bwd_oracle(orc, arr, dtype, eps, with_dh)
     assert np.array_equal(host(h), orc.encode(h_o, dtype)), "h not RNE(x + r)"
-    stats = tol.check_out(host(dx)[rows], dx_o[rows], dtype, orc, "fused dx",
-                          term_scale=ts[rows])
+    del h_o
+    stats = tol.check_out(host(dx), dx_o, dtype, orc, _lab(tag, f"fused dx {dtype}"),
+                          term_scale=ts, max_floored_frac=FLOOR_FRAC if tag else None)
     if write_dres:
         assert torch.equal(dres, dx), "dres differs from dx"
     else:
         assert dres is None
-    rr = tol.check_param(orc.decode(host(dg), pdt(arr, dtype)), dg_o, "fused dgamma")
+    rr = tol.check_param(orc.decode(host(dg), pdt(arr, dtype)), dg_o,
+                         _lab(tag, "fused dgamma"))
     return stats, rr
 
 
@@ -158,8 +174,8 @@ def check_fused_bwd(orc, arr, dtype, eps, rows=None, with_dh=True,
 def test_ln_f32_64x1000_fwd_bwd(orc):
     w = synth.WORKLOADS["ln_f32_64x1000"]
     arr = synth.generate(w)
-    check_ln_fwd(orc, arr, "f32", w.eps)
-    check_bwd(orc, arr, "f32", w.eps, layernorm=True)
+    check_ln_fwd(orc, arr, "f32", w.eps, tag=w.name)
+    check_bwd(orc, arr, "f32", w.eps, layernorm=True, tag=w.name)
 
 
 @pytest.mark.parametrize("op", ["ln", "rms"])
@@ -167,7 +183,8 @@ def test_fwd_bf16_8192x1024(orc, op):
     w = synth.WORKLOADS["fwd_bf16_8192x1024"]
     arr = synth.generate(w)
     if op == "ln":
-        y, mean, rstd, _ = check_ln_fwd(orc, arr, "bf16", w.eps, use_beta=False)
+        y, mean, rstd, _ = check_ln_fwd(orc, arr, "bf16", w.eps, use_beta=False,
+                                        tag=w.name)
         # rows [N/2, N) are exactly 50.0 after rounding: zero variance,
         # y = beta = 0, mean = 50, rstd = 1/sqrt(eps) (in float32)
         lo = w.N // 2
@@ -176,7 +193,7 @@ def test_fwd_bf16_8192x1024(orc, op):
         want = np.float32(1.0) / np.sqrt(np.float32(w.eps))
         assert np.allclose(host(rstd)[lo:], want, rtol=1e-6)
     else:
-        check_rms_fwd(orc, arr, "bf16", w.eps)
+        check_rms_fwd(orc, arr, "bf16", w.eps, tag=w.name)
 
 
 def test_fused_bf16_32768x4096(orc):
@@ -190,33 +207,54 @@ def test_fused_bf16_32768x4096(orc):
     # h: every element, bit-exact
     h_exact = orc.decode(arr["x"], "bf16") + orc.decode(arr["residual"], "bf16")
     assert np.array_equal(host(h), orc.bf16_encode(h_exact)), "h not RNE(x + r)"
-    rows = sample_rows(w.N)
+    del h_exact
     y_o, h_o, r_o = orc.fused_add_rms_fwd(
-        orc.decode(arr["x"][rows], "bf16"), orc.decode(arr["residual"][rows], "bf16"),
+        orc.decode(arr["x"], "bf16"), orc.decode(arr["residual"], "bf16"),
         orc.decode(arr["gamma"], "bf16"), oracle.eps_at_boundary(w.eps))
-    tol.check_bf16(host(y)[rows], y_o, orc, "fused y")
-    tol.check_rstd(host(rstd)[rows], r_o, "fused rstd")
+    del h_o
+    tol.check_bf16(host(y), y_o, orc, _lab(w.name, "fused y bf16"), strict=True)
+    tol.check_rstd(host(rstd), r_o, _lab(w.name, "fused rstd"))
 
 
 def test_fused_bwd_bf16_32768x4096(orc):
     w = synth.WORKLOADS["fused_bwd_bf16_32768x4096"]
     arr = synth.generate(w)
-    check_fused_bwd(orc, arr, "bf16", w.eps, rows=sample_rows(w.N))
+    check_fused_bwd(orc, arr, "bf16", w.eps, tag=w.name)
 
 
 @pytest.mark.parametrize("name", ["mixed_bf16_f32w_32768x1024", "f16_32768x1024"])
 def test_storage_workloads(orc, name):
     """Full-size runs of the float32-parameter and fp16 paths: every op,
-    sampled rows, parameter gradients over all rows."""
+    every row."""
     w = synth.WORKLOADS[name]
     arr = synth.generate(w)
-    rows = sample_rows(w.N)
-    y, _, _, _ = check_ln_fwd(orc, arr, w.dtype, w.eps, rows=rows)
+    y, _, _, _ = check_ln_fwd(orc, arr, w.dtype, w.eps, tag=name)
     assert y.dtype == TORCH_DT[w.dtype]
-    check_rms_fwd(orc, arr, w.dtype, w.eps, rows=rows)
-    check_bwd(orc, arr, w.dtype, w.eps, layernorm=True, rows=rows)
-    check_bwd(orc, arr, w.dtype, w.eps, layernorm=False, rows=rows)
-    check_fused_bwd(orc, arr, w.dtype, w.eps, rows=rows)
+    check_rms_fwd(orc, arr, w.dtype, w.eps, tag=name)
+    check_bwd(orc, arr, w.dtype, w.eps, layernorm=True, tag=name)
+    check_bwd(orc, arr, w.dtype, w.eps, layernorm=False, tag=name)
+    check_fused_bwd(orc, arr, w.dtype, w.eps, tag=name)
+
+
+def test_step_workload(orc):
+    """The benchmark step's own inputs (32768 x 1024 bf16, with a residual):
+    the five ops in the step's order, every row."""
+    w = synth.WORKLOADS["step_bf16_32768x1024"]
+    arr = synth.generate(w)
+    check_ln_fwd(orc, arr, "bf16", w.eps, tag=w.name)
+    check_rms_fwd(orc, arr, "bf16", w.eps, tag=w.name)
+    x, r, g = (to_dev(arr[k]) for k in ("x", "residual", "gamma"))
+    y, h, rstd = rn.fused_add_rms_fwd(x, r, g, 1e-6)
+    torch.cuda.synchronize()
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(
+        orc.decode(arr["x"], "bf16"), orc.decode(arr["residual"], "bf16"),
+        orc.decode(arr["gamma"], "bf16"), oracle.eps_at_boundary(1e-6))
+    assert np.array_equal(host(h), orc.bf16_encode(h_o)), "h not RNE(x + r)"
+    del h_o
+    tol.check_bf16(host(y), y_o, orc, _lab(w.name, "fused y bf16"), strict=True)
+    tol.check_rstd(host(rstd), r_o, _lab(w.name, "fused rstd"))
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=True, tag=w.name)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=False, tag=w.name)
 
 
 BWD = ["bwd_bf16_32768x1024", "bwd_bf16_16384x2048", "bwd_bf16_512x16384",
@@ -228,12 +266,11 @@ BWD = ["bwd_bf16_32768x1024", "bwd_bf16_16384x2048", "bwd_bf16_512x16384",
 def test_bwd_workloads(orc, name, op):
     w = synth.WORKLOADS[name]
     arr = synth.generate(w)
-    rows = sample_rows(w.N)
     if op == "ln":
-        check_ln_fwd(orc, arr, "bf16", w.eps, rows=rows)
+        check_ln_fwd(orc, arr, "bf16", w.eps, tag=name)
     else:
-        check_rms_fwd(orc, arr, "bf16", w.eps, rows=rows)
-    check_bwd(orc, arr, "bf16", w.eps, layernorm=(op == "ln"), rows=rows)
+        check_rms_fwd(orc, arr, "bf16", w.eps, tag=name)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=(op == "ln"), tag=name)
 
 
 # ------------------------------------------------------------ edge cases --
@@ -267,8 +304,8 @@ def test_shapes_all_ops(orc, storage, H):
     y_o, h_o, r_o = orc.fused_add_rms_fwd(xd, rd, dec(orc, arr, "gamma", dtype),
                                           oracle.eps_at_boundary(1e-6))
     assert np.array_equal(host(h), orc.encode(h_o, dtype))
-    tol.check_out(host(y), y_o, dtype, orc, "fused y")
-    tol.check_rstd(host(rstd), r_o, "fused rstd")
+    tol.check_out(host(y), y_o, dtype, orc, f"edge: fused y {dtype}", strict=True)
+    tol.check_rstd(host(rstd), r_o, "edge: fused rstd")
     check_fused_bwd(orc, arr, dtype, 1e-6)
 
 
@@ -291,15 +328,13 @@ def test_short_rows(orc, storage, H):
 
 
 def test_qk_norm_bf16_1048576x128(orc):
-    """Head-dimension rows (a million rows of 128): sampled rows against the
-    oracle, parameter gradients over all rows."""
+    """Head-dimension rows (a million rows of 128), every row."""
     w = synth.WORKLOADS["rows_bf16_1048576x128"]
     arr = synth.generate(w)
-    rows = sample_rows(w.N, k=200)
-    check_ln_fwd(orc, arr, "bf16", w.eps, rows=rows)
-    check_rms_fwd(orc, arr, "bf16", w.eps, rows=rows)
-    check_bwd(orc, arr, "bf16", w.eps, layernorm=True, rows=rows)
-    check_bwd(orc, arr, "bf16", w.eps, layernorm=False, rows=rows)
+    check_ln_fwd(orc, arr, "bf16", w.eps, tag=w.name)
+    check_rms_fwd(orc, arr, "bf16", w.eps, tag=w.name)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=True, tag=w.name)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=False, tag=w.name)
 
 
 # Rows whose mean dwarfs their spread, on single-wave rows (1024) and on
@@ -368,10 +403,10 @@ def test_strided_rows_and_canaries(orc, dtype, pad, H):
     xd = orc.decode(arr["x"], dtype)
     gd, bd = orc.decode(arr["gamma"], dtype), orc.decode(arr["beta"], dtype)
     y_o, _, _ = orc.ln_fwd(xd, gd, bd, e)
-    tol.check_out(host(Y[:N, :H].contiguous()), y_o, dtype, orc, "strided LN y")
+    tol.check_out(host(Y[:N, :H].contiguous()), y_o, dtype, orc, f"edge: strided LN y {dtype}")
     dyd = orc.decode(arr["dy"], dtype)
     dx_o, _, _, _, r_o = orc.ln_bwd(dyd, xd, gd, e)
-    tol.check_out(host(DX[:N, :H].contiguous()), dx_o, dtype, orc, "strided dx",
+    tol.check_out(host(DX[:N, :H].contiguous()), dx_o, dtype, orc, f"edge: strided dx {dtype}",
                   term_scale=tol.dx_term_scale(dyd, gd, r_o))
     h_o = xd + orc.decode(arr["residual"], dtype)
     assert np.array_equal(host(HH[:N, :H].contiguous()), orc.encode(h_o, dtype))
@@ -390,7 +425,7 @@ def test_fused_in_place(orc, alias):
     y_o, h_o, _ = orc.fused_add_rms_fwd(xd, rd, orc.decode(arr["gamma"], "bf16"),
                                         oracle.eps_at_boundary(1e-6))
     assert np.array_equal(host(target), orc.bf16_encode(h_o))
-    tol.check_bf16(host(y), y_o, orc, "in-place fused y")
+    tol.check_bf16(host(y), y_o, orc, "edge: in-place fused y bf16", strict=True)
 
 
 @pytest.mark.parametrize("with_dh,write_dres,in_place", [
@@ -494,13 +529,12 @@ def test_workspace_contents_on_entry(orc, N, H):
     e = oracle.eps_at_boundary(1e-5)
     xd, dyd, gd = (orc.decode(arr[k], "bf16") for k in ("x", "dy", "gamma"))
     dx_o, dg_o, db_o, _, rstd_o = orc.ln_bwd(dyd, xd, gd, e)
-    rows = sample_rows(N)
-    tol.check_out(host(want[0])[rows], dx_o[rows], "bf16", orc, "dx",
-                  term_scale=tol.dx_term_scale(dyd[rows], gd, rstd_o[rows]))
-    tol.check_param(orc.decode(host(want[1]), "bf16"), dg_o, "dgamma")
-    tol.check_param(orc.decode(host(want[2]), "bf16"), db_o, "dbeta")
+    tol.check_out(host(want[0]), dx_o, "bf16", orc, "edge: workspace states LN dx",
+                  term_scale=tol.dx_term_scale(dyd, gd, rstd_o))
+    tol.check_param(orc.decode(host(want[1]), "bf16"), dg_o, "edge: workspace states dgamma")
+    tol.check_param(orc.decode(host(want[2]), "bf16"), db_o, "edge: workspace states dbeta")
     _, dg_r, _ = orc.rms_bwd(dyd, xd, gd, e)
-    tol.check_param(orc.decode(host(want[4]), "bf16"), dg_r, "dgamma (rms)")
+    tol.check_param(orc.decode(host(want[4]), "bf16"), dg_r, "edge: workspace states RMS dgamma")
 
     states = {"reused": None, "ones": 0xFF, "fe": 0xFE, "random": rand}
     for name, fill in states.items():
@@ -541,8 +575,8 @@ def test_wide_rows(orc, N, H, storage):
         orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype),
         dec(orc, arr, "gamma", dtype), oracle.eps_at_boundary(1e-5))
     assert np.array_equal(host(hf), orc.encode(h_o, dtype)), "h not RNE(x + r)"
-    tol.check_out(host(yf), y_o, dtype, orc, "fused y")
-    tol.check_rstd(host(rsf), r_o, "fused rstd")
+    tol.check_out(host(yf), y_o, dtype, orc, f"edge: fused y {dtype}", strict=True)
+    tol.check_rstd(host(rsf), r_o, "edge: fused rstd")
     check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
     check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
     check_fused_bwd(orc, arr, dtype, 1e-5)
@@ -590,10 +624,9 @@ def test_many_short_rows(orc):
     """Persistent loops with many iterations per workgroup."""
     N, H = 200003, 64
     arr = synth.custom(15, N, H, "bf16")
-    rows = sample_rows(N, k=300)
-    check_ln_fwd(orc, arr, "bf16", 1e-5, rows=rows)
-    check_rms_fwd(orc, arr, "bf16", 1e-5, rows=rows)
-    check_bwd(orc, arr, "bf16", 1e-5, layernorm=True, rows=rows)
+    check_ln_fwd(orc, arr, "bf16", 1e-5)
+    check_rms_fwd(orc, arr, "bf16", 1e-5)
+    check_bwd(orc, arr, "bf16", 1e-5, layernorm=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -720,3 +753,60 @@ def test_forward_without_stats(N, H):
     y1, h1, s1 = rn.fused_add_rms_fwd(x, r, g, 1e-5)
     y0, h0, s0 = rn.fused_add_rms_fwd(x, r, g, 1e-5, save_stats=False)
     assert s0 is None and torch.equal(y0, y1) and torch.equal(h0, h1)
+
+
+@pytest.mark.parametrize("H", [64, 128, 200])
+def test_short_rows_huge_stride(orc, H):
+    """Short rows run several rows per wave through one buffer range per row
+    group, which needs (rows per wave) * stride * e < 2^31; a stride just past
+    that bound makes the host take the one-row-per-wave plan instead (the
+    backward keeps the segment plan's partial-row count).  Forward,
+    backward and fused forward/backward against the oracle, with the bytes
+    after each row and after the last row untouched."""
+    N, e = 3, 2
+    rpw = 8 if H <= 64 else 4 if H <= 128 else 2
+    ld = (1 << 31) // (rpw * e) + 8          # 16-byte rows, bound just crossed
+    assert rpw * ld * e >= 1 << 31
+    arr = synth.custom(70 + H, N, H, "bf16")
+    SENT = -7.0
+    n_el = (N - 1) * ld + H + 64
+
+    def buf(a=None):
+        t = torch.full((n_el,), SENT, dtype=torch.bfloat16, device=DEV)
+        if a is not None:
+            view(t).copy_(to_dev(a))
+        return t
+
+    def view(t):
+        return t.as_strided((N, H), (ld, 1))
+
+    X, DY, R, DH = (buf(arr[k]) for k in ("x", "dy", "residual", "dh"))
+    Y, DX, HH, Y2, DX2 = buf(), buf(), buf(), buf(), buf()
+    g, b = to_dev(arr["gamma"]), to_dev(arr["beta"])
+    _, mean, rstd = rn.ln_fwd(view(X), g, b, 1e-5, y=view(Y))
+    _, _, db = rn.ln_bwd(view(DY), view(X), g, mean, rstd, 1e-5, dx=view(DX))
+    _, _, rs3 = rn.fused_add_rms_fwd(view(X), view(R), g, 1e-6, y=view(Y2), h=view(HH))
+    rn.fused_add_rms_bwd(view(DY), view(HH), g, rs3, 1e-6, dh_in=view(DH), dx=view(DX2))
+    torch.cuda.synchronize()
+    for t, name in ((Y, "y"), (DX, "dx"), (HH, "h"), (Y2, "fused y"), (DX2, "fused dx")):
+        for r in range(N):
+            tail = t[r * ld + H: r * ld + H + 64].float().cpu().numpy()
+            assert np.all(tail == SENT), f"{name}: bytes after row {r} written"
+    e64 = oracle.eps_at_boundary(1e-5)
+    xd, dyd = orc.decode(arr["x"], "bf16"), orc.decode(arr["dy"], "bf16")
+    gd, bd = orc.decode(arr["gamma"], "bf16"), orc.decode(arr["beta"], "bf16")
+    y_o, _, _ = orc.ln_fwd(xd, gd, bd, e64)
+    tol.check_out(host(view(Y).contiguous()), y_o, "bf16", orc, "edge: huge-stride LN y")
+    dx_o, _, db_o, _, r_o = orc.ln_bwd(dyd, xd, gd, e64)
+    tol.check_out(host(view(DX).contiguous()), dx_o, "bf16", orc, "edge: huge-stride LN dx",
+                  term_scale=tol.dx_term_scale(dyd, gd, r_o))
+    tol.check_param(orc.decode(host(db), "bf16"), db_o, "edge: huge-stride LN dbeta")
+    y3_o, h_o, _ = orc.fused_add_rms_fwd(xd, orc.decode(arr["residual"], "bf16"), gd,
+                                         oracle.eps_at_boundary(1e-6))
+    assert np.array_equal(host(view(HH).contiguous()), orc.bf16_encode(h_o))
+    tol.check_out(host(view(Y2).contiguous()), y3_o, "bf16", orc,
+                  "edge: huge-stride fused y", strict=True)
+    arr2 = dict(arr, x=arr["x"])
+    dx2_o, _, ts2, _ = fused_bwd_oracle(orc, arr2, "bf16", 1e-6)
+    tol.check_out(host(view(DX2).contiguous()), dx2_o, "bf16", orc,
+                  "edge: huge-stride fused dx", term_scale=ts2)
