@@ -128,7 +128,7 @@ int fused_add_rms_fwd(const void *x, int64_t ldx, const void *residual,
  *     eps is already inside rstd, so `eps` is only validated);
  *   dx [N, H] out;  dgamma, dbeta [H] out (required);
  *   workspace: device scratch of at least rn_bwd_workspace_bytes(N, H,
- *     dtype, 1) bytes, 256-byte aligned, owned by the caller; it holds the
+ *     dtype, 1, device) bytes, 256-byte aligned, owned by the caller; it holds the
  *     float32 partial rows between the two kernels and must not be touched
  *     until the call's work on `stream` is done.  NULL is fine when that size
  *     is 0.
@@ -163,7 +163,8 @@ int rms_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
  *   dh_in [N, H] in, or NULL for no residual-stream gradient;
  *   dx [N, H] out;  dres [N, H] out, or NULL to write the gradient once
  *     (dx then serves both inputs);  dgamma [H] out;
- *   workspace as for rms_bwd (rn_bwd_workspace_bytes(N, H, dtype, 0)).
+ *   workspace as for rms_bwd (rn_bwd_workspace_bytes(N, H, dtype, 0,
+ *     device)).
  * dx may be exactly dh_in (same pointer and stride: in-place accumulation);
  * any other overlap is RN_EOVERLAP. */
 int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h, int64_t ldh,
@@ -173,12 +174,20 @@ int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h, int64_t ldh,
                       size_t workspace_bytes, int64_t N, int64_t H, int dtype,
                       float eps, hipStream_t stream);
 
-/* Bytes of backward workspace needed on the CURRENT device for (N, H,
- * dtype, LayerNorm or RMSNorm).  It grows with H and the device's
- * compute-unit count, and with N only up to a small multiple of the CU
- * count.  Returns RN_OK and sets *bytes, or an error code. */
+/* Bytes of backward workspace ln_bwd / rms_bwd / fused_add_rms_bwd need for
+ * (N, H, dtype, LayerNorm or RMSNorm) on GPU `device` (-1: the current
+ * device).  The workspace holds the float32 partial rows of dgamma (and
+ * dbeta) between the two backward kernels; their count is the first
+ * kernel's workgroup count, a small multiple of the compute-unit count, so
+ * the size grows with H and with N only up to that count ("Rewrite Triton
+ * normalization backward kernel_1 (#499)", Summary: bounded partial rows,
+ * program count tied to the CU count).  It depends on dtype because each
+ * storage pair has its own team plans, and on the device's CU count.
+ * Returns RN_OK and sets *bytes (0 for N = 0, without touching any GPU), or
+ * RN_EINVAL (bytes NULL, device < -1, bad N/H), RN_EDTYPE, RN_EUNSUPPORTED,
+ * or RN_EHIP (the device cannot be queried). */
 int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype, int is_layernorm,
-                           size_t *bytes);
+                           int device, size_t *bytes);
 
 /* Largest H supported for `dtype` (rows are held in registers): for rows
  * whose size, stride or base address is not a multiple of 16 bytes a
@@ -186,22 +195,12 @@ int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype, int is_layernorm,
  * `vectorizable` = 0. */
 int64_t rn_max_hidden(int dtype, int vectorizable);
 
+/* Text for a status code.  The argument checks behind the codes follow the
+ * pages' launcher duties ("Write Triton Fused Add Rmsnorm Kernel", Required
+ * reasoning process: validate shapes, strides and aliasing before launch;
+ * "Write Triton Layernorm Kernel", Correctness requirements: reject a
+ * non-positive eps).  Never NULL; unknown codes give "unknown status". */
 const char *rn_status_str(int status);
-
-/* Benchmark helper, not part of the normalization: copies `bytes` bytes
- * between two device buffers with 16-byte loads/stores (used as the
- * streaming-copy ceiling, as a cache flush, and as the known-size kernel
- * that calibrates hardware byte counters).  Buffers must not overlap. */
-int rn_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
-
-/* Benchmark helper, not part of the normalization: out = a + b over n
- * elements of the activation type of `dtype` (float32 add, rounded to the
- * storage type), the first launch of the unfused add-then-RMSNorm
- * comparison ("Write Triton Fused Add Rmsnorm Kernel", Required reasoning
- * process, the traffic comparison).  out may be exactly a or b; any other
- * overlap is RN_EOVERLAP. */
-int rn_add(const void *a, const void *b, void *out, int64_t n, int dtype,
-           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "RN_OK", -1: "RN_EINVAL", -2: "RN_EDTYPE",
                 -3: "RN_EOVERLAP", -4: "RN_EWORKSPACE", -5: "RN_EHIP",
                 -6: "RN_EUNSUPPORTED"}
 
-# name -> (argtypes, restype); mirrors include/rownorm.h
+# name -> (argtypes, restype); mirrors include/rownorm.h and (the benchmark
+# helpers rn_copy, rn_add) include/rownorm_bench.h
 _P, _I64, _I, _F, _SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                          ctypes.c_float, ctypes.c_size_t)
 SIGNATURES = {
@@ -39,7 +40,7 @@ SIGNATURES = {
                  _I64, _I, _F, _P], _I),
     "fused_add_rms_bwd": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _P,
                            _I64, _P, _P, _SZ, _I64, _I64, _I, _F, _P], _I),
-    "rn_bwd_workspace_bytes": ([_I64, _I64, _I, _I, ctypes.POINTER(_SZ)], _I),
+    "rn_bwd_workspace_bytes": ([_I64, _I64, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
     "rn_max_hidden": ([_I, _I], _I64),
     "rn_status_str": ([_I], ctypes.c_char_p),
     "rn_copy": ([_P, _P, _SZ, _P], _I),
@@ -205,20 +206,26 @@ def fused_add_rms_fwd(x, residual, gamma, eps=1e-6, *, y=None, h=None,
 
 
 # --------------------------------------------------------------- backward --
-def workspace_bytes(N, H, dtype, layernorm: bool, param_dtype=None) -> int:
-    """Backward workspace size on the current device (rn_bwd_workspace_bytes)
-    for activations of `dtype` and parameters of `param_dtype` (default:
-    the same)."""
+def workspace_bytes(N, H, dtype, layernorm: bool, param_dtype=None,
+                    device=None) -> int:
+    """Backward workspace size (rn_bwd_workspace_bytes) for activations of
+    `dtype` and parameters of `param_dtype` (default: the same) on GPU
+    `device` (an index or torch.device; default: the current device)."""
     code = _code_of(dtype, dtype if param_dtype is None else param_dtype)
+    if device is None:
+        dev = -1
+    else:
+        dev = device if isinstance(device, int) else device.index
+        dev = -1 if dev is None else dev
     out = ctypes.c_size_t(0)
     _check("rn_bwd_workspace_bytes", lib().rn_bwd_workspace_bytes(
-        N, H, code, 1 if layernorm else 0, ctypes.byref(out)))
+        N, H, code, 1 if layernorm else 0, dev, ctypes.byref(out)))
     return int(out.value)
 
 
 def _workspace(workspace, N, H, x, gamma, layernorm):
     import torch
-    need = workspace_bytes(N, H, x.dtype, layernorm, gamma.dtype)
+    need = workspace_bytes(N, H, x.dtype, layernorm, gamma.dtype, x.device)
     if workspace is None:
         # 256-byte aligned by torch's caching allocator
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)

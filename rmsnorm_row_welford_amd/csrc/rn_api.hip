@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/rownorm.h"
+#include "../../include/rownorm_bench.h"
 #include "rn_internal.h"
 
 using namespace rn;
@@ -245,15 +246,8 @@ static int partial_rows(int dtype, int64_t N, int64_t H, bool vec, int cus) {
     return bwd_partials(dtype, N, (int)H, vec, cus);
 }
 
-extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
-                                      int is_layernorm, size_t *bytes) {
-    if (!bytes) return RN_EINVAL;
-    if (!dtype_ok(dtype)) return RN_EDTYPE;
-    RN_TRY(check_shape(N, H));
-    if (N == 0) {
-        *bytes = 0;
-        return RN_OK;
-    }
+static int workspace_bytes_here(int64_t N, int64_t H, int dtype, int is_layernorm,
+                                size_t *bytes) {
     int cus = 0;
     RN_TRY(current_cus(&cus));
     // The vector and element-wise plans may differ; size for the larger of
@@ -273,6 +267,25 @@ extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
     if (!any) return RN_EUNSUPPORTED;
     *bytes = need;
     return RN_OK;
+}
+
+extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
+                                      int is_layernorm, int device, size_t *bytes) {
+    if (!bytes || device < -1) return RN_EINVAL;
+    if (!dtype_ok(dtype)) return RN_EDTYPE;
+    RN_TRY(check_shape(N, H));
+    if (N == 0) {
+        *bytes = 0;
+        return RN_OK;
+    }
+    if (device == -1) return workspace_bytes_here(N, H, dtype, is_layernorm, bytes);
+    // another device: make it current for the query, then restore
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return RN_EHIP;
+    if (device != cur && hipSetDevice(device) != hipSuccess) return RN_EHIP;
+    const int st = workspace_bytes_here(N, H, dtype, is_layernorm, bytes);
+    if (device != cur && hipSetDevice(cur) != hipSuccess) return RN_EHIP;
+    return st;
 }
 
 // Shared by the three backward entry points.  `fused` = the fused

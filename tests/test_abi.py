@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: librownorm.so loads, exports every function
-include/rownorm.h declares, and rejects bad arguments before anything is
+include/rownorm.h and include/rownorm_bench.h declare (with the argument
+count the binding declares), and rejects bad arguments before anything is
 enqueued (all of these return before the library's first HIP call, so no
 compute call is made here).  Pointers below are fake, suitably aligned
 addresses that are never dereferenced."""
@@ -12,7 +13,7 @@ import pytest
 import rmsnorm_row_welford_amd as rn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rownorm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rownorm.h", "rownorm_bench.h")]
 
 OK, EINVAL, EDTYPE, EOVERLAP, EWORKSPACE, EHIP, EUNSUP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16, F16, BF16_F32W, F16_F32W = 0, 1, 2, 3, 4
@@ -26,12 +27,21 @@ def L():
     return rn.lib()
 
 
+def declarations():
+    """name -> parameter count of every function the headers declare."""
+    out = {}
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char|void)\s*\*?\s*"
+                             r"(\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+            params = [p for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+            out[m.group(1)] = len(params)
+    return out
+
+
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char|void)\s*\*?\s*"
-                       r"(\w+)\s*\(", text, flags=re.M)
-    return sorted(set(names))
+    return sorted(declarations())
 
 
 def test_header_declares_the_boundary():
@@ -42,10 +52,17 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_symbol(L):
-    names = declared_functions()
-    assert names == sorted(rn.SIGNATURES), "binding and header disagree"
-    for n in names:
+    decl = declarations()
+    assert sorted(decl) == sorted(rn.SIGNATURES), "binding and headers disagree"
+    for n, nargs in decl.items():
         assert hasattr(L, n), f"{n} not exported"
+        assert len(rn.SIGNATURES[n][0]) == nargs, f"{n}: binding has the wrong arity"
+
+
+def test_bench_helpers_live_in_their_own_header():
+    main = open(HEADERS[0]).read()
+    for n in ("rn_copy", "rn_add"):
+        assert n + "(" not in re.sub(r"/\*.*?\*/", "", main, flags=re.S)
 
 
 def test_status_strings(L):
@@ -165,12 +182,17 @@ def test_rms_bwd_argument_errors(L):
 
 
 def test_workspace_query_without_device(L):
+    # (N, H, dtype, is_layernorm, device, &bytes); device -1 = current
     out = ctypes.c_size_t(123)
-    assert L.rn_bwd_workspace_bytes(0, 1024, BF16, 1, ctypes.byref(out)) == OK
+    assert L.rn_bwd_workspace_bytes(0, 1024, BF16, 1, -1, ctypes.byref(out)) == OK
     assert out.value == 0
-    assert L.rn_bwd_workspace_bytes(10, 1024, 9, 1, ctypes.byref(out)) == EDTYPE
-    assert L.rn_bwd_workspace_bytes(10, 0, BF16, 1, ctypes.byref(out)) == EINVAL
-    assert L.rn_bwd_workspace_bytes(10, 1024, BF16, 1, None) == EINVAL
+    out.value = 7
+    assert L.rn_bwd_workspace_bytes(0, 1024, BF16, 0, 3, ctypes.byref(out)) == OK
+    assert out.value == 0                    # N = 0 touches no device
+    assert L.rn_bwd_workspace_bytes(10, 1024, 9, 1, -1, ctypes.byref(out)) == EDTYPE
+    assert L.rn_bwd_workspace_bytes(10, 0, BF16, 1, -1, ctypes.byref(out)) == EINVAL
+    assert L.rn_bwd_workspace_bytes(10, 1024, BF16, 1, -1, None) == EINVAL
+    assert L.rn_bwd_workspace_bytes(10, 1024, BF16, 1, -2, ctypes.byref(out)) == EINVAL
 
 
 def test_copy_argument_errors(L):

@@ -714,6 +714,8 @@ def test_workspace_errors():
     _, rstd = rn.rms_fwd(x, g, 1e-5)
     need = rn.workspace_bytes(64, H, torch.bfloat16, False)
     assert need >= H * 4          # at least one float32 partial row
+    # the same size when the device is named explicitly
+    assert rn.workspace_bytes(64, H, torch.bfloat16, False, device=0) == need
     small = torch.empty(H * 4 - 4, dtype=torch.uint8, device=DEV)
     with pytest.raises(rn.RowNormError) as ei:
         rn.rms_bwd(x, x, g, rstd, 1e-5, workspace=small)
