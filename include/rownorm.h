@@ -140,6 +140,25 @@ int ln_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
            size_t workspace_bytes, int64_t N, int64_t H, int dtype, float eps,
            hipStream_t stream);
 
+/* ln_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture that may not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation).  The partial rows
+ * live in a static device array of RN_NOALLOC_MAX_WORKSPACE_BYTES inside
+ * the library, one per GPU, held until the process ends; the call itself
+ * allocates nothing.  Same arguments, checks, kernels and results (bit for
+ * bit) as ln_bwd with a caller workspace.  A shape whose partial rows need
+ * more than RN_NOALLOC_MAX_WORKSPACE_BYTES (rn_bwd_workspace_bytes(N, H,
+ * dtype, 1, device) larger than it) returns RN_EWORKSPACE and enqueues
+ * nothing.  All calls on one GPU share its array: calls whose work may
+ * overlap in time on that GPU (e.g. on two streams) race and must be
+ * ordered by the caller.  The first call on each GPU looks up the array's
+ * address there (RN_EHIP if that fails); make it outside graph capture. */
+#define RN_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)32 << 20)
+int ln_bwd_noalloc(const void *dy, int64_t lddy, const void *x, int64_t ldx,
+                   const void *gamma, const float *mean, const float *rstd,
+                   void *dx, int64_t lddx, void *dgamma, void *dbeta, int64_t N,
+                   int64_t H, int dtype, float eps, hipStream_t stream);
+
 /* RMSNorm backward.  The pages ask for it but print no formula; it is the
  * derivative of rms_fwd: with x_hat = x * rstd and g = dy * gamma,
  *   c2 = sum(g * x_hat)/H,   dx = rstd * (g - x_hat * c2),

@@ -36,6 +36,8 @@ SIGNATURES = {
                            _I64, _I64, _I, _F, _P], _I),
     "ln_bwd": ([_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P, _P, _SZ,
                 _I64, _I64, _I, _F, _P], _I),
+    "ln_bwd_noalloc": ([_P, _I64, _P, _I64, _P, _P, _P, _P, _I64, _P, _P,
+                        _I64, _I64, _I, _F, _P], _I),
     "rms_bwd": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _I64,
                  _I64, _I, _F, _P], _I),
     "fused_add_rms_bwd": ([_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64, _P,
@@ -253,6 +255,32 @@ def ln_bwd(dy, x, gamma, mean, rstd, eps=1e-5, *, dx=None, dgamma=None,
         _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(mean), _ptr(rstd),
         _ptr(dx), _rows(dx, "dx"), _ptr(dgamma), _ptr(dbeta), _ptr(ws), wsb,
         N, H, _dtype_code(x, gamma), float(eps), _stream(stream)))
+    return dx, dgamma, dbeta
+
+
+def ln_bwd_noalloc(dy, x, gamma, mean, rstd, eps=1e-5, *, dx=None, dgamma=None,
+                   dbeta=None, stream=None):
+    """LayerNorm backward with the library's static per-GPU partial-row
+    array instead of a workspace (the entry point allocates nothing; pass
+    dx, dgamma and dbeta to allocate nothing here either).  Returns
+    (dx, dgamma, dbeta)."""
+    import torch
+    N, H = x.shape
+    ldx = _rows(x, "x")
+    lddy = _rows(dy, "dy")
+    _vec(gamma, H, "gamma")
+    _stats(mean, N, "mean")
+    _stats(rstd, N, "rstd")
+    if dx is None:
+        dx = torch.empty((N, H), dtype=x.dtype, device=x.device)
+    if dgamma is None:
+        dgamma = torch.empty(H, dtype=gamma.dtype, device=x.device)
+    if dbeta is None:
+        dbeta = torch.empty(H, dtype=gamma.dtype, device=x.device)
+    _check("ln_bwd_noalloc", lib().ln_bwd_noalloc(
+        _ptr(dy), lddy, _ptr(x), ldx, _ptr(gamma), _ptr(mean), _ptr(rstd),
+        _ptr(dx), _rows(dx, "dx"), _ptr(dgamma), _ptr(dbeta), N, H,
+        _dtype_code(x, gamma), float(eps), _stream(stream)))
     return dx, dgamma, dbeta
 
 

@@ -374,6 +374,53 @@ extern "C" int ln_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
                       workspace_bytes, N, H, dtype, eps, stream);
 }
 
+// ------------------------------------------------ no-allocation backward --
+// ln_bwd_noalloc keeps its partial rows in this array instead of a caller
+// workspace: one copy per GPU the library runs on, held until the process
+// ends.  On the host the array's name is only a stand-in for the symbol,
+// not a device address: host code uses the address hipGetSymbolAddress
+// returns for the current device (scratch_here), never the name.  Kernel 1
+// writes every partial-row slot kernel 2 reads, within the same call, so
+// nothing in it has to start at zero; calls on one GPU share it, and calls
+// whose work overlaps in time on that GPU (two streams) race.
+static __device__ __align__(256) unsigned char scratch[RN_NOALLOC_MAX_WORKSPACE_BYTES];
+
+namespace {
+void *g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) on the first call there.
+int scratch_here(void **p) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return RN_EHIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *q = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        g_scratch[dev] = g_scratch_err[dev] == hipSuccess ? q : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || g_scratch[dev] == nullptr) return RN_EHIP;
+    *p = g_scratch[dev];
+    return RN_OK;
+}
+}  // namespace
+
+extern "C" int ln_bwd_noalloc(const void *dy, int64_t lddy, const void *x,
+                              int64_t ldx, const void *gamma, const float *mean,
+                              const float *rstd, void *dx, int64_t lddx,
+                              void *dgamma, void *dbeta, int64_t N, int64_t H,
+                              int dtype, float eps, hipStream_t stream) {
+    void *ws = nullptr;
+    RN_TRY(scratch_here(&ws));
+    // the same checks and kernels as ln_bwd; a shape whose partial rows
+    // exceed the array is RN_EWORKSPACE before anything is enqueued
+    return bwd_common(true, false, dy, lddy, x, ldx, gamma, mean, rstd, nullptr, 0,
+                      dx, lddx, nullptr, 0, dgamma, dbeta, ws,
+                      RN_NOALLOC_MAX_WORKSPACE_BYTES, N, H, dtype, eps, stream);
+}
+
 extern "C" int rms_bwd(const void *dy, int64_t lddy, const void *x,
                        int64_t ldx, const void *gamma, const float *rstd,
                        void *dx, int64_t lddx, void *dgamma, void *workspace,
