@@ -315,16 +315,23 @@ def time_op_swept(sets, op, K, sweep):
     return float(np.median([a.elapsed_time(b) for a, b in ms])) * 1e3
 
 
-def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24):
+def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24, only_ops=None):
     """Per-op times at the other workload shapes: for each, enough rotating
     copies that consecutive launches touch data last used about `cold_bytes`
-    of traffic earlier (so it comes from HBM), K launches back to back."""
+    of traffic earlier (so it comes from HBM), K launches back to back.
+    names: workloads to time (any synth workload; default: the SHAPES
+    table); only_ops: restrict each workload to these ops (used to profile
+    one op of one shape per kernel trace)."""
     import torch
     from rmsnorm_row_welford_amd import synth
     out = {}
-    for name, ops in SHAPES:
-        if names is not None and name not in names:
-            continue
+    table = dict(SHAPES)
+    todo = SHAPES if names is None else [(n, table.get(n, NORM_OPS)) for n in names]
+    for name, ops in todo:
+        if only_ops is not None:
+            ops = tuple(o for o in only_ops if o in ALL_OPS)
+            if not ops:
+                continue
         w = synth.WORKLOADS[name]
         arr = synth.generate(w)
         N, H = w.N, w.H
@@ -475,6 +482,11 @@ def main():
     ap.add_argument("--shapes-only", default=None,
                     help="comma list of shape workloads (or 'all'): time only "
                          "those, print their table as the JSON line, no step")
+    ap.add_argument("--ops", default=None,
+                    help="with --shapes-only: comma list of the ops to time")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="with --shapes-only: also run one 1 GiB rn_copy (the "
+                         "known-size kernel that calibrates byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -494,7 +506,15 @@ def main():
     torch.cuda.set_device(dev)
     if args.shapes_only:
         names = None if args.shapes_only == "all" else args.shapes_only.split(",")
-        print(json.dumps({"shapes": time_shapes(rn, dev, names)}), flush=True)
+        only = None if not args.ops else args.ops.split(",")
+        if args.calib_copy:
+            a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            rn.copy(a, b)
+            torch.cuda.synchronize()
+            del a, b
+        print(json.dumps({"shapes": time_shapes(rn, dev, names, only_ops=only)}),
+              flush=True)
         return
     w = synth.WORKLOADS[WORKLOAD]
     N, H = w.N, w.H

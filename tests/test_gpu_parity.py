@@ -49,8 +49,9 @@ def pdt(arr, dtype):
 
 # Share of LayerNorm y and dx elements that may pass only through the
 # cancellation floor on the named workloads: only |v| below about 2^-14 of
-# the row scale can need it, about 5e-5 of a normal sample.
-FLOOR_FRAC = 2e-4
+# the row scale can need it, about 5e-5 of a normal sample (measured on
+# MI355X: at most 5.4e-6 on any of them).
+FLOOR_FRAC = 5e-5
 
 
 def dec(orc, arr, k, dtype):
@@ -474,7 +475,7 @@ def test_fused_bwd_strided(orc, dtype, pad):
         assert np.all(hb[N, :] == SENT), f"{name}: guard row written"
     dx_o, _, ts, _ = fused_bwd_oracle(orc, arr, dtype, 1e-6)
     tol.check_out(host(DX[:N, :H].contiguous()), dx_o, dtype, orc,
-                  "strided fused dx", term_scale=ts)
+                  f"edge: strided fused dx {dtype}", term_scale=ts)
     assert torch.equal(DX, DR)
 
 
