@@ -78,7 +78,7 @@ enum {
     RN_EOVERLAP = -3,      /* an output overlaps an input or another output */
     RN_EWORKSPACE = -4,    /* backward workspace missing or too small       */
     RN_EHIP = -5,          /* a HIP runtime call failed                     */
-    RN_EUNSUPPORTED = -6   /* H above the largest row length (rn_max_hidden) */
+    RN_EUNSUPPORTED = -6   /* H above the longest row (rn_max_hidden)         */
 };
 
 /* LayerNorm forward ("Write Triton Layernorm Kernel", Required reasoning
@@ -208,10 +208,17 @@ int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h, int64_t ldh,
 int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype, int is_layernorm,
                            int device, size_t *bytes);
 
-/* Largest H supported for `dtype` (rows are held in registers): for rows
- * whose size, stride or base address is not a multiple of 16 bytes a
- * narrower element-wise path runs, with a lower limit, given by
- * `vectorizable` = 0. */
+/* Longest row (H) supported for `dtype`: 4194304 elements on both the 16-byte
+ * path (rows whose size, stride and base addresses are multiples of 16
+ * bytes) and the element-wise path (`vectorizable` = 0).  Rows of up to
+ * 16384 (16-byte path) or 8192 (element-wise) elements are held in
+ * registers and cross HBM once; longer rows are walked in segments by one
+ * 1024-thread workgroup, cached in LDS between the statistics and the
+ * output pass where they fit (160 KiB on MI355X: x for the LayerNorm and
+ * RMSNorm forward, x and the residual for the fused forward, x and dy for
+ * the backward) and read twice otherwise ("Write Triton Layernorm Kernel",
+ * Required reasoning process, large-H loop over column blocks).  Returns 0
+ * for an unknown dtype. */
 int64_t rn_max_hidden(int dtype, int vectorizable);
 
 /* Text for a status code.  The argument checks behind the codes follow the

@@ -20,6 +20,9 @@ constexpr int kMaxDevices = 64;
 int g_cus[kMaxDevices];
 std::once_flag g_once[kMaxDevices];
 
+int g_lds[kMaxDevices];
+std::once_flag g_lds_once[kMaxDevices];
+
 // Compute-unit count of the current device, cached per device.
 int current_cus(int *cus) {
     int dev = 0;
@@ -36,6 +39,25 @@ int current_cus(int *cus) {
     *cus = g_cus[dev];
     return RN_OK;
 }
+
+}  // namespace
+
+// Dynamic LDS a long-row workgroup may use: the device's per-workgroup
+// limit, less 1 KiB for the kernels' static LDS; cached per device.
+int rn::long_lds_budget() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::call_once(g_lds_once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+            n = 0;
+        g_lds[dev] = n > 1024 ? n - 1024 : 0;
+    });
+    return g_lds[dev];
+}
+
+namespace {
 
 // Bytes per element of the rn_dtype codes: activations (x, residual, h, y,
 // dy, dx, ...) and parameters (gamma, beta, dgamma, dbeta).
@@ -194,7 +216,6 @@ static int fwd_common(int op, const void *x, int64_t ldx, const void *res,
         vc.ld(ldr);
         vc.ld(ldh);
     }
-    if (!vc.ok && H > kMaxHiddenScalar) return RN_EUNSUPPORTED;
 
     if (N == 0) return RN_OK;
     int cus = 0;
@@ -259,7 +280,9 @@ static int workspace_bytes_here(int64_t N, int64_t H, int dtype, int is_layernor
         const int P = partial_rows(dtype, N, H, v == 0, cus);
         if (P < 0) continue;
         any = true;
-        if (bwd_use_colsum(N, (int)H, e, P, is_layernorm != 0, cus)) continue;
+        if (bwd_force_colsum(H, v == 0) ||
+            bwd_use_colsum(N, (int)H, e, P, is_layernorm != 0, cus))
+            continue;
         const size_t b = (size_t)partial_stride(P) * (size_t)H * sizeof(float) *
                          (is_layernorm ? 2 : 1);
         if (b > need) need = b;
@@ -345,12 +368,12 @@ static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
 
     const int64_t lds[] = {lddy, ldx, lddx, add ? ldadd : lddx, dx2 ? lddx2 : lddx};
     const bool vec = bwd_vec_ok(e, H, ptrs, 8, lds, 5);
-    if (!vec && H > kMaxHiddenScalar) return RN_EUNSUPPORTED;
     int cus = 0;
     RN_TRY(current_cus(&cus));
     const int P = N == 0 ? 0 : partial_rows(dtype, N, H, vec, cus);
     if (P < 0) return RN_EUNSUPPORTED;
-    const bool colsum = bwd_use_colsum(N, (int)H, (int)e, P, ln, cus);
+    const bool colsum =
+        N > 0 && (bwd_force_colsum(H, vec) || bwd_use_colsum(N, (int)H, (int)e, P, ln, cus));
     const size_t need =
         colsum ? 0 : (size_t)partial_stride(P) * (size_t)H * sizeof(float) * (ln ? 2 : 1);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RN_EWORKSPACE;
@@ -446,7 +469,8 @@ extern "C" int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h,
 // ------------------------------------------------------------------- misc --
 extern "C" int64_t rn_max_hidden(int dtype, int vectorizable) {
     if (!dtype_ok(dtype)) return 0;
-    return vectorizable ? kMaxHidden : kMaxHiddenScalar;
+    (void)vectorizable;   // both paths walk long rows in segments
+    return kMaxHidden;
 }
 
 extern "C" const char *rn_status_str(int status) {

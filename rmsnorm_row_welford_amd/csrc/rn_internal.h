@@ -55,9 +55,26 @@ struct BwdArgs {
 // multiple of 8 slots.
 __host__ __device__ inline int partial_stride(int P) { return (P + 7) & ~7; }
 
-// Largest H each path supports: 16-byte vector path, element-wise path.
-constexpr int kMaxHidden = 16384;
-constexpr int kMaxHiddenScalar = 8192;
+// Longest rows the register-resident plans hold: 16-byte vector path,
+// element-wise path.  Longer rows walk their row in segments (rn_long.h).
+constexpr int kMaxHiddenReg = 16384;
+constexpr int kMaxHiddenRegScalar = 8192;
+// Longest row any path takes (4 Mi elements: byte offsets within a row stay
+// far below 2^31).
+constexpr int kMaxHidden = 1 << 22;
+inline bool is_long_row(int64_t H, bool vec) {
+    return H > (vec ? kMaxHiddenReg : kMaxHiddenRegScalar);
+}
+// The long-row backward keeps per-lane dgamma/dbeta accumulators (and so
+// writes partial rows) for rows of up to this many elements; longer rows
+// always take the column-sum strategy.
+constexpr int kLongAccMaxH = 32768;
+inline bool bwd_force_colsum(int64_t H, bool vec) {
+    return is_long_row(H, vec) && H > kLongAccMaxH;
+}
+// Dynamic LDS a long-row workgroup may use on the current device for its row
+// cache (the device's per-workgroup limit less a margin for static LDS).
+int long_lds_budget();
 
 // Per storage pair (activations / parameters), one translation unit per
 // direction defines:

@@ -1,0 +1,474 @@
+// Rows longer than the register-resident plans reach (16-byte path: above
+// 16384 elements; element-wise path: above 8192).
+//
+// One 1024-thread workgroup owns a row at a time and walks it in segments of
+// 1024*VEC elements, lane l holding chunk [(s*1024 + l)*VEC, +VEC) of
+// segment s (coalesced 16-byte accesses, as in the register plans).  Each
+// row is passed over twice: the first pass reads the row from HBM and forms
+// the statistics, the second forms the outputs.  Between the two passes the
+// row waits in LDS when it fits ("cache": the raw chunks of x, and of the
+// residual or dy, at the same place for the same lane, so no lane reads what
+// another wrote and no barrier is needed); otherwise the second pass reads
+// it again from global memory, where it usually still sits in L2.  These are
+// the pages' two-pass designs for rows wider than one tile ("Write Triton
+// Layernorm Kernel", Required reasoning process, the loop over column
+// blocks for large H; "Write Triton Fused Add Rmsnorm Kernel", Required
+// reasoning process, the two-pass variant; "Write Cuda Layernorm Kernel",
+// Kernel design rules, the stride loop).
+//
+// LayerNorm statistics in one read pass: every value is shifted by the
+// row's first element (as in the register plans), each lane forms the exact
+// mean and M2 of each of its chunks and merges them into a running
+// (count, mean, M2) with the parallel merge ("Write Cuda Layernorm Kernel",
+// Required reasoning process, the Welford merge formula), and the 1024
+// lanes' states are combined by the multi-way form of the same merge:
+// mean = sum(n_l m_l)/H, M2 = sum(M2_l + n_l (m_l - mean)^2).  RMSNorm and
+// the fused op sum squares.  The denominator is always H.
+//
+// Backward: the first pass forms x_hat, g = dy*gamma and the row sums of g
+// and g*x_hat (and, for rows of up to 32 elements per lane, adds dy*x_hat and
+// dy into per-lane accumulators that become the workgroup's partial row);
+// the second pass forms dx.  Wider rows leave dgamma/dbeta to the column-sum
+// kernel.
+#pragma once
+
+#include "rn_kernels.h"
+
+namespace rn {
+
+constexpr int kLongThreads = 1024;
+// The backward's per-lane dgamma/dbeta accumulators: 32 elements per lane.
+static_assert(kLongAccMaxH == 32 * kLongThreads, "accumulators for 32 elements per lane");
+// Segments whose loads are issued together.
+#ifndef RN_LONG_UNROLL
+#define RN_LONG_UNROLL 4
+#endif
+
+// Sum over the 16 waves of a 1024-thread workgroup; every lane gets the same
+// bits.  `red` holds two slots of 16 floats used in turn (a slot is written
+// again only after every wave has passed the barrier of the sum in between,
+// so after every wave has read it).
+__device__ __forceinline__ float block_sum16(float v, float *red, int &parity) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63;
+    float *slot = red + parity * 16;
+    if (lane == 0) slot[wave_id_uniform()] = v;
+    __syncthreads();
+    const float t = wave_sum(lane < 16 ? slot[lane] : 0.0f);
+    parity ^= 1;
+    return t;
+}
+
+// A raw chunk in LDS: lane-private slots, stored and loaded whole.
+template <class T, int VEC>
+__device__ __forceinline__ void lds_put(unsigned char *p, const RawChunk<T, VEC> &c) {
+    if constexpr (VEC * sizeof(T) == 16) *(u32x4 *)p = __builtin_bit_cast(u32x4, c.v);
+    else if constexpr (VEC * sizeof(T) == 4) *(uint32_t *)p = __builtin_bit_cast(uint32_t, c.v);
+    else *(uint16_t *)p = (uint16_t)c.v;
+}
+template <class T, int VEC>
+__device__ __forceinline__ void lds_get(const unsigned char *p, RawChunk<T, VEC> &c) {
+    if constexpr (VEC * sizeof(T) == 16) c.v = __builtin_bit_cast(decltype(c.v), *(const u32x4 *)p);
+    else if constexpr (VEC * sizeof(T) == 4)
+        c.v = __builtin_bit_cast(decltype(c.v), *(const uint32_t *)p);
+    else c.v = *(const uint16_t *)p;
+}
+
+// Bytes of one row of T in the LDS cache (rounded to 16).
+__host__ __device__ inline uint32_t long_row_pad(int H, int esize) {
+    return ((uint32_t)H * (uint32_t)esize + 15u) & ~15u;
+}
+
+// Forward.  `cache`: the row's raw inputs fit in the dynamic LDS (NIN rows of
+// long_row_pad bytes) and wait there between the passes.
+template <class T, class W, int VEC, int OP>
+__global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a, int cache) {
+    using Raw = RawChunk<T, VEC>;
+    using RawW = RawChunk<W, VEC>;
+    constexpr int U = RN_LONG_UNROLL;
+    constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;
+    constexpr int SPAN = kLongThreads * VEC;
+    extern __shared__ f32x4 lds_cache[];
+    __shared__ float red[2 * 16];
+    unsigned char *lds = (unsigned char *)lds_cache;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int nseg = (H + SPAN - 1) / SPAN;
+    const uint32_t pad = long_row_pad(H, (int)sizeof(T));
+    const uint32_t nb = (uint32_t)H * (uint32_t)sizeof(T);
+    const rsrc_t rg = make_rsrc(a.gamma, (uint32_t)H * (uint32_t)sizeof(W));
+    const rsrc_t rbt = make_rsrc(a.beta ? a.beta : a.gamma,
+                                 a.beta ? (uint32_t)H * (uint32_t)sizeof(W) : 0u);
+    int parity = 0;
+
+    for (int64_t row = blockIdx.x; row < a.N; row += gridDim.x) {
+        const rsrc_t rx = make_rsrc((const T *)a.x + row * a.ldx, nb);
+        const rsrc_t rr =
+            make_rsrc(OP == OP_FUSED ? (const T *)a.res + row * a.ldr : (const T *)a.x,
+                      OP == OP_FUSED ? nb : 0u);
+        // LayerNorm pivot: the row's first element (every lane loads it)
+        float pivot = 0.0f;
+        if constexpr (OP == OP_LN) {
+            RawChunk<T, 1> p0;
+            p0.template bload<0>(rx, 0);
+            pivot = p0.get(0);
+        }
+        // ---- pass 1: statistics (and the LDS copy of the row)
+        float ln_n = 0.0f, ln_m = 0.0f, ln_q = 0.0f, q = 0.0f;
+        for (int s0 = 0; s0 < nseg; s0 += U) {
+            Raw cx[U][NIN];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t off = (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T));
+                cx[u][0].template bload<RN_LOAD_AUX>(rx, off);
+                if constexpr (OP == OP_FUSED) cx[u][1].template bload<RN_LOAD_AUX>(rr, off);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = (s0 + u) * SPAN + tid * VEC;
+                const bool valid = e0 < H;
+                if (cache && valid) {
+                    const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
+#pragma unroll
+                    for (int i = 0; i < NIN; ++i) lds_put<T, VEC>(lds + i * pad + off, cx[u][i]);
+                }
+                if constexpr (OP == OP_LN) {
+                    if (valid) {
+                        // exact two-pass mean and M2 of the chunk, then the
+                        // parallel merge into the lane's running state
+                        float uu[VEC], sm = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            uu[k] = cx[u][0].get(k) - pivot;
+                            sm += uu[k];
+                        }
+                        const float mc = sm * (1.0f / (float)VEC);
+                        float m2c = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < VEC; ++k) {
+                            const float d = uu[k] - mc;
+                            m2c = __builtin_fmaf(d, d, m2c);
+                        }
+                        const float n1 = ln_n + (float)VEC;
+                        const float f = (float)VEC / n1;
+                        const float dl = mc - ln_m;
+                        ln_m = __builtin_fmaf(dl, f, ln_m);
+                        ln_q += m2c + dl * dl * (ln_n * f);
+                        ln_n = n1;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        float v = cx[u][0].get(k);
+                        if constexpr (OP == OP_FUSED) v += cx[u][1].get(k);
+                        q = __builtin_fmaf(v, v, q);
+                    }
+                }
+            }
+        }
+        float mean = 0.0f, ms = 0.0f, var;
+        if constexpr (OP == OP_LN) {
+            // multi-way merge of the lanes' states (about the pivot)
+            ms = block_sum16(ln_n * ln_m, red, parity) * a.inv_H;
+            const float dm = ln_m - ms;
+            var = block_sum16(__builtin_fmaf(ln_n * dm, dm, ln_q), red, parity) * a.inv_H;
+            mean = pivot + ms;
+        } else {
+            var = block_sum16(q, red, parity) * a.inv_H;
+        }
+        const float rstd = rsqrt_pos(var + a.eps);
+        if (tid == 0) {
+            if constexpr (OP == OP_LN) {
+                if (a.mean) a.mean[row] = mean;
+            }
+            if (a.rstd) a.rstd[row] = rstd;
+        }
+        // ---- pass 2: outputs
+        const rsrc_t ry = make_rsrc((T *)a.y + row * a.ldy, nb);
+        const rsrc_t rh = make_rsrc(OP == OP_FUSED ? (T *)a.h + row * a.ldh : (T *)a.y,
+                                    OP == OP_FUSED ? nb : 0u);
+        for (int s0 = 0; s0 < nseg; s0 += U) {
+            Raw cx[U][NIN];
+            RawW cg[U], cb[(OP == OP_LN) ? U : 1];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = (s0 + u) * SPAN + tid * VEC;
+                const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
+                if (cache) {
+#pragma unroll
+                    for (int i = 0; i < NIN; ++i) {
+                        if (e0 < H) lds_get<T, VEC>(lds + i * pad + off, cx[u][i]);
+                        else cx[u][i].zero();
+                    }
+                } else {
+                    cx[u][0].template bload<RN_LOAD_AUX>(rx, off);
+                    if constexpr (OP == OP_FUSED) cx[u][1].template bload<RN_LOAD_AUX>(rr, off);
+                }
+                const uint32_t woff = (uint32_t)(e0 * (int)sizeof(W));
+                cg[u].template bload<0>(rg, woff);
+                if constexpr (OP == OP_LN) cb[u].template bload<0>(rbt, woff);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t off = (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T));
+                float v[VEC], out[VEC];
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    v[k] = cx[u][0].get(k);
+                    if constexpr (OP == OP_FUSED) v[k] += cx[u][1].get(k);
+                }
+                // h in the same pass as y; every element of this lane's
+                // chunk was read before, so h may alias x or the residual
+                if constexpr (OP == OP_FUSED) bstore_chunk<VEC>((T *)nullptr, rh, off, v);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    if constexpr (OP == OP_LN) {
+                        const float d = (v[k] - pivot) - ms;   // x - mean
+                        out[k] = __builtin_fmaf(d * rstd, cg[u].get(k), cb[u].get(k));
+                    } else {
+                        out[k] = (v[k] * rstd) * cg[u].get(k);
+                    }
+                }
+                bstore_chunk<VEC>((T *)nullptr, ry, off, out);
+            }
+        }
+    }
+}
+
+// Backward.  ACC: persistent grid, per-lane dgamma (and dbeta) accumulators
+// over all the workgroup's rows, written at the end as the workgroup's
+// float32 partial row (row-major: part[b*H + j], dbeta rows after
+// partial_stride(P)*H floats); rows of at most kLongAccMaxH elements.
+// Without ACC only dx is written and the column-sum kernel forms the
+// parameter gradients.  ADD: the fused add+RMSNorm backward (a.add, if set,
+// is added to dx; a.dx2, if set, receives dx as well).  `cache`: x and dy of
+// the row (two rows of long_row_pad bytes) wait in LDS between the passes.
+template <class T, class W, int VEC, bool LN, bool ADD, bool ACC>
+__global__ __launch_bounds__(kLongThreads) void bwd_long_kernel(const BwdArgs a, int cache) {
+    static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
+    using Raw = RawChunk<T, VEC>;
+    using RawW = RawChunk<W, VEC>;
+    // with accumulators, two segments in flight (registers)
+    constexpr int U = ACC ? 2 : RN_LONG_UNROLL;
+    constexpr int SPAN = kLongThreads * VEC;
+    constexpr int MAXSEG = ACC ? kLongAccMaxH / SPAN : 1;
+    static_assert(!ACC || MAXSEG % U == 0, "whole segment groups");
+    constexpr int EA = ACC ? MAXSEG * VEC : 1;
+    extern __shared__ f32x4 lds_cache[];
+    __shared__ float red[2 * 16];
+    unsigned char *lds = (unsigned char *)lds_cache;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int nseg = (H + SPAN - 1) / SPAN;
+    const uint32_t pad = long_row_pad(H, (int)sizeof(T));
+    const uint32_t nb = (uint32_t)H * (uint32_t)sizeof(T);
+    const rsrc_t rg = make_rsrc(a.gamma, (uint32_t)H * (uint32_t)sizeof(W));
+    const T *addb = (const T *)a.add;
+    const bool has_add = ADD && addb != nullptr;
+    int parity = 0;
+
+    float adg[EA], adb[(ACC && LN) ? EA : 1];
+#pragma unroll
+    for (int e = 0; e < EA; ++e) adg[e] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < ((ACC && LN) ? EA : 1); ++e) adb[e] = 0.0f;
+
+    for (int64_t row = blockIdx.x; row < a.N; row += gridDim.x) {
+        const rsrc_t rx = make_rsrc((const T *)a.x + row * a.ldx, nb);
+        const rsrc_t rdy = make_rsrc((const T *)a.dy + row * a.lddy, nb);
+        const float mu = LN ? a.mean[row] : 0.0f;
+        const float s = a.rstd[row];
+        float sg = 0.0f, sgx = 0.0f;
+        // ---- pass 1: the row sums (and the accumulators, and the LDS copy)
+        auto pass1 = [&](const int s0) {
+            Raw cx[U], cd[U];
+            RawW cg[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = (s0 + u) * SPAN + tid * VEC;
+                const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
+                cx[u].template bload<RN_LOAD_AUX>(rx, off);
+                cd[u].template bload<RN_LOAD_AUX>(rdy, off);
+                cg[u].template bload<0>(rg, (uint32_t)(e0 * (int)sizeof(W)));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = (s0 + u) * SPAN + tid * VEC;
+                if (cache && e0 < H) {
+                    const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
+                    lds_put<T, VEC>(lds + off, cx[u]);
+                    lds_put<T, VEC>(lds + pad + off, cd[u]);
+                }
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float dyv = cd[u].get(k);
+                    const float xhat = (cx[u].get(k) - mu) * s;
+                    const float gv = dyv * cg[u].get(k);
+                    sg += gv;
+                    sgx = __builtin_fmaf(gv, xhat, sgx);
+                    if constexpr (ACC) {
+                        const int e = (s0 + u) * VEC + k;   // constant: s0 is unrolled
+                        adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
+                        if constexpr (LN) adb[e] += dyv;
+                    }
+                }
+            }
+        };
+        if constexpr (ACC) {
+#pragma unroll
+            for (int s0 = 0; s0 < MAXSEG; s0 += U)
+                if (s0 < nseg) pass1(s0);
+        } else {
+            for (int s0 = 0; s0 < nseg; s0 += U) pass1(s0);
+        }
+        const float c1 = LN ? block_sum16(sg, red, parity) * a.inv_H : 0.0f;
+        const float c2 = block_sum16(sgx, red, parity) * a.inv_H;
+        // LayerNorm: dx = rstd*g + (x_hat*(-c2*rstd) + (-c1*rstd))
+        const float k2 = -c2 * s, k1 = -c1 * s;
+        // ---- pass 2: dx
+        const rsrc_t rdx = make_rsrc((T *)a.dx + row * a.lddx, nb);
+        const rsrc_t rad = make_rsrc(has_add ? addb + row * a.ldadd : (const T *)a.x,
+                                     has_add ? nb : 0u);
+        const bool two = ADD && a.dx2 != nullptr;
+        const rsrc_t rdx2 = make_rsrc(two ? (T *)a.dx2 + row * a.lddx2 : (T *)a.dx,
+                                      two ? nb : 0u);
+        for (int s0 = 0; s0 < nseg; s0 += U) {
+            Raw cx[U], cd[U], ca[ADD ? U : 1];
+            RawW cg[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = (s0 + u) * SPAN + tid * VEC;
+                const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
+                if (cache) {
+                    if (e0 < H) {
+                        lds_get<T, VEC>(lds + off, cx[u]);
+                        lds_get<T, VEC>(lds + pad + off, cd[u]);
+                    } else {
+                        cx[u].zero();
+                        cd[u].zero();
+                    }
+                } else {
+                    cx[u].template bload<RN_LOAD_AUX>(rx, off);
+                    cd[u].template bload<RN_LOAD_AUX>(rdy, off);
+                }
+                cg[u].template bload<0>(rg, (uint32_t)(e0 * (int)sizeof(W)));
+                if constexpr (ADD) ca[u].template bload<RN_LOAD_AUX>(rad, off);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t off =
+                    (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T));
+                float dx[VEC];
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float xhat = (cx[u].get(k) - mu) * s;
+                    const float t = cd[u].get(k) * cg[u].get(k);
+                    if constexpr (LN) dx[k] = __builtin_fmaf(t, s, __builtin_fmaf(xhat, k2, k1));
+                    else dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
+                    if constexpr (ADD) {
+                        if (has_add) dx[k] += ca[u].get(k);
+                    }
+                }
+                bstore_chunk<VEC>((T *)nullptr, rdx, off, dx);
+                if constexpr (ADD) bstore_chunk<VEC>((T *)nullptr, rdx2, off, dx);
+            }
+        }
+    }
+
+    if constexpr (ACC) {
+        float *pg = a.part + (int64_t)blockIdx.x * H;
+        float *pb = a.part + (int64_t)partial_stride(gridDim.x) * H + (int64_t)blockIdx.x * H;
+#pragma unroll
+        for (int sg_ = 0; sg_ < MAXSEG; ++sg_) {
+            const int col = sg_ * SPAN + tid * VEC;
+            if (col < H) {
+                store_f32s<VEC>(pg + col, adg + sg_ * VEC);
+                if constexpr (LN) store_f32s<VEC>(pb + col, adb + sg_ * VEC);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launches --
+// Dynamic LDS the cache of `rows` rows of H elements of T needs, or 0 when
+// it does not fit in `budget` bytes.
+inline int long_cache_bytes(int H, int esize, int rows, int budget) {
+    const int64_t b = (int64_t)rows * long_row_pad(H, esize);
+    return b <= budget ? (int)b : 0;
+}
+
+// Allow kernel K up to `bytes` of dynamic LDS (once per kernel).
+template <auto K>
+inline void allow_lds(int bytes) {
+    static std::atomic<int> done{0};
+    if (bytes > 0 && done.load(std::memory_order_relaxed) < bytes) {
+        if (hipFuncSetAttribute((const void *)K, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                bytes) == hipSuccess)
+            done.store(bytes, std::memory_order_relaxed);
+    }
+}
+
+template <class T, class W, int VEC, int OP>
+hipError_t launch_fwd_long_op(const FwdArgs &a, hipStream_t s) {
+    constexpr auto k = fwd_long_kernel<T, W, VEC, OP>;
+    constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;
+    const int lds = long_cache_bytes(a.H, (int)sizeof(T), NIN, long_lds_budget());
+    allow_lds<k>(lds);
+    const int64_t grid = a.N < (1 << 20) ? a.N : (1 << 20);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kLongThreads), lds, s, a, lds > 0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <class T, class W, int VEC>
+hipError_t launch_fwd_long(int op, const FwdArgs &a, hipStream_t s) {
+    switch (op) {
+    case OP_LN: return launch_fwd_long_op<T, W, VEC, OP_LN>(a, s);
+    case OP_RMS: return launch_fwd_long_op<T, W, VEC, OP_RMS>(a, s);
+    default: return launch_fwd_long_op<T, W, VEC, OP_FUSED>(a, s);
+    }
+}
+
+// The long-row backward's partial-row count: one persistent workgroup per
+// CU (at most one row each).
+inline int bwd_long_partials(int64_t N, int cus) {
+    return (int)(N < cus ? N : cus);
+}
+
+template <class T, class W, int VEC, bool LN, bool ADD>
+hipError_t launch_bwd_long_t(const BwdArgs &a, int P, bool colsum, void *dg, void *db,
+                             hipStream_t s) {
+    const int lds = long_cache_bytes(a.H, (int)sizeof(T), 2, long_lds_budget());
+    if (!colsum) {
+        constexpr auto k = bwd_long_kernel<T, W, VEC, LN, ADD, true>;
+        allow_lds<k>(lds);
+        if (P > 0) {
+            hipLaunchKernelGGL(k, dim3(P), dim3(kLongThreads), lds, s, a, lds > 0 ? 1 : 0);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return launch_bwd2<W>(a.part, P, a.H, LN, dg, db, s);
+    }
+    constexpr auto k = bwd_long_kernel<T, W, VEC, LN, ADD, false>;
+    allow_lds<k>(lds);
+    const int64_t grid = a.N < (1 << 20) ? a.N : (1 << 20);
+    if (grid > 0) {
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kLongThreads), lds, s, a,
+                           lds > 0 ? 1 : 0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int COLS = 8 * VEC;
+    hipLaunchKernelGGL((bwd_colsum_kernel<T, W, VEC, LN>), dim3((a.H + COLS - 1) / COLS),
+                       dim3(1024), 0, s, a, (W *)dg, (W *)db);
+    return hipGetLastError();
+}
+
+template <class T, class W, int VEC>
+hipError_t launch_bwd_long(bool ln, bool fused, const BwdArgs &a, int P, bool colsum,
+                           void *dg, void *db, hipStream_t s) {
+    if (ln) return launch_bwd_long_t<T, W, VEC, true, false>(a, P, colsum, dg, db, s);
+    if (fused) return launch_bwd_long_t<T, W, VEC, false, true>(a, P, colsum, dg, db, s);
+    return launch_bwd_long_t<T, W, VEC, false, false>(a, P, colsum, dg, db, s);
+}
+
+}  // namespace rn

@@ -10,6 +10,7 @@
 #include <initializer_list>
 
 #include "rn_kernels.h"
+#include "rn_long.h"
 #include "rn_seg.h"
 
 namespace rn {
@@ -228,9 +229,14 @@ using BwdPlansScalar = PlanList<SegPlan<1, 8, 4, 1>,   //     8
                                 Plan<1, 4, 16, 1>,  //  4096
                                 Plan<1, 8, 16, 1>>; //  8192
 
+// Rows past the register plans (is_long_row) walk their row in segments:
+// 16-byte chunks on the vector path, single elements otherwise.
 template <class T, class W, class VecPlans>
 hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
                         hipStream_t s) {
+    if (is_long_row(a.H, vec))
+        return vec ? launch_fwd_long<T, W, Vec16<T>::N>(op, a, s)
+                   : launch_fwd_long<T, W, 1>(op, a, s);
     auto f = [&]<class P>() { return launch_fwd_any<T, W, P>(op, a, cus, s); };
     return vec ? pick_plan(VecPlans{}, a.H, f)
                : pick_plan(FwdPlansScalar{}, a.H, f);
@@ -238,6 +244,7 @@ hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
 
 template <class T, class W, class VecPlans>
 int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
+    if (is_long_row(H, vec)) return bwd_long_partials(N, cus);
     auto f = [&]<class P>() { return bwd_grid_any<T, W, P>(N, H, cus); };
     return vec ? pick_plan_int(VecPlans{}, H, f)
                : pick_plan_int(BwdPlansScalar{}, H, f);
@@ -246,6 +253,9 @@ int bwd_partials_t(int64_t N, int H, bool vec, int cus) {
 template <class T, class W, class VecPlans>
 hipError_t launch_bwd_t(bool ln, bool fused, const BwdArgs &a, bool vec, int P,
                         bool colsum, int cus, void *dg, void *db, hipStream_t s) {
+    if (is_long_row(a.H, vec))
+        return vec ? launch_bwd_long<T, W, Vec16<T>::N>(ln, fused, a, P, colsum, dg, db, s)
+                   : launch_bwd_long<T, W, 1>(ln, fused, a, P, colsum, dg, db, s);
     auto f = [&]<class Pl>() {
         return launch_bwd_any<T, W, Pl>(ln, fused, a, P, colsum, cus, dg, db, s);
     };

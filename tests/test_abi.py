@@ -72,12 +72,13 @@ def test_status_strings(L):
     assert L.rn_status_str(12345).decode() == "unknown status"
 
 
+MAXH = 1 << 22
+
+
 def test_max_hidden(L):
-    assert L.rn_max_hidden(BF16, 1) == 16384
-    assert L.rn_max_hidden(F32, 1) == 16384
-    assert L.rn_max_hidden(BF16, 0) == 8192
-    for dt in (F16, BF16_F32W, F16_F32W):
-        assert L.rn_max_hidden(dt, 1) == 16384
+    for dt in (F32, BF16, F16, BF16_F32W, F16_F32W):
+        assert L.rn_max_hidden(dt, 1) == MAXH
+        assert L.rn_max_hidden(dt, 0) == MAXH
     assert L.rn_max_hidden(9, 1) == 0
     assert L.rn_max_hidden(5, 1) == 0
 
@@ -97,7 +98,8 @@ def ln_fwd(L, x=X, ldx=1024, g=G, b=B, y=Y, ldy=1024, m=M, r=R, N=8,
     (dict(eps=float("nan")), EINVAL), (dict(eps=float("inf")), EINVAL),
     (dict(eps=1e-40), EINVAL),               # subnormal in binary32
     (dict(dt=7), EDTYPE), (dict(H=0), EINVAL), (dict(N=-1), EINVAL),
-    (dict(H=16385, ldx=16385, ldy=16385), EUNSUP),
+    (dict(H=MAXH + 1, ldx=MAXH + 1, ldy=MAXH + 1), EUNSUP),
+    (dict(H=MAXH + 8, ldx=MAXH + 8, ldy=MAXH + 8), EUNSUP),
     (dict(ldx=1000), EINVAL), (dict(ldy=1023), EINVAL),
     (dict(x=None), EINVAL), (dict(g=None), EINVAL), (dict(y=None), EINVAL),
     (dict(x=X + 1), EINVAL),                 # bf16 pointer not 2-aligned
@@ -110,8 +112,8 @@ def ln_fwd(L, x=X, ldx=1024, g=G, b=B, y=Y, ldy=1024, m=M, r=R, N=8,
     (dict(N=0, b=None, m=None, r=None), OK),
     (dict(N=0, x=None, y=None), OK),         # torch gives NULL for 0 rows
     (dict(N=0, g=None), EINVAL),             # gamma is always required
-    # odd H cannot use 16-byte rows; the element-wise path stops at 8192
-    (dict(H=8193, ldx=8193, ldy=8193), EUNSUP),
+    (dict(N=0, H=MAXH, ldx=MAXH, ldy=MAXH), OK),        # the longest row
+    (dict(N=0, H=8193, ldx=8193, ldy=8193), OK),        # long odd rows too
 ])
 def test_ln_fwd_argument_errors(L, kw, want):
     assert ln_fwd(L, **kw) == want
@@ -165,7 +167,7 @@ def ln_bwd(L, dy=DY, lddy=1024, x=X, ldx=1024, g=G, m=M, r=R, dx=DX,
     (dict(dg=DB), EOVERLAP), (dict(w=X), EOVERLAP),
     (dict(dg=G), EOVERLAP),
     (dict(eps=0.0), EINVAL), (dict(dt=5), EDTYPE),
-    (dict(H=16385, lddy=16385, ldx=16385, lddx=16385), EUNSUP),
+    (dict(H=MAXH + 1, lddy=MAXH + 1, ldx=MAXH + 1, lddx=MAXH + 1), EUNSUP),
     (dict(lddx=1000), EINVAL),
 ])
 def test_ln_bwd_argument_errors(L, kw, want):
@@ -224,8 +226,8 @@ def fused_bwd(L, dy=DY, lddy=1024, h=H_, ldh=1024, g=G, r=R, dh=DH, lddh=1024,
     (dict(dh=DH + 1), EINVAL), (dict(dres=RES + 1), EINVAL),
     (dict(lddh=1000), EINVAL), (dict(lddres=512), EINVAL),
     (dict(eps=0.0), EINVAL), (dict(dt=5), EDTYPE),
-    (dict(H=16385, lddy=16385, ldh=16385, lddx=16385, lddh=16385,
-          lddres=16385), EUNSUP),
+    (dict(H=MAXH + 1, lddy=MAXH + 1, ldh=MAXH + 1, lddx=MAXH + 1, lddh=MAXH + 1,
+          lddres=MAXH + 1), EUNSUP),
 ])
 def test_fused_bwd_argument_errors(L, kw, want):
     assert fused_bwd(L, **kw) == want

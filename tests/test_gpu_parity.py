@@ -696,16 +696,121 @@ def test_graph_capture_replays(N, H):
 
 
 def test_unsupported_sizes():
-    g = torch.ones(16385, dtype=torch.bfloat16, device=DEV)
-    x = torch.ones((2, 16385), dtype=torch.bfloat16, device=DEV)
+    H = (1 << 22) + 8          # past the longest supported row
+    g = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    x = torch.ones((2, H), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(rn.RowNormError) as ei:
         rn.rms_fwd(x, g, 1e-5)
     assert ei.value.status == -6
-    # odd H above the element-wise limit
-    x = torch.ones((2, 8193), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(rn.RowNormError) as ei:
-        rn.rms_fwd(x, g[:8193], 1e-5)
+        rn.workspace_bytes(2, H, torch.bfloat16, True)
     assert ei.value.status == -6
+
+
+# Rows past the register plans (16-byte path above 16384 elements, the
+# element-wise path above 8192): one workgroup per row walks it in segments,
+# caching it in LDS between the passes where it fits (160 KiB on MI355X),
+# reading it again otherwise; the backward writes partial rows for rows of up
+# to 32768 elements when N makes them pay, else column sums.  Cases:
+#   (600, 20480, bf16)     16-byte path, LDS cache, partial rows
+#   (37, 32768, bf16)      cache (x and dy: 128 KiB), column sums (few rows)
+#   (300, 32768, bf16/f32) float32 parameters; RMS partial rows, LN column sums
+#   (3, 49152, bf16)       forward cached, backward read twice, column sums
+#   (5, 98304, bf16)       nothing cached (192 KiB rows), column sums
+#   (600, 24576, f32)      float32 rows: forward cached, backward read twice
+#                          with partial rows
+#   (50, 40000, f32)       LN/RMS forward cached (156 KiB), fused not
+#   (300, 8193, bf16)      element-wise path (odd H), cache, RMS partial rows
+#   (600, 12002, f16)      element-wise path (rows not 16-byte multiples),
+#                          partial rows with 12 segments of accumulators
+LONG = [(600, 20480, "bf16"), (37, 32768, "bf16"), (300, 32768, "bf16/f32"),
+        (3, 49152, "bf16"), (5, 98304, "bf16"), (600, 24576, "f32"),
+        (50, 40000, "f32"), (300, 8193, "bf16"), (600, 12002, "f16")]
+
+
+@pytest.mark.parametrize("N,H,storage", LONG)
+def test_long_rows(orc, N, H, storage):
+    """LN, RMS and fused forward and backward against the oracle on every
+    element, and bit for bit the same run to run."""
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(80 + H % 97, N, H, dtype, wdtype=wdt or None)
+    print(f"long rows N={N} H={H} {storage}", flush=True)
+    check_ln_fwd(orc, arr, dtype, 1e-5)
+    check_rms_fwd(orc, arr, dtype, 1e-5)
+    xf, rf, gf = (to_dev(arr[k], dtype) for k in ("x", "residual", "gamma"))
+    yf, hf, rsf = rn.fused_add_rms_fwd(xf, rf, gf, 1e-5)
+    torch.cuda.synchronize()
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(
+        orc.decode(arr["x"], dtype), orc.decode(arr["residual"], dtype),
+        dec(orc, arr, "gamma", dtype), oracle.eps_at_boundary(1e-5))
+    assert np.array_equal(host(hf), orc.encode(h_o, dtype)), "h not RNE(x + r)"
+    tol.check_out(host(yf), y_o, dtype, orc, f"edge: long fused y {dtype}", strict=True)
+    tol.check_rstd(host(rsf), r_o, "edge: long fused rstd")
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
+    check_fused_bwd(orc, arr, dtype, 1e-5)
+    x, dy, g, dh = (to_dev(arr[k], dtype) for k in ("x", "dy", "gamma", "dh"))
+
+    def run():
+        _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+        _, rs2 = rn.rms_fwd(x, g, 1e-5)
+        dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5)
+        dx2, dg2 = rn.rms_bwd(dy, x, g, rs2, 1e-5)
+        dx3, dr3, dg3 = rn.fused_add_rms_bwd(dy, x, g, rs2, 1e-5, dh_in=dh,
+                                             write_dres=True)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (mean, rstd, rs2, dx, dg, db, dx2, dg2, dx3, dr3, dg3)]
+
+    for a_, b_ in zip(run(), run()):
+        assert torch.equal(a_, b_), "not reproducible run to run"
+
+
+@pytest.mark.parametrize("H,pad", [(20480, 24), (20480, 3), (40960, 8)])
+def test_long_rows_strided_in_place(orc, H, pad):
+    """Long rows at a row stride of H + pad (pad 3: the element-wise path):
+    the padding and a guard row stay untouched; the fused forward writes h
+    over x (at 40960 the fused rows do not fit in LDS, so x is read twice and
+    h may only be written in the second pass)."""
+    N = 7
+    arr = synth.custom(21, N, H, "bf16")
+    SENT = -7.0
+
+    def buf(a=None):
+        t = torch.full((N + 1, H + pad), SENT, dtype=torch.bfloat16, device=DEV)
+        if a is not None:
+            t[:N, :H] = to_dev(a)
+        return t
+
+    def view(t):
+        return t.as_strided((N, H), (H + pad, 1))
+
+    X, DY, R = buf(arr["x"]), buf(arr["dy"]), buf(arr["residual"])
+    Y, DX, Y2 = buf(), buf(), buf()
+    g, b = to_dev(arr["gamma"]), to_dev(arr["beta"])
+    _, mean, rstd = rn.ln_fwd(view(X), g, b, 1e-5, y=view(Y))
+    rn.ln_bwd(view(DY), view(X), g, mean, rstd, 1e-5, dx=view(DX))
+    torch.cuda.synchronize()
+    e = oracle.eps_at_boundary(1e-5)
+    xd = orc.decode(arr["x"], "bf16")
+    gd, bd = orc.decode(arr["gamma"], "bf16"), orc.decode(arr["beta"], "bf16")
+    y_o, _, _ = orc.ln_fwd(xd, gd, bd, e)
+    tol.check_out(host(Y[:N, :H].contiguous()), y_o, "bf16", orc, "edge: long strided LN y")
+    dyd = orc.decode(arr["dy"], "bf16")
+    dx_o, _, _, _, r_o = orc.ln_bwd(dyd, xd, gd, e)
+    tol.check_out(host(DX[:N, :H].contiguous()), dx_o, "bf16", orc, "edge: long strided dx",
+                  term_scale=tol.dx_term_scale(dyd, gd, r_o))
+    # fused, h over x
+    rn.fused_add_rms_fwd(view(X), view(R), g, 1e-6, y=view(Y2), h=view(X))
+    torch.cuda.synchronize()
+    y3_o, h_o, _ = orc.fused_add_rms_fwd(xd, orc.decode(arr["residual"], "bf16"), gd,
+                                         oracle.eps_at_boundary(1e-6))
+    assert np.array_equal(host(X[:N, :H].contiguous()), orc.bf16_encode(h_o))
+    tol.check_out(host(Y2[:N, :H].contiguous()), y3_o, "bf16", orc,
+                  "edge: long in-place fused y", strict=True)
+    for t, name in ((X, "h"), (Y, "y"), (DX, "dx"), (Y2, "fused y")):
+        hb = t.float().cpu().numpy()
+        assert np.all(hb[:N, H:] == SENT), f"{name}: row padding written"
+        assert np.all(hb[N, :] == SENT), f"{name}: guard row written"
 
 
 def test_workspace_errors():

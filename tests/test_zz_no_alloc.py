@@ -76,9 +76,22 @@ def test_noalloc_matches_workspace_entry_point(orc, first, second):
 
 
 def test_noalloc_rejects_what_does_not_fit():
-    """The array holds RN_NOALLOC_MAX_WORKSPACE_BYTES; the query says what a
-    shape needs, and every supported shape on this device fits."""
+    """The array holds RN_NOALLOC_MAX_WORKSPACE_BYTES: every register-plan
+    shape fits; a long-row shape whose LayerNorm partial rows need more
+    (600 x 32768: 256 partial rows of 32768 floats, twice) is refused with
+    RN_EWORKSPACE, leaving the outputs untouched."""
     bf = torch.bfloat16
     cap = 32 << 20
     for H in (1024, 2048, 4096, 8192, 16384):
         assert rn.workspace_bytes(1 << 20, H, bf, True) <= cap
+    N, H = 600, 32768
+    assert rn.workspace_bytes(N, H, bf, True) > cap
+    x = torch.randn(N, H, device=DEV).to(bf)
+    g = torch.ones(H, dtype=bf, device=DEV)
+    _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+    dx = torch.full((N, H), 3.0, dtype=bf, device=DEV)
+    with pytest.raises(rn.RowNormError) as ei:
+        rn.ln_bwd_noalloc(x, x, g, mean, rstd, 1e-5, dx=dx)
+    assert ei.value.status == -4
+    torch.cuda.synchronize()
+    assert torch.all(dx == 3.0), "a refused call wrote its output"
