@@ -41,9 +41,9 @@ rotating copies that its data comes from HBM.  --shapes-only NAME[,NAME]
 (or all) times just those and prints their table.
 
 decode (not in the step): the latency regime of a few rows (N = 1, 16, 64
-at H = 4096, bf16, data in cache): 50 back-to-back calls captured in one HIP
-graph and replayed, GPU time per call (launch gaps included, host overhead
-excluded).
+at H = 4096, bf16, data in cache), every op, forward and backward: 50
+back-to-back calls captured in one HIP graph and replayed, GPU time per call
+(launch gaps included, host overhead excluded).
 """
 import argparse
 import json
@@ -358,22 +358,37 @@ def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24, only_ops=None):
 
 
 def decode_latency(rn, dev, H=4096, Ns=(1, 16, 64), K=50, reps=5):
-    """us per call of the forward ops at decode-size N, from graph replays."""
+    """us per call of every op at decode-size N, from graph replays (data in
+    cache, so this is the launch-bound regime: kernels plus the gaps between
+    them)."""
     import torch
     bf = torch.bfloat16
     out = {}
     for N in Ns:
         x = torch.randn(N, H, device=dev).to(bf)
         r = torch.randn(N, H, device=dev).to(bf)
+        dy = torch.randn(N, H, device=dev).to(bf)
         g = (1 + 0.1 * torch.randn(H, device=dev)).to(bf)
-        y, h = torch.empty_like(x), torch.empty_like(x)
+        y, h, dx = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
         rstd = torch.empty(N, dtype=torch.float32, device=dev)
+        mean = torch.empty(N, dtype=torch.float32, device=dev)
+        dg, db = torch.empty_like(g), torch.empty_like(g)
+        rn.ln_fwd(x, g, None, 1e-6, y=y, mean=mean, rstd=rstd)
+        ws = torch.empty(max(1, rn.workspace_bytes(N, H, bf, True),
+                             rn.workspace_bytes(N, H, bf, False)),
+                         dtype=torch.uint8, device=dev)
         ops = {
             "rms_fwd": lambda: rn.rms_fwd(x, g, 1e-6, y=y, rstd=rstd),
             "ln_fwd": lambda: rn.ln_fwd(x, g, None, 1e-6, y=y, rstd=rstd,
                                         save_stats=False),
             "fused_add_rms_fwd": lambda: rn.fused_add_rms_fwd(x, r, g, 1e-6, y=y,
                                                               h=h, rstd=rstd),
+            "ln_bwd": lambda: rn.ln_bwd(dy, x, g, mean, rstd, 1e-6, dx=dx, dgamma=dg,
+                                        dbeta=db, workspace=ws),
+            "rms_bwd": lambda: rn.rms_bwd(dy, x, g, rstd, 1e-6, dx=dx, dgamma=dg,
+                                          workspace=ws),
+            "fused_add_rms_bwd": lambda: rn.fused_add_rms_bwd(
+                dy, h, g, rstd, 1e-6, dh_in=r, dx=dx, dgamma=dg, workspace=ws),
         }
         for name, f in ops.items():
             f()
@@ -484,6 +499,8 @@ def main():
                          "those, print their table as the JSON line, no step")
     ap.add_argument("--ops", default=None,
                     help="with --shapes-only: comma list of the ops to time")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode-size table and print it")
     ap.add_argument("--calib-copy", action="store_true",
                     help="with --shapes-only: also run one 1 GiB rn_copy (the "
                          "known-size kernel that calibrates byte counters)")
@@ -504,6 +521,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode_only:
+        print(json.dumps({"decode_us_per_call": decode_latency(rn, dev)}), flush=True)
+        return
     if args.shapes_only:
         names = None if args.shapes_only == "all" else args.shapes_only.split(",")
         only = None if not args.ops else args.ops.split(",")

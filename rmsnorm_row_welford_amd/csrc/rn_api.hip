@@ -283,6 +283,8 @@ static int workspace_bytes_here(int64_t N, int64_t H, int dtype, int is_layernor
         if (bwd_force_colsum(H, v == 0) ||
             bwd_use_colsum(N, (int)H, e, P, is_layernorm != 0, cus))
             continue;
+        // one workgroup of a register plan writes dgamma/dbeta itself
+        if (P == 1 && !is_long_row(H, v == 0)) continue;
         const size_t b = (size_t)partial_stride(P) * (size_t)H * sizeof(float) *
                          (is_layernorm ? 2 : 1);
         if (b > need) need = b;
@@ -374,13 +376,18 @@ static int bwd_common(bool ln, bool fused, const void *dy, int64_t lddy,
     if (P < 0) return RN_EUNSUPPORTED;
     const bool colsum =
         N > 0 && (bwd_force_colsum(H, vec) || bwd_use_colsum(N, (int)H, (int)e, P, ln, cus));
-    const size_t need =
-        colsum ? 0 : (size_t)partial_stride(P) * (size_t)H * sizeof(float) * (ln ? 2 : 1);
+    // no partial rows: the column sums, or one workgroup of a register plan
+    // (kernel 1 then writes dgamma/dbeta itself)
+    const bool no_partials = colsum || (P == 1 && !is_long_row(H, vec));
+    const size_t need = no_partials ? 0
+                                    : (size_t)partial_stride(P) * (size_t)H * sizeof(float) *
+                                          (ln ? 2 : 1);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RN_EWORKSPACE;
 
     BwdArgs a{};
     a.dy = dy; a.x = x; a.gamma = gamma; a.mean = mean; a.rstd = rstd;
     a.dx = dx; a.part = (float *)workspace; a.add = add; a.dx2 = dx2;
+    a.dgamma = dgamma; a.dbeta = dbeta;
     a.lddy = lddy; a.ldx = ldx; a.lddx = lddx; a.ldadd = ldadd; a.lddx2 = lddx2;
     a.N = N; a.H = (int)H; a.inv_H = 1.0f / (float)H;
     return hip_status(

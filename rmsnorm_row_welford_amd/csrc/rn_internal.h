@@ -44,6 +44,8 @@ struct BwdArgs {
     float *part;
     const void *add;
     void *dx2;
+    void *dgamma;   // written by kernel 1 itself when one workgroup holds every row
+    void *dbeta;
     int64_t lddy, ldx, lddx, ldadd, lddx2;
     int64_t N;
     int H;
@@ -114,6 +116,14 @@ RN_DECLARE_STORAGE(f16_f32w)
 #ifndef RN_BWD_COLSUM_PCT
 #define RN_BWD_COLSUM_PCT 50
 #endif
+// Rows each team of a backward workgroup may take before the grid grows
+// past one workgroup: with a single workgroup its partial row is already
+// the column sum, so kernel 1 writes dgamma/dbeta itself and the backward
+// is one launch (the few-row, latency-bound regime).
+#ifndef RN_BWD_DECODE_ROWS
+#define RN_BWD_DECODE_ROWS 4
+#endif
+
 inline bool bwd_use_colsum(int64_t N, int H, int e, int P, bool ln, int cus) {
     if (N <= 0 || P <= 0) return false;
     const int cols_per_tile = 8 * (16 / e);

@@ -506,8 +506,11 @@ __device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
 // leaves each wave 256 registers): gamma is widened once for the whole
 // loop and the float32 x_hat and g of a row are kept from the sums to the
 // dx pass; otherwise only the packed chunks are kept and widened again.
+// FINAL (a grid of one workgroup): the workgroup's sums are the column sums,
+// written straight to dgamma/dbeta in the parameter type (the same bits
+// kernel 2 would produce from the single partial row).
 template <class T, class W, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC,
-          bool ADD = false, bool KEEP = false>
+          bool ADD = false, bool KEEP = false, bool FINAL = false>
 __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     using Lay = Layout<VEC, CPL, TW>;
@@ -778,6 +781,16 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     // thread then adds a column over the teams in team order.
     if constexpr (!ACC) {
         return;
+    } else if constexpr (RT == 1 && FINAL) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            if (!L.valid(c)) continue;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                store_one((W *)a.dgamma + L.off(c) + k, adg[c * VEC + k]);
+                if constexpr (LN) store_one((W *)a.dbeta + L.off(c) + k, adb[c * VEC + k]);
+            }
+        }
     } else if constexpr (RT == 1) {
         float *pb = a.part + (int64_t)partial_stride(gridDim.x) * H;
         if (partial_colmajor(H)) {
@@ -817,7 +830,8 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
                 float t = accbuf[col];
 #pragma unroll
                 for (int tm = 1; tm < RT; ++tm) t += accbuf[tm * H + col];
-                dst[partial_index(blockIdx.x, gridDim.x, H, col)] = t;
+                if constexpr (FINAL) store_one((W *)(p == 0 ? a.dgamma : a.dbeta) + col, t);
+                else dst[partial_index(blockIdx.x, gridDim.x, H, col)] = t;
             }
             if (p + 1 < NV) __syncthreads();
         }
@@ -1084,6 +1098,7 @@ hipError_t launch_fwd_op(int op, const FwdArgs &a, int cus, hipStream_t s) {
 // occupancy, which keeps the workspace size independent of the norm.
 template <class T, class W, class P>
 inline int bwd_grid(int64_t N, int H, int cus) {
+    if (N <= (int64_t)P::RT * RN_BWD_DECODE_ROWS) return N > 0 ? 1 : 0;
     const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
     constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true,
                                    false, P::KEEP>;
@@ -1095,6 +1110,15 @@ inline int bwd_grid(int64_t N, int H, int cus) {
 template <class T, class W, class P, bool LN, bool ADD>
 hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *dg,
                          void *db, hipStream_t s) {
+    if (!colsum && P_ == 1) {
+        // one workgroup holds every row: kernel 1 writes dgamma/dbeta itself
+        const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
+        hipLaunchKernelGGL(
+            (bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD, P::KEEP,
+                         true>),
+            dim3(1), dim3(P::THREADS), lds, s, a);
+        return hipGetLastError();
+    }
     if (!colsum) {
         // partial rows: kernel 1 with the persistent grid P_, then kernel 2
         if (P_ > 0) {

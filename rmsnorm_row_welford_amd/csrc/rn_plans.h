@@ -76,6 +76,7 @@ template <class T, class W, class P>
 int bwd_grid_any(int64_t N, int H, int cus) {
     if constexpr (P::SEG > 0) {
         constexpr auto k = bwd1_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, true, false>;
+        if (N <= (int64_t)P::RPW * P::WPG * RN_BWD_DECODE_ROWS) return N > 0 ? 1 : 0;
         const int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU
                                              : resident_per_cu<k>(P::THREADS, 0);
         const int64_t groups = (N + P::RPW * P::WPG - 1) / (P::RPW * P::WPG);
@@ -88,6 +89,12 @@ int bwd_grid_any(int64_t N, int H, int cus) {
 
 template <class T, class W, class P, bool LN, bool ADD>
 hipError_t launch_bwd_seg(const BwdArgs &a, int P_, void *dg, void *db, hipStream_t s) {
+    if (P_ == 1) {
+        // one workgroup holds every row: kernel 1 writes dgamma/dbeta itself
+        hipLaunchKernelGGL((bwd1_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, LN, ADD, true>),
+                           dim3(1), dim3(P::THREADS), 0, s, a);
+        return hipGetLastError();
+    }
     if (P_ > 0) {
         hipLaunchKernelGGL((bwd1_seg_kernel<T, W, P::VEC, P::SEG, P::WPG, LN, ADD>),
                            dim3(P_), dim3(P::THREADS), 0, s, a);

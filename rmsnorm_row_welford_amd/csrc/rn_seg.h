@@ -224,7 +224,9 @@ void fwd_seg_kernel(const FwdArgs a) {
 // in segment order, into ONE float32 partial row (two for LayerNorm), as in
 // bwd1_kernel.  ADD: the fused add+RMSNorm variant (a.add added to dx, a.dx2
 // a second copy).
-template <class T, class W, int VEC, int SEG, int WPG, bool LN, bool ADD>
+// FINAL (a grid of one workgroup): the column sums go straight to
+// dgamma/dbeta in the parameter type, as in bwd1_kernel.
+template <class T, class W, int VEC, int SEG, int WPG, bool LN, bool ADD, bool FINAL = false>
 __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     constexpr int RPW = 64 / SEG;
@@ -324,8 +326,10 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
             const int fc = c0 + lane / SLOTS;
             const float v = fc < H ? acc[(lane % SLOTS) * SPAN + fc] : 0.0f;
             const float t = seg_sum<SLOTS>(v);
-            if (lane % SLOTS == 0 && fc < H)
-                dst[partial_index(blockIdx.x, gridDim.x, H, fc)] = t;
+            if (lane % SLOTS == 0 && fc < H) {
+                if constexpr (FINAL) store_one((W *)(p == 0 ? a.dgamma : a.dbeta) + fc, t);
+                else dst[partial_index(blockIdx.x, gridDim.x, H, fc)] = t;
+            }
         }
         __syncthreads();
     }
