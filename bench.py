@@ -430,9 +430,23 @@ def copy_ceiling(rn, dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(arr, eps, budget_s=20.0):
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and logical CPU count."""
+    name = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return name, os.cpu_count()
+
+
+def cpu_baseline(arr, eps, budget_s=12.0, budget_1t_s=8.0):
     """The oracle as it stands, on the host cores, on a bounded row sample of
-    the same workload; GB/s over the sample's algorithmic bytes."""
+    the same workload; GB/s over the sample's algorithmic bytes.  Timed with
+    the oracle's default OpenMP thread count, then with one thread."""
     import oracle
     orc = oracle.default()
     N, H = arr["x"].shape
@@ -462,19 +476,32 @@ def cpu_baseline(arr, eps, budget_s=20.0):
         orc.encode(dg, "bf16")
         return time.perf_counter() - t0
 
-    probe_rows = min(N, 1024)
-    per_row = one_pass(probe_rows) / probe_rows
-    rows = int(min(N, max(probe_rows, budget_s / 3.0 / max(per_row, 1e-9))))
-    t = float(np.median([one_pass(rows) for _ in range(3)]))
-    nbytes = sum(alg_bytes(rows, H, 2).values())
+    def measure(budget):
+        probe_rows = min(N, 256)
+        per_row = one_pass(probe_rows) / probe_rows
+        rows = int(min(N, max(probe_rows, budget / 3.0 / max(per_row, 1e-9))))
+        t = float(np.median([one_pass(rows) for _ in range(3)]))
+        return rows, t, sum(alg_bytes(rows, H, 2).values()) / t / 1e9
+
+    threads = orc.num_threads()
+    rows, t, gbs = measure(budget_s)
+    orc.set_threads(1)
+    rows1, t1, gbs1 = measure(budget_1t_s)
+    orc.set_threads(threads)
+    model, ncpu = cpu_model()
     return {
-        "value": nbytes / t / 1e9,
+        "value": gbs,
         "unit": "GB/s",
-        "cores": orc.num_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"{rows} of {N} rows x H={H}: the full five-op step (bf16 "
                   f"decode/encode included), median of 3 passes, "
-                  f"{t * 1e3:.1f} ms per pass",
+                  f"{t * 1e3:.1f} ms per pass on {threads} OpenMP threads",
+        "one_thread": {"value": gbs1, "unit": "GB/s", "cores": 1,
+                       "sample": f"{rows1} rows, median of 3 passes, "
+                                 f"{t1 * 1e3:.1f} ms per pass"},
+        "cpu_model": model,
+        "logical_cpus": ncpu,
     }
 
 

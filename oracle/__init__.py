@@ -44,6 +44,7 @@ _SIGNATURES = {
     "orc_f16_decode": [_P, _P, _i64],
     "orc_f16_encode": [_P, _P, _i64],
     "orc_num_threads": [],
+    "orc_set_threads": [ctypes.c_int],
 }
 
 
@@ -80,6 +81,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.orc_num_threads())
+
+    def set_threads(self, n: int) -> None:
+        """OpenMP threads for later calls (the CPU baseline's 1-thread run)."""
+        self.lib.orc_set_threads(int(n))
 
     # ------------------------------------------------------------ codec --
     def bf16_decode(self, bits):

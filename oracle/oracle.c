@@ -428,6 +428,17 @@ void orc_f32_encode(const double *in, float *out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = (float)in[i];
 }
 
+/* Threads the OpenMP loops use from now on (the CPU baseline's 1-thread
+ * run); n <= 0 leaves the setting unchanged. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -621,6 +621,28 @@ def test_row_counts(orc, N):
     check_fused_bwd(orc, arr, "bf16", 1e-5)
 
 
+@pytest.mark.parametrize("N", [1, 8, 9, 16, 64])
+def test_decode_sizes(orc, N):
+    """Few rows at H = 4096: N <= 8 runs the backward as one workgroup that
+    writes dgamma/dbeta itself (one launch), N = 9 just past it, 16 and 64
+    two launches; LN, RMS and fused backward against the oracle."""
+    arr = synth.custom(500 + N, N, 4096, "bf16")
+    check_ln_fwd(orc, arr, "bf16", 1e-5)
+    check_bwd(orc, arr, "bf16", 1e-5, layernorm=True)
+    check_bwd(orc, arr, "bf16", 1e-5, layernorm=False)
+    check_fused_bwd(orc, arr, "bf16", 1e-6)
+    if N <= 8:
+        # one workgroup: no workspace at all
+        assert rn.workspace_bytes(N, 4096, torch.bfloat16, True) == 0
+        x, dy, g = (to_dev(arr[k]) for k in ("x", "dy", "gamma"))
+        _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+        empty = torch.empty(0, dtype=torch.uint8, device=DEV)
+        dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5, workspace=empty)
+        dx2, dg2, db2 = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5)
+        torch.cuda.synchronize()
+        assert torch.equal(dx, dx2) and torch.equal(dg, dg2) and torch.equal(db, db2)
+
+
 def test_many_short_rows(orc):
     """Persistent loops with many iterations per workgroup."""
     N, H = 200003, 64
