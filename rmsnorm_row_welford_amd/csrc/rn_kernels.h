@@ -454,11 +454,13 @@ void fwd_kernel(const FwdArgs a) {
 // (b mod 8, as the dispatcher deals them out) take adjacent slots, so each
 // column's cache line is filled from one L2; slots no workgroup owns are
 // skipped.  Longer rows keep the partial rows row-major (part[slot * H + j],
-// slot = b): a workgroup's scattered column-major stores would touch more
-// lines than an L2 can merge, while kernel 2 finds enough columns to spread
-// over the CUs.  The dbeta partials follow at part + Pp * H.
+// slot = b): a workgroup's partial row then leaves in whole lines.  At 2048
+// the scattered 4-byte stores of the column-major layout cost the LayerNorm
+// backward 1.8 us at the end of kernel 1 (measured), and at 16384 they touch
+// more lines than an L2 can merge.  The dbeta partials follow at
+// part + Pp * H.
 #ifndef RN_PART_COLMAJOR_MAX_H
-#define RN_PART_COLMAJOR_MAX_H 4096
+#define RN_PART_COLMAJOR_MAX_H 1024
 #endif
 __host__ __device__ inline bool partial_colmajor(int H) {
     return H <= RN_PART_COLMAJOR_MAX_H;
@@ -877,19 +879,20 @@ __global__ __launch_bounds__(256) void bwd2_cols_kernel(const float *part, int P
     }
 }
 
-// Row-major partials: a workgroup of 1024 threads owns COLS columns; its
-// lanes form SLOTS = 1024/COLS row slots, slot j adding the contiguous
+// Row-major partials: a workgroup of THREADS threads owns COLS columns; its
+// lanes form SLOTS = THREADS/COLS row slots, slot j adding the contiguous
 // block of partial rows [j*R, (j+1)*R) (R = ceil(P / SLOTS)) in increasing
 // order with up to 32 loads in flight.  The slot sums meet in LDS, and each
 // column's SLOTS values are then added by one segment of SLOTS lanes with
-// the fixed segment-sum tree.
-template <class T, int COLS>
-__global__ __launch_bounds__(1024) void bwd2_rows_kernel(const float *part, int P,
-                                                        int H, T *dgamma, T *dbeta) {
-    constexpr int SLOTS = 1024 / COLS;
+// the fixed segment-sum tree.  Narrow rows take small tiles (16 columns per
+// 256 threads) so that the few columns still spread over many CUs.
+template <class T, int COLS, int THREADS = 1024>
+__global__ __launch_bounds__(THREADS) void bwd2_rows_kernel(const float *part, int P,
+                                                           int H, T *dgamma, T *dbeta) {
+    constexpr int SLOTS = THREADS / COLS;
     static_assert(SLOTS == 8 || SLOTS == 16 || SLOTS == 32, "column tile");
     constexpr int CPW = 64 / SLOTS;   // columns folded per wave
-    static_assert(COLS == 16 * CPW, "16 waves fold the tile");
+    static_assert(COLS == (THREADS / 64) * CPW, "the waves fold the tile");
     __shared__ float red[SLOTS][COLS];
     const int cl = threadIdx.x % COLS;
     const int slot = threadIdx.x / COLS;
@@ -923,6 +926,10 @@ __global__ __launch_bounds__(1024) void bwd2_rows_kernel(const float *part, int 
 #ifndef RN_BWD2_CPW
 #define RN_BWD2_CPW 1
 #endif
+// Longest row whose row-major partial rows kernel 2 sums in small tiles.
+#ifndef RN_BWD2_SMALL_H
+#define RN_BWD2_SMALL_H 2048
+#endif
 template <class T>
 hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void *db,
                        hipStream_t s) {
@@ -930,6 +937,9 @@ hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void 
     if (partial_colmajor(H))
         hipLaunchKernelGGL((bwd2_cols_kernel<T, RN_BWD2_CPW>),
                            dim3((H + 4 * RN_BWD2_CPW - 1) / (4 * RN_BWD2_CPW), np), dim3(256),
+                           0, s, part, P, H, (T *)dg, (T *)db);
+    else if (H <= RN_BWD2_SMALL_H)
+        hipLaunchKernelGGL((bwd2_rows_kernel<T, 16, 256>), dim3((H + 15) / 16, np), dim3(256),
                            0, s, part, P, H, (T *)dg, (T *)db);
     else
         hipLaunchKernelGGL((bwd2_rows_kernel<T, 64>), dim3((H + 63) / 64, np), dim3(1024),
