@@ -454,13 +454,14 @@ void fwd_kernel(const FwdArgs a) {
 // (b mod 8, as the dispatcher deals them out) take adjacent slots, so each
 // column's cache line is filled from one L2; slots no workgroup owns are
 // skipped.  Longer rows keep the partial rows row-major (part[slot * H + j],
-// slot = b): a workgroup's partial row then leaves in whole lines.  At 2048
-// the scattered 4-byte stores of the column-major layout cost the LayerNorm
-// backward 1.8 us at the end of kernel 1 (measured), and at 16384 they touch
-// more lines than an L2 can merge.  The dbeta partials follow at
-// part + Pp * H.
+// slot = b): a workgroup's partial row then leaves in whole lines, while in
+// the column-major layout the 32 workgroups of an XCD each write 4 bytes of
+// every line.  Measured: at 2048 row-major partials took 1.8 us off the
+// LayerNorm backward; at 1024 kernel 1 gains 0.5-0.75 us and kernel 2 loses
+// 0.4; at 16384 column-major stores touch more lines than an L2 can merge.
+// The dbeta partials follow at part + Pp * H.
 #ifndef RN_PART_COLMAJOR_MAX_H
-#define RN_PART_COLMAJOR_MAX_H 1024
+#define RN_PART_COLMAJOR_MAX_H 512
 #endif
 __host__ __device__ inline bool partial_colmajor(int H) {
     return H <= RN_PART_COLMAJOR_MAX_H;
