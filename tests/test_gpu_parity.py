@@ -748,9 +748,12 @@ def test_unsupported_sizes():
 #   (300, 8193, bf16)      element-wise path (odd H), cache, RMS partial rows
 #   (600, 12002, f16)      element-wise path (rows not 16-byte multiples),
 #                          partial rows with 12 segments of accumulators
+#   (1, 16392, bf16), (2, 8201, f32)  one or two rows just past the register
+#                          plans (16-byte and element-wise paths)
 LONG = [(600, 20480, "bf16"), (37, 32768, "bf16"), (300, 32768, "bf16/f32"),
         (3, 49152, "bf16"), (5, 98304, "bf16"), (600, 24576, "f32"),
-        (50, 40000, "f32"), (300, 8193, "bf16"), (600, 12002, "f16")]
+        (50, 40000, "f32"), (300, 8193, "bf16"), (600, 12002, "f16"),
+        (1, 16392, "bf16"), (2, 8201, "f32")]
 
 
 @pytest.mark.parametrize("N,H,storage", LONG)
