@@ -720,6 +720,84 @@ def test_graph_capture_replays(N, H):
             assert torch.equal(t, w_), f"replay {rep} differs from eager"
 
 
+def test_two_streams_at_once(orc):
+    """Backward calls on two streams at once, each with its own workspace
+    (the library keeps no per-call state): both results equal the same calls
+    made one after the other, and the first matches the oracle."""
+    shapes = [(32771, 1024), (4099, 4096)]
+    arrs = [synth.custom(600 + i, N, H, "bf16") for i, (N, H) in enumerate(shapes)]
+    ins = []
+    for a in arrs:
+        x, dy, g = (to_dev(a[k]) for k in ("x", "dy", "gamma"))
+        _, mean, rstd = rn.ln_fwd(x, g, None, 1e-5)
+        ins.append((x, dy, g, mean, rstd))
+    torch.cuda.synchronize()
+    want = [rn.ln_bwd(dy, x, g, m, r, 1e-5) for (x, dy, g, m, r) in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    for rep in range(3):
+        for i, st in enumerate(streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                x, dy, g, m, r = ins[i]
+                got[i] = rn.ln_bwd(dy, x, g, m, r, 1e-5, stream=st)
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a_, b_ in zip(want[i], got[i]):
+                assert torch.equal(a_, b_), f"stream {i}, repetition {rep}"
+    a = arrs[0]
+    e = oracle.eps_at_boundary(1e-5)
+    xd, dyd, gd = (orc.decode(a[k], "bf16") for k in ("x", "dy", "gamma"))
+    dx_o, dg_o, db_o, _, r_o = orc.ln_bwd(dyd, xd, gd, e)
+    tol.check_out(host(got[0][0]), dx_o, "bf16", orc, "edge: two streams LN dx",
+                  term_scale=tol.dx_term_scale(dyd, gd, r_o))
+    tol.check_param(orc.decode(host(got[0][1]), "bf16"), dg_o, "edge: two streams dgamma")
+
+
+@pytest.mark.parametrize("N,H", [(600, 20480), (37, 40960), (5, 4096), (3, 16384)])
+def test_graph_capture_long_and_one_workgroup(N, H):
+    """HIP graph capture of the long-row kernels (partial rows at 600 x 20480,
+    column sums at 37 x 40960) and of the one-launch backward of a few rows
+    (5 x 4096, 3 x 16384): replayed four times with eager work and
+    synchronizations between replays, every replay reproduces the eager
+    results bit for bit."""
+    arr = synth.custom(23, N, H, "bf16")
+    x, r, g, b, dy, dh = (to_dev(arr[k]) for k in ("x", "residual", "gamma", "beta",
+                                                   "dy", "dh"))
+    bf = torch.bfloat16
+    y, hh, dx, dx2, y2 = (torch.empty((N, H), dtype=bf, device=DEV) for _ in range(5))
+    rstd, mean, rstd2 = (torch.empty(N, dtype=torch.float32, device=DEV) for _ in range(3))
+    dg, dg2, db2 = (torch.empty(H, dtype=bf, device=DEV) for _ in range(3))
+    ws = torch.empty(max(1, rn.workspace_bytes(N, H, bf, True),
+                         rn.workspace_bytes(N, H, bf, False)), dtype=torch.uint8, device=DEV)
+
+    def step():
+        rn.fused_add_rms_fwd(x, r, g, 1e-6, y=y, h=hh, rstd=rstd)
+        rn.fused_add_rms_bwd(dy, hh, g, rstd, 1e-6, dh_in=dh, dx=dx, dgamma=dg,
+                             workspace=ws)
+        rn.ln_fwd(x, g, b, 1e-5, y=y2, mean=mean, rstd=rstd2)
+        rn.ln_bwd(dy, x, g, mean, rstd2, 1e-5, dx=dx2, dgamma=dg2, dbeta=db2,
+                  workspace=ws)
+
+    outs = (y, hh, rstd, dx, dg, y2, mean, rstd2, dx2, dg2, db2)
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, w_ in zip(outs, want):
+            assert torch.equal(t, w_), f"replay {rep} differs from eager"
+
+
 def test_unsupported_sizes():
     H = (1 << 22) + 8          # past the longest supported row
     g = torch.ones(H, dtype=torch.bfloat16, device=DEV)
