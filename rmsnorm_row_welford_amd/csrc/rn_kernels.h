@@ -499,6 +499,16 @@ __device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
 #ifndef RN_BWD_KEEP_MAXW
 #define RN_BWD_KEEP_MAXW 8
 #endif
+// LayerNorm teams park both accumulators in LDS at once at the end (one
+// barrier instead of three; twice the LDS).
+#ifndef RN_BWD_MERGE_ONCE
+#define RN_BWD_MERGE_ONCE 1
+#endif
+// Dynamic LDS floats of backward kernel 1 for a plan of RT teams (the
+// teams' accumulators meet there at the end).
+__host__ __device__ constexpr int bwd1_lds_floats(int RT, int H, bool ln) {
+    return RT > 1 ? RT * H * ((ln && RN_BWD_MERGE_ONCE) ? 2 : 1) : 0;
+}
 
 // ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
 // kernel only writes dx (the column-sum strategy computes the parameter
@@ -818,6 +828,34 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
                 if constexpr (LN) store_f32s<VEC>(pb + o + L.off(c), adb + c * VEC);
             }
         }
+    } else if constexpr (RN_BWD_MERGE_ONCE && NV == 2) {
+        // LayerNorm: both accumulators parked at once (2 * RT * H floats of
+        // LDS), one barrier, then both column sums
+        float *accbuf = (float *)acc_lds;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            if (L.valid(c)) {
+                store_f32s<VEC>(accbuf + team * H + L.off(c), adg + c * VEC);
+                store_f32s<VEC>(accbuf + (RT + team) * H + L.off(c), adb + c * VEC);
+            }
+        __syncthreads();
+        float *dst0 = a.part, *dst1 = a.part + (int64_t)partial_stride(gridDim.x) * H;
+        for (int col = threadIdx.x; col < H; col += 64 * TW * RT) {
+            float t0 = accbuf[col], t1 = accbuf[RT * H + col];
+#pragma unroll
+            for (int tm = 1; tm < RT; ++tm) {
+                t0 += accbuf[tm * H + col];
+                t1 += accbuf[(RT + tm) * H + col];
+            }
+            if constexpr (FINAL) {
+                store_one((W *)a.dgamma + col, t0);
+                store_one((W *)a.dbeta + col, t1);
+            } else {
+                const int64_t o = partial_index(blockIdx.x, gridDim.x, H, col);
+                dst0[o] = t0;
+                dst1[o] = t1;
+            }
+        }
     } else {
         float *accbuf = (float *)acc_lds;
 #pragma unroll
@@ -1110,7 +1148,7 @@ hipError_t launch_fwd_op(int op, const FwdArgs &a, int cus, hipStream_t s) {
 template <class T, class W, class P>
 inline int bwd_grid(int64_t N, int H, int cus) {
     if (N <= (int64_t)P::RT * RN_BWD_DECODE_ROWS) return N > 0 ? 1 : 0;
-    const int lds = P::RT > 1 ? P::RT * H * (int)sizeof(float) : 0;
+    const int lds = bwd1_lds_floats(P::RT, H, true) * (int)sizeof(float);
     constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, true, P::PF, true,
                                    false, P::KEEP>;
     int per_cu = RN_BWD_PER_CU > 0 ? RN_BWD_PER_CU : resident_per_cu<k>(P::THREADS, lds);
@@ -1123,7 +1161,7 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
                          void *db, hipStream_t s) {
     if (!colsum && P_ == 1) {
         // one workgroup holds every row: kernel 1 writes dgamma/dbeta itself
-        const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
+        const int lds = bwd1_lds_floats(P::RT, a.H, LN) * (int)sizeof(float);
         hipLaunchKernelGGL(
             (bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD, P::KEEP,
                          true>),
@@ -1133,7 +1171,7 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
     if (!colsum) {
         // partial rows: kernel 1 with the persistent grid P_, then kernel 2
         if (P_ > 0) {
-            const int lds = P::RT > 1 ? P::RT * a.H * (int)sizeof(float) : 0;
+            const int lds = bwd1_lds_floats(P::RT, a.H, LN) * (int)sizeof(float);
             hipLaunchKernelGGL(
                 (bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, true, ADD,
                              P::KEEP>),
