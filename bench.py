@@ -412,22 +412,52 @@ def decode_latency(rn, dev, H=4096, Ns=(1, 16, 64), K=50, reps=5):
     return out
 
 
-def copy_ceiling(rn, dev, nbytes=1 << 30, reps=5):
-    """Streaming copy bandwidth over rotating buffers (read + write bytes)."""
+def stream_ceilings(rn, dev, nbytes=64 << 20, cold_bytes=1 << 30, K=24, reps=5):
+    """Plain streams measured like the ops: K launches over rotating buffers
+    of `nbytes` (the step's tensor size) captured in a HIP graph, each replay
+    timed between events on the launch stream, the median of `reps`.
+    copy: one read and one write stream (the library's 16-byte copy); add:
+    two reads and one write (the library's add over bf16 elements).  GB/s
+    over the bytes read and written."""
     import torch
+    M = int(max(3, -(-cold_bytes // (2 * nbytes)) + 1))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(3 * M)]
+    bf = [b.view(torch.bfloat16) for b in bufs]
+
+    def run(kind, i):
+        j = 3 * (i % M)
+        if kind == "copy":
+            rn.copy(bufs[j], bufs[j + 1])
+        else:
+            rn.add(bf[j], bf[j + 1], out=bf[j + 2])
+
+    out = {}
     stream = torch.cuda.current_stream()
-    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(4)]
-    rn.copy(bufs[0], bufs[1])
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(reps):
-        rn.copy(bufs[(2 * i) % 4], bufs[(2 * i + 1) % 4])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    del bufs
-    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    for kind, moved in (("copy", 2 * nbytes), ("add", 3 * nbytes)):
+        for i in range(M):
+            run(kind, i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                run(kind, i)
+        graph.replay()
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / K)
+        del graph
+        t = float(np.median(us))
+        out[kind] = {"us": round(t, 3), "bytes": moved,
+                     "GBps": round(moved / (t * 1e-6) / 1e9, 1)}
+    del bufs, bf
+    return out
 
 
 def cpu_model():
@@ -529,7 +559,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-size table and print it")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="with --shapes-only: also run one 1 GiB rn_copy (the "
+                    help="with --shapes-only: also run one 64 MiB rn_copy (the "
                          "known-size kernel that calibrates byte counters)")
     args = ap.parse_args()
 
@@ -555,7 +585,7 @@ def main():
         names = None if args.shapes_only == "all" else args.shapes_only.split(",")
         only = None if not args.ops else args.ops.split(",")
         if args.calib_copy:
-            a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+            a = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
             b = torch.empty_like(a)
             rn.copy(a, b)
             torch.cuda.synchronize()
@@ -613,8 +643,10 @@ def main():
     shapes = None
     if not (args.no_shapes or args.only):
         shapes = time_shapes(rn, dev)
-    copy_gbs = copy_ceiling(rn, dev)
-    log(f"copy ceiling {copy_gbs:.0f} GB/s ({100 * copy_gbs / PEAK_GBS:.1f}% of peak)")
+    ceil = stream_ceilings(rn, dev)
+    copy_gbs = ceil["copy"]["GBps"]
+    for k, v in ceil.items():
+        log(f"{k} stream ceiling {v['GBps']:.0f} GB/s ({100 * v['GBps'] / PEAK_GBS:.1f}% of peak)")
 
     dom = max(ops, key=lambda k: per_op[k]["us"])
     achieved = nbytes[dom] / (per_op[dom]["us"] * 1e-6) / 1e9
@@ -643,6 +675,7 @@ def main():
         "pct_peak": round(100.0 * value / PEAK_GBS, 2),
         "per_op": per_op,
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "stream_ceilings": ceil,
         "decode_us_per_call": decode,
         "shapes": shapes,
         "wall_ms_per_step": round(wall_ms, 5),

@@ -17,7 +17,8 @@
       traffic per call) from a FETCH_SIZE run and a
       WRITE_SIZE run (both KiB per dispatch), each scaled by what the same
       counter reads for the streaming copy kernel of known size
-      (rn::copy16_kernel moving `calib-bytes` each way); written as JSON with
+      (rn::copy16_kernel moving `calib-bytes` each way, 64 MiB by default:
+      the size bench.py's stream ceilings and --calib-copy copy); written as JSON with
       a digest of the kernel sources it was measured on.
 """
 import glob
@@ -133,7 +134,7 @@ def _counter(db, counter, substr):
 
 
 def traffic(fetch_db, write_db, substr, out_json, calib="copy16_kernel",
-            calib_bytes=1 << 30):
+            calib_bytes=64 << 20):
     """Bytes per launch of the kernels matching each of the substrings in
     `substr` (one string, or a list for an op made of several kernels, one
     launch each per call), their sum as the op's traffic per call."""
