@@ -828,10 +828,15 @@ def test_unsupported_sizes():
 #                          partial rows with 12 segments of accumulators
 #   (1, 16392, bf16), (2, 8201, f32)  one or two rows just past the register
 #                          plans (16-byte and element-wise paths)
+#   (2, 2^22, bf16), (1, 2^22, f32), (2, 2^22 - 1, f16/f32)  the longest rows
+#                          the library takes, on both paths: 4096 values per
+#                          lane in each fp32 sum, column sums over 2^22 columns
+MAXH = 1 << 22
 LONG = [(600, 20480, "bf16"), (37, 32768, "bf16"), (300, 32768, "bf16/f32"),
         (3, 49152, "bf16"), (5, 98304, "bf16"), (600, 24576, "f32"),
         (50, 40000, "f32"), (300, 8193, "bf16"), (600, 12002, "f16"),
-        (1, 16392, "bf16"), (2, 8201, "f32")]
+        (1, 16392, "bf16"), (2, 8201, "f32"),
+        (2, MAXH, "bf16"), (1, MAXH, "f32"), (2, MAXH - 1, "f16/f32")]
 
 
 @pytest.mark.parametrize("N,H,storage", LONG)

@@ -49,10 +49,15 @@ def _both(x, dy, g, mean, rstd):
 # (first call, second smaller call): tall rows on the one-workgroup-per-CU
 # plans (column-major partial rows), wide rows (row-major partial rows, the
 # largest LayerNorm partial set: 256 x 16384 x 2 floats = the array's size),
-# and a short wide input that takes the column sums (no partial rows).
+# a short wide input that takes the column sums (no partial rows), rows
+# past the register plans (column sums), and decode sizes (64 rows: partial
+# rows of a few workgroups; one row: a single workgroup writes dgamma/dbeta
+# itself).
 CASES = [((32771, 1024), (4099, 1024)),
          ((4099, 16384), (1000, 2048)),
-         ((2048, 16384), (300, 16384))]
+         ((2048, 16384), (300, 16384)),
+         ((37, 32768), (5, 20480)),
+         ((64, 4096), (1, 4096))]
 
 
 @pytest.mark.parametrize("first,second", CASES)
