@@ -69,7 +69,9 @@ EXTRA_OPS = ("fused_add_rms_bwd", "fused_add_rms_fwd_inplace", "unfused_add_rms"
 # Beyond those: the other storage pairs at the headline shape (IEEE
 # binary16 throughout; bf16 activations with float32 gamma/beta and their
 # gradients) and short rows (2^20 rows of 128: a normalization over a head
-# dimension), each for every op they have a workload for.
+# dimension), each for every op they have a workload for, and rows past the
+# register-resident plans (32768 elements: cached in LDS between the two
+# passes; 131072: read twice).
 NORM_OPS = ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd")
 ALL_OPS = NORM_OPS + ("fused_add_rms_fwd", "fused_add_rms_bwd")
 SHAPES = (
@@ -81,6 +83,8 @@ SHAPES = (
     ("f16_32768x1024", ALL_OPS),
     ("mixed_bf16_f32w_32768x1024", ALL_OPS),
     ("rows_bf16_1048576x128", NORM_OPS),
+    ("long_bf16_2048x32768", NORM_OPS + ("fused_add_rms_fwd",)),
+    ("long_bf16_256x131072", NORM_OPS),
 )
 
 
@@ -329,7 +333,8 @@ def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24, only_ops=None):
     todo = SHAPES if names is None else [(n, table.get(n, NORM_OPS)) for n in names]
     for name, ops in todo:
         if only_ops is not None:
-            ops = tuple(o for o in only_ops if o in ALL_OPS)
+            allowed = table.get(name, ALL_OPS)
+            ops = tuple(o for o in only_ops if o in allowed)
             if not ops:
                 continue
         w = synth.WORKLOADS[name]

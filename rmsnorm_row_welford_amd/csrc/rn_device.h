@@ -204,6 +204,10 @@ __device__ __forceinline__ void opaque(u32x4 &v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(f32x4 &v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(unsigned &v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void opaque(float &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(f32x4 (&v)[2]) {
+    opaque(v[0]);
+    opaque(v[1]);
+}
 
 // Store a chunk of VEC float32 values, rounded to the storage type, through
 // a buffer resource.

@@ -57,8 +57,10 @@ struct BwdArgs {
 // multiple of 8 slots.
 __host__ __device__ inline int partial_stride(int P) { return (P + 7) & ~7; }
 
-// Longest rows the register-resident plans hold: 16-byte vector path,
-// element-wise path.  Longer rows walk their row in segments (rn_long.h).
+// Longest rows the register-resident backward plans hold: 16-byte vector
+// path, element-wise path.  Longer rows walk their row in segments
+// (rn_long.h).  The forward's vector-path limit is the widest span of its
+// plan list (32768 for 2-byte rows with 2-byte parameters, else 16384).
 constexpr int kMaxHiddenReg = 16384;
 constexpr int kMaxHiddenRegScalar = 8192;
 // Longest row any path takes (4 Mi elements: byte offsets within a row stay

@@ -201,7 +201,7 @@ void fwd_kernel(const FwdArgs a) {
     // PD rows are requested ahead: a ring of PD + 1 row buffers, which the
     // loop below walks unrolled so that each buffer keeps its registers (no
     // copies from one buffer to the next).
-    constexpr int PD = !PF ? 0 : sizeof(T) == 2 ? RN_FWD_PF_DEPTH : 1;
+    constexpr int PD = !PF ? 0 : (sizeof(T) == 2 && VEC * CPL <= 16) ? RN_FWD_PF_DEPTH : 1;
     constexpr int NR = PD + 1;
     Raw ring[NR][NIN][CPL];
     // URING: the ring's loads and stores are all issued, with no branch
@@ -252,6 +252,11 @@ void fwd_kernel(const FwdArgs a) {
         }
 
         float mean = 0.0f, var;
+        // rows of more than 16 elements per lane: LayerNorm's shifted values
+        // are widened again from the packed chunks where used instead of
+        // kept as float32 (the registers of the ring and the parameters)
+        constexpr bool REW = OP == OP_LN && E > 16;
+        float pv = 0.0f, mv = 0.0f;   // REW: x - mean = (x - pv) - mv
         if constexpr (OP == OP_LN) {
             // Shift by a pivot (the first element of the row, or of the
             // wave's part of it) so that the sums and deviations are formed
@@ -284,12 +289,17 @@ void fwd_kernel(const FwdArgs a) {
                 mean = pivot + ms;
             } else {
                 const float mw = wave_sum(s) * inv_cnt;
+                if constexpr (REW) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) opaque(cur[0][c].v);
+                }
                 float q = 0.0f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
-                        const float d = (FULL || L.valid(c)) ? v[c * VEC + k] - mw : 0.0f;
+                        const float u = REW ? cur[0][c].get(k) - pivot : v[c * VEC + k];
+                        const float d = (FULL || L.valid(c)) ? u - mw : 0.0f;
                         q = __builtin_fmaf(d, d, q);
                     }
                 q = wave_sum(q);
@@ -316,7 +326,12 @@ void fwd_kernel(const FwdArgs a) {
             // widened again from the packed chunks (made opaque so the
             // compiler cannot keep the first widening live), which frees E
             // registers for occupancy.  Same operations, same bits.
-            if constexpr (PD >= 2) {
+            if constexpr (REW) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) opaque(cur[0][c].v);
+                pv = pivot;
+                mv = ms;
+            } else if constexpr (PD >= 2) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) v[e] -= ms;   // x - mean
             } else {
@@ -345,11 +360,24 @@ void fwd_kernel(const FwdArgs a) {
         const float rstd = rsqrt_pos(var + a.eps);
 
         if (URING || active) {
+            if constexpr (REW) {
+                // widen the parameters per row too (not hoisted out of the loop)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    opaque(g[c].v);
+                    opaque(bt[c].v);
+                }
+            }
             float out[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float ge = g[e / VEC].get(e % VEC);
-                if constexpr (OP == OP_LN)
+                if constexpr (REW) {
+                    const float d = (FULL || L.valid(e / VEC))
+                                        ? (cur[0][e / VEC].get(e % VEC) - pv) - mv
+                                        : 0.0f;
+                    out[e] = __builtin_fmaf(d * rstd, ge, bt[e / VEC].get(e % VEC));
+                } else if constexpr (OP == OP_LN)
                     out[e] = __builtin_fmaf(v[e] * rstd, ge, bt[e / VEC].get(e % VEC));
                 else
                     out[e] = (v[e] * rstd) * ge;

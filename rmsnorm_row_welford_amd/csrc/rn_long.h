@@ -5,25 +5,28 @@
 // 1024*VEC elements, lane l holding chunk [(s*1024 + l)*VEC, +VEC) of
 // segment s (coalesced 16-byte accesses, as in the register plans).  Each
 // row is passed over twice: the first pass reads the row from HBM and forms
-// the statistics, the second forms the outputs.  Between the two passes the
-// row waits in LDS when it fits ("cache": the raw chunks of x, and of the
-// residual or dy, at the same place for the same lane, so no lane reads what
-// another wrote and no barrier is needed); otherwise the second pass reads
-// it again from global memory, where it usually still sits in L2.  These are
-// the pages' two-pass designs for rows wider than one tile ("Write Triton
-// Layernorm Kernel", Required reasoning process, the loop over column
-// blocks for large H; "Write Triton Fused Add Rmsnorm Kernel", Required
-// reasoning process, the two-pass variant; "Write Cuda Layernorm Kernel",
-// Kernel design rules, the stride loop).
+// the statistics, the second forms the outputs.  These are the pages'
+// two-pass designs for rows wider than one tile ("Write Triton Layernorm
+// Kernel", Required reasoning process, the loop over column blocks for
+// large H; "Write Triton Fused Add Rmsnorm Kernel", Required reasoning
+// process, the two-pass variant; "Write Cuda Layernorm Kernel", Kernel
+// design rules, the stride loop).  Between the two passes the row stays on
+// chip where it fits: its first segments in registers, the next ones in LDS
+// (the raw chunks of x, and of the residual or dy, at the same place for the
+// same lane, so no lane reads what another wrote and no barrier is needed).
+// Otherwise the second pass reads it again from global memory.
 //
-// LayerNorm statistics in one read pass: every value is shifted by the
-// row's first element (as in the register plans), each lane forms the exact
-// mean and M2 of each of its chunks and merges them into a running
-// (count, mean, M2) with the parallel merge ("Write Cuda Layernorm Kernel",
-// Required reasoning process, the Welford merge formula), and the 1024
-// lanes' states are combined by the multi-way form of the same merge:
-// mean = sum(n_l m_l)/H, M2 = sum(M2_l + n_l (m_l - mean)^2).  RMSNorm and
-// the fused op sum squares.  The denominator is always H.
+// Forward statistics of a row held on chip: the exact two-pass over the
+// held values (LayerNorm: the mean of the values shifted by the row's first
+// element, as in the register plans, then the sum of squared deviations
+// from it; RMSNorm and the fused op: the sum of squares).  Of a row read
+// twice, in one read pass: each lane forms the exact mean and M2 of each of
+// its chunks and merges them into a running (count, mean, M2) with the
+// parallel merge ("Write Cuda Layernorm Kernel", Required reasoning
+// process, the Welford merge formula), and the 1024 lanes' states are
+// combined by the multi-way form of the same merge:
+// mean = sum(n_l m_l)/H, M2 = sum(M2_l + n_l (m_l - mean)^2).  The
+// denominator is always H.
 //
 // Backward: the first pass forms x_hat, g = dy*gamma and the row sums of g
 // and g*x_hat (and, for rows of up to 32 elements per lane, adds dy*x_hat and
@@ -42,6 +45,10 @@ static_assert(kLongAccMaxH == 32 * kLongThreads, "accumulators for 32 elements p
 // Segments whose loads are issued together.
 #ifndef RN_LONG_UNROLL
 #define RN_LONG_UNROLL 4
+#endif
+// Segments whose parameters the forward's output pass requests together.
+#ifndef RN_LONG_OUT_GROUP
+#define RN_LONG_OUT_GROUP 2
 #endif
 
 // Sum over the 16 waves of a 1024-thread workgroup; every lane gets the same
@@ -79,22 +86,253 @@ __host__ __device__ inline uint32_t long_row_pad(int H, int esize) {
     return ((uint32_t)H * (uint32_t)esize + 15u) & ~15u;
 }
 
-// Forward.  `cache`: the row's raw inputs fit in the dynamic LDS (NIN rows of
-// long_row_pad bytes) and wait there between the passes.
+// Raw chunks of each input that the on-chip forward keeps in registers:
+// 32 registers' worth (16 for each of the fused op's two inputs).
+template <class T, int VEC, int OP>
+constexpr int fwd_reg_segs() {
+    constexpr int words = (VEC * (int)sizeof(T) + 3) / 4;
+    return (OP == OP_FUSED ? 16 : 32) / words;
+}
+
+// Output of one chunk of the forward: y (and h for the fused op).  v: the
+// chunk's values (x, or x + residual in fp32).
 template <class T, class W, int VEC, int OP>
-__global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a, int cache) {
+__device__ __forceinline__ void fwd_long_out(const float *v, const RawChunk<W, VEC> &cg,
+                                             const RawChunk<W, VEC> &cb, float pivot,
+                                             float ms, float rstd, rsrc_t ry, rsrc_t rh,
+                                             uint32_t off) {
+    // h in the same pass as y; every input of the row was read before, so
+    // h may alias x or the residual
+    if constexpr (OP == OP_FUSED) bstore_chunk<VEC>((T *)nullptr, rh, off, v);
+    float out[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        if constexpr (OP == OP_LN) {
+            const float d = (v[k] - pivot) - ms;   // x - mean
+            out[k] = __builtin_fmaf(d * rstd, cg.get(k), cb.get(k));
+        } else {
+            out[k] = (v[k] * rstd) * cg.get(k);
+        }
+    }
+    bstore_chunk<VEC>((T *)nullptr, ry, off, out);
+}
+
+// Forward of rows held on chip: segments [0, R) of each input in registers,
+// the next `nlds` in LDS (LSEG), so every input element crosses HBM once.
+// Rows that half the register budget holds (R below fwd_reg_segs) leave
+// room for two workgroups per CU: one loads its row while the other reduces
+// and stores.
+template <class T, class W, int VEC, int OP, int R, bool LSEG>
+__global__ __launch_bounds__(kLongThreads, (R < fwd_reg_segs<T, VEC, OP>()) ? 8 : 1)
+void fwd_onchip_kernel(const FwdArgs a, int nlds) {
     using Raw = RawChunk<T, VEC>;
     using RawW = RawChunk<W, VEC>;
     constexpr int U = RN_LONG_UNROLL;
+    // float32 parameters beside 16-bit rows take twice the registers
+    constexpr int G = sizeof(W) > sizeof(T) ? 1 : RN_LONG_OUT_GROUP;
+    static_assert(R % G == 0, "whole output groups");
     constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;
     constexpr int SPAN = kLongThreads * VEC;
+    constexpr int ES = (int)sizeof(T);
     extern __shared__ f32x4 lds_cache[];
     __shared__ float red[2 * 16];
     unsigned char *lds = (unsigned char *)lds_cache;
     const int tid = threadIdx.x;
     const int H = a.H;
+    const int nseg = (H + SPAN - 1) / SPAN;   // at most R + nlds
+    const uint32_t nb = (uint32_t)H * (uint32_t)ES;
+    const uint32_t lin = (uint32_t)nlds * (uint32_t)(SPAN * ES);   // LDS bytes per input
+    const rsrc_t rg = make_rsrc(a.gamma, (uint32_t)H * (uint32_t)sizeof(W));
+    const rsrc_t rbt = make_rsrc(a.beta ? a.beta : a.gamma,
+                                 a.beta ? (uint32_t)H * (uint32_t)sizeof(W) : 0u);
+    // first element of the lane's chunk in segment s, and its LDS slot
+    auto el = [&](int s) { return s * SPAN + tid * VEC; };
+    auto lslot = [&](int s) { return (uint32_t)(((s - R) * SPAN + tid * VEC) * ES); };
+    int parity = 0;
+
+    for (int64_t row = blockIdx.x; row < a.N; row += gridDim.x) {
+        const rsrc_t rx = make_rsrc((const T *)a.x + row * a.ldx, nb);
+        const rsrc_t rr =
+            make_rsrc(OP == OP_FUSED ? (const T *)a.res + row * a.ldr : (const T *)a.x,
+                      OP == OP_FUSED ? nb : 0u);
+        // ---- pass 1: every load of the row, the LDS copies and the first sums
+        Raw reg[NIN][R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            reg[0][u].template bload<RN_LOAD_AUX>(rx, el(u) * ES);
+            if constexpr (OP == OP_FUSED) reg[1][u].template bload<RN_LOAD_AUX>(rr, el(u) * ES);
+        }
+        float pivot = 0.0f;
+        if constexpr (OP == OP_LN) {
+            RawChunk<T, 1> p0;
+            p0.template bload<0>(rx, 0);
+            pivot = p0.get(0);
+        }
+        // LayerNorm: sum of x - pivot; the others: sum of squares
+        float s1 = 0.0f;
+        auto add1 = [&](const float *v) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                if constexpr (OP == OP_LN) s1 += v[k] - pivot;
+                else s1 = __builtin_fmaf(v[k], v[k], s1);
+            }
+        };
+        auto widen = [&](const Raw &c0, const Raw &c1, float *v) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                v[k] = c0.get(k);
+                if constexpr (OP == OP_FUSED) v[k] += c1.get(k);
+            }
+        };
+        // LDS segments, a group of U at a time, the next group requested
+        // before the current one is parked
+        if constexpr (LSEG) {
+            Raw ca[U][NIN], cb[U][NIN];
+            auto request = [&](Raw (&c)[U][NIN], int s0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    c[u][0].template bload<RN_LOAD_AUX>(rx, el(s0 + u) * ES);
+                    if constexpr (OP == OP_FUSED)
+                        c[u][1].template bload<RN_LOAD_AUX>(rr, el(s0 + u) * ES);
+                }
+            };
+            auto park = [&](Raw (&c)[U][NIN], int s0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (el(s0 + u) < H) {   // chunks are whole (H is a multiple of VEC)
+#pragma unroll
+                        for (int i = 0; i < NIN; ++i)
+                            lds_put<T, VEC>(lds + i * lin + lslot(s0 + u), c[u][i]);
+                        float v[VEC];
+                        widen(c[u][0], c[u][NIN - 1], v);
+                        add1(v);
+                    }
+                }
+            };
+            if (R < nseg) request(ca, R);
+            for (int s0 = R; s0 < nseg; s0 += 2 * U) {
+                if (s0 + U < nseg) request(cb, s0 + U);
+                park(ca, s0);
+                if (s0 + U >= nseg) break;
+                if (s0 + 2 * U < nseg) request(ca, s0 + 2 * U);
+                park(cb, s0 + U);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if (el(u) < H) {
+                float v[VEC];
+                widen(reg[0][u], reg[NIN - 1][u], v);
+                add1(v);
+            }
+        }
+        // keep the held chunks packed across the reductions (widened again
+        // where used) rather than as float32 copies
+        auto repack = [&]() {
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+#pragma unroll
+                for (int i = 0; i < NIN; ++i) opaque(reg[i][u].v);
+        };
+        repack();
+        float ms = 0.0f, var;
+        if constexpr (OP == OP_LN) {
+            // exact two-pass: the mean about the pivot, then the squared
+            // deviations from it over the held row
+            ms = block_sum16(s1, red, parity) * a.inv_H;
+            float q = 0.0f;
+            auto add2 = [&](const Raw &c) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float d = (c.get(k) - pivot) - ms;
+                    q = __builtin_fmaf(d, d, q);
+                }
+            };
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+                if (el(u) < H) add2(reg[0][u]);
+            if constexpr (LSEG) {
+                for (int sg = R; sg < nseg; ++sg) {
+                    if (el(sg) < H) {
+                        Raw c;
+                        lds_get<T, VEC>(lds + lslot(sg), c);
+                        add2(c);
+                    }
+                }
+            }
+            repack();
+            var = block_sum16(q, red, parity) * a.inv_H;
+        } else {
+            var = block_sum16(s1, red, parity) * a.inv_H;
+        }
+        const float rstd = rsqrt_pos(var + a.eps);
+        if (tid == 0) {
+            if constexpr (OP == OP_LN) {
+                if (a.mean) a.mean[row] = pivot + ms;
+            }
+            if (a.rstd) a.rstd[row] = rstd;
+        }
+        // ---- pass 2: outputs, parameters requested G segments at a time
+        const rsrc_t ry = make_rsrc((T *)a.y + row * a.ldy, nb);
+        const rsrc_t rh = make_rsrc(OP == OP_FUSED ? (T *)a.h + row * a.ldh : (T *)a.y,
+                                    OP == OP_FUSED ? nb : 0u);
+#pragma unroll
+        for (int u0 = 0; u0 < R; u0 += G) {
+            if (u0 < nseg) {
+                RawW cg[G], cb[G];
+#pragma unroll
+                for (int u = 0; u < G; ++u) {
+                    const int woff = el(u0 + u) * (int)sizeof(W);
+                    cg[u].template bload<0>(rg, woff);
+                    if constexpr (OP == OP_LN) cb[u].template bload<0>(rbt, woff);
+                }
+#pragma unroll
+                for (int u = 0; u < G; ++u) {
+                    float v[VEC];
+                    widen(reg[0][u0 + u], reg[NIN - 1][u0 + u], v);
+                    fwd_long_out<T, W, VEC, OP>(v, cg[u], cb[u], pivot, ms, rstd, ry, rh,
+                                                (uint32_t)(el(u0 + u) * ES));
+                }
+            }
+        }
+        if constexpr (LSEG) for (int s0 = R; s0 < nseg; s0 += G) {
+            Raw c[G][NIN];
+            RawW cg[G], cb[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                const int woff = el(s0 + u) * (int)sizeof(W);
+                cg[u].template bload<0>(rg, woff);
+                if constexpr (OP == OP_LN) cb[u].template bload<0>(rbt, woff);
+#pragma unroll
+                for (int i = 0; i < NIN; ++i) {
+                    if (el(s0 + u) < H) lds_get<T, VEC>(lds + i * lin + lslot(s0 + u), c[u][i]);
+                    else c[u][i].zero();
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                float v[VEC];
+                widen(c[u][0], c[u][NIN - 1], v);
+                fwd_long_out<T, W, VEC, OP>(v, cg[u], cb[u], pivot, ms, rstd, ry, rh,
+                                            (uint32_t)(el(s0 + u) * ES));
+            }
+        }
+    }
+}
+
+// Forward of rows too long to hold on chip: x (and the residual) are read
+// twice, the statistics in one pass by the chunk-wise parallel merge.
+template <class T, class W, int VEC, int OP>
+__global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a) {
+    using Raw = RawChunk<T, VEC>;
+    using RawW = RawChunk<W, VEC>;
+    constexpr int U = RN_LONG_UNROLL;
+    constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;
+    constexpr int SPAN = kLongThreads * VEC;
+    __shared__ float red[2 * 16];
+    const int tid = threadIdx.x;
+    const int H = a.H;
     const int nseg = (H + SPAN - 1) / SPAN;
-    const uint32_t pad = long_row_pad(H, (int)sizeof(T));
     const uint32_t nb = (uint32_t)H * (uint32_t)sizeof(T);
     const rsrc_t rg = make_rsrc(a.gamma, (uint32_t)H * (uint32_t)sizeof(W));
     const rsrc_t rbt = make_rsrc(a.beta ? a.beta : a.gamma,
@@ -113,7 +351,7 @@ __global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a,
             p0.template bload<0>(rx, 0);
             pivot = p0.get(0);
         }
-        // ---- pass 1: statistics (and the LDS copy of the row)
+        // ---- pass 1: statistics
         float ln_n = 0.0f, ln_m = 0.0f, ln_q = 0.0f, q = 0.0f;
         for (int s0 = 0; s0 < nseg; s0 += U) {
             Raw cx[U][NIN];
@@ -126,14 +364,8 @@ __global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e0 = (s0 + u) * SPAN + tid * VEC;
-                const bool valid = e0 < H;
-                if (cache && valid) {
-                    const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
-#pragma unroll
-                    for (int i = 0; i < NIN; ++i) lds_put<T, VEC>(lds + i * pad + off, cx[u][i]);
-                }
                 if constexpr (OP == OP_LN) {
-                    if (valid) {
+                    if (e0 < H) {
                         // exact two-pass mean and M2 of the chunk, then the
                         // parallel merge into the lane's running state
                         float uu[VEC], sm = 0.0f;
@@ -166,70 +398,51 @@ __global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a,
                 }
             }
         }
-        float mean = 0.0f, ms = 0.0f, var;
+        float ms = 0.0f, var;
         if constexpr (OP == OP_LN) {
             // multi-way merge of the lanes' states (about the pivot)
             ms = block_sum16(ln_n * ln_m, red, parity) * a.inv_H;
             const float dm = ln_m - ms;
             var = block_sum16(__builtin_fmaf(ln_n * dm, dm, ln_q), red, parity) * a.inv_H;
-            mean = pivot + ms;
         } else {
             var = block_sum16(q, red, parity) * a.inv_H;
         }
         const float rstd = rsqrt_pos(var + a.eps);
         if (tid == 0) {
             if constexpr (OP == OP_LN) {
-                if (a.mean) a.mean[row] = mean;
+                if (a.mean) a.mean[row] = pivot + ms;
             }
             if (a.rstd) a.rstd[row] = rstd;
         }
-        // ---- pass 2: outputs
+        // ---- pass 2: outputs, the row read again
         const rsrc_t ry = make_rsrc((T *)a.y + row * a.ldy, nb);
         const rsrc_t rh = make_rsrc(OP == OP_FUSED ? (T *)a.h + row * a.ldh : (T *)a.y,
                                     OP == OP_FUSED ? nb : 0u);
         for (int s0 = 0; s0 < nseg; s0 += U) {
             Raw cx[U][NIN];
-            RawW cg[U], cb[(OP == OP_LN) ? U : 1];
+            RawW cg[U], cb[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e0 = (s0 + u) * SPAN + tid * VEC;
                 const uint32_t off = (uint32_t)(e0 * (int)sizeof(T));
-                if (cache) {
-#pragma unroll
-                    for (int i = 0; i < NIN; ++i) {
-                        if (e0 < H) lds_get<T, VEC>(lds + i * pad + off, cx[u][i]);
-                        else cx[u][i].zero();
-                    }
-                } else {
-                    cx[u][0].template bload<RN_LOAD_AUX>(rx, off);
-                    if constexpr (OP == OP_FUSED) cx[u][1].template bload<RN_LOAD_AUX>(rr, off);
-                }
+                cx[u][0].template bload<RN_LOAD_AUX>(rx, off);
+                if constexpr (OP == OP_FUSED) cx[u][1].template bload<RN_LOAD_AUX>(rr, off);
                 const uint32_t woff = (uint32_t)(e0 * (int)sizeof(W));
                 cg[u].template bload<0>(rg, woff);
                 if constexpr (OP == OP_LN) cb[u].template bload<0>(rbt, woff);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t off = (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T));
-                float v[VEC], out[VEC];
+                float v[VEC];
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     v[k] = cx[u][0].get(k);
                     if constexpr (OP == OP_FUSED) v[k] += cx[u][1].get(k);
                 }
-                // h in the same pass as y; every element of this lane's
-                // chunk was read before, so h may alias x or the residual
-                if constexpr (OP == OP_FUSED) bstore_chunk<VEC>((T *)nullptr, rh, off, v);
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    if constexpr (OP == OP_LN) {
-                        const float d = (v[k] - pivot) - ms;   // x - mean
-                        out[k] = __builtin_fmaf(d * rstd, cg[u].get(k), cb[u].get(k));
-                    } else {
-                        out[k] = (v[k] * rstd) * cg[u].get(k);
-                    }
-                }
-                bstore_chunk<VEC>((T *)nullptr, ry, off, out);
+                // h is stored from values this lane read in this same pass
+                fwd_long_out<T, W, VEC, OP>(
+                    v, cg[u], cb[u], pivot, ms, rstd, ry, rh,
+                    (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T)));
             }
         }
     }
@@ -410,12 +623,32 @@ inline void allow_lds(int bytes) {
 
 template <class T, class W, int VEC, int OP>
 hipError_t launch_fwd_long_op(const FwdArgs &a, hipStream_t s) {
-    constexpr auto k = fwd_long_kernel<T, W, VEC, OP>;
     constexpr int NIN = (OP == OP_FUSED) ? 2 : 1;
-    const int lds = long_cache_bytes(a.H, (int)sizeof(T), NIN, long_lds_budget());
-    allow_lds<k>(lds);
+    constexpr int R = fwd_reg_segs<T, VEC, OP>();
+    constexpr int SPAN = kLongThreads * VEC;
+    const int nseg = (a.H + SPAN - 1) / SPAN;
+    const int nlds = nseg > R ? nseg - R : 0;
+    const int64_t lds = (int64_t)nlds * NIN * SPAN * (int64_t)sizeof(T);
     const int64_t grid = a.N < (1 << 20) ? a.N : (1 << 20);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kLongThreads), lds, s, a, lds > 0 ? 1 : 0);
+    if (lds <= long_lds_budget()) {
+        // the row fits in registers (and LDS): one read
+        constexpr int RH = R / 2;
+        if (nseg <= RH) {
+            hipLaunchKernelGGL((fwd_onchip_kernel<T, W, VEC, OP, RH, false>),
+                               dim3((unsigned)grid), dim3(kLongThreads), 0, s, a, 0);
+        } else if (nlds == 0) {
+            hipLaunchKernelGGL((fwd_onchip_kernel<T, W, VEC, OP, R, false>),
+                               dim3((unsigned)grid), dim3(kLongThreads), 0, s, a, 0);
+        } else {
+            constexpr auto k = fwd_onchip_kernel<T, W, VEC, OP, R, true>;
+            allow_lds<k>((int)lds);
+            hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kLongThreads), (unsigned)lds, s,
+                               a, nlds);
+        }
+    } else {
+        hipLaunchKernelGGL((fwd_long_kernel<T, W, VEC, OP>), dim3((unsigned)grid),
+                           dim3(kLongThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -165,6 +165,9 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 #ifndef RN_FWD_BF16_16384
 #define RN_FWD_BF16_16384 Plan<8, 2, 16, 1>
 #endif
+#ifndef RN_FWD_BF16_32768
+#define RN_FWD_BF16_32768 Plan<8, 4, 16, 1>
+#endif
 // One 8-wave workgroup per CU: with two, the waves that a CU's arbitration
 // serves last leave a long tail of a few rows in flight.
 #ifndef RN_BWD_BF16_1024
@@ -186,7 +189,13 @@ using FwdPlans2B = PlanList<SegPlan<8, 8, 4, 2>,          //    64
                             RN_FWD_BF16_2048,             //  2048
                             RN_FWD_BF16_4096,             //  4096
                             Plan<8, 2, 8, 1, false>,      //  8192
-                            RN_FWD_BF16_16384>;           // 16384
+                            RN_FWD_BF16_16384,            // 16384
+                            RN_FWD_BF16_32768>;           // 32768
+// float32 parameters take twice the registers: no 32768 plan (those rows
+// take the long-row kernels).
+using FwdPlans2BW = PlanList<SegPlan<8, 8, 4, 2>, SegPlan<8, 16, 4, 2>, SegPlan<8, 32, 4, 2>,
+                             RN_FWD_BF16_512, RN_FWD_BF16_1024, RN_FWD_BF16_2048,
+                             RN_FWD_BF16_4096, Plan<8, 2, 8, 1, false>, RN_FWD_BF16_16384>;
 using FwdPlansF32 = PlanList<SegPlan<4, 8, 4, 2>,         //    32
                              SegPlan<4, 16, 4, 2>,        //    64
                              SegPlan<4, 32, 4, 2>,        //   128
@@ -238,10 +247,17 @@ using BwdPlansScalar = PlanList<SegPlan<1, 8, 4, 1>,   //     8
 
 // Rows past the register plans (is_long_row) walk their row in segments:
 // 16-byte chunks on the vector path, single elements otherwise.
+template <class... Ps>
+constexpr int max_span(PlanList<Ps...>) {
+    int m = 0;
+    ((m = Ps::SPAN > m ? Ps::SPAN : m), ...);
+    return m;
+}
+
 template <class T, class W, class VecPlans>
 hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
                         hipStream_t s) {
-    if (is_long_row(a.H, vec))
+    if (a.H > (vec ? max_span(VecPlans{}) : kMaxHiddenRegScalar))
         return vec ? launch_fwd_long<T, W, Vec16<T>::N>(op, a, s)
                    : launch_fwd_long<T, W, 1>(op, a, s);
     auto f = [&]<class P>() { return launch_fwd_any<T, W, P>(op, a, cus, s); };

@@ -107,6 +107,14 @@ WORKLOADS: Dict[str, Workload] = {
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         Workload("bwd_bf16_2048x16384", 1005, 2048, 16384, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        # rows past the register-resident plans: one that the LDS row cache
+        # holds (x and dy of a 32768-element bf16 row: 128 KiB), one that no
+        # cache holds (256 KiB rows, read twice)
+        Workload("long_bf16_2048x32768", 1010, 2048, 32768, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1),
+                 residual=(0.0, 1.0)),
+        Workload("long_bf16_256x131072", 1011, 256, 131072, "bf16", 1e-5,
+                 x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
     ]
 }
 

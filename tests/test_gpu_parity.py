@@ -274,6 +274,38 @@ def test_bwd_workloads(orc, name, op):
     check_bwd(orc, arr, "bf16", w.eps, layernorm=(op == "ln"), tag=name)
 
 
+# The benchmark's long-row shapes (rows past the register-resident plans):
+# every element of the forward outputs and of dx, in the launch
+# configuration the benchmark times.
+LONG_W = ["long_bf16_2048x32768", "long_bf16_256x131072"]
+
+
+@pytest.mark.parametrize("name", LONG_W)
+@pytest.mark.parametrize("op", ["ln", "rms", "fused"])
+def test_long_workloads(orc, name, op):
+    w = synth.WORKLOADS[name]
+    arr = synth.generate(w)
+    if op == "fused":
+        if "residual" not in arr:
+            pytest.skip("no fused op at this shape in the benchmark")
+        x, r, g = (to_dev(arr[k]) for k in ("x", "residual", "gamma"))
+        y, h, rstd = rn.fused_add_rms_fwd(x, r, g, w.eps)
+        torch.cuda.synchronize()
+        y_o, h_o, r_o = orc.fused_add_rms_fwd(
+            orc.decode(arr["x"], "bf16"), orc.decode(arr["residual"], "bf16"),
+            orc.decode(arr["gamma"], "bf16"), oracle.eps_at_boundary(w.eps))
+        assert np.array_equal(host(h), orc.bf16_encode(h_o)), "h not RNE(x + r)"
+        del h_o
+        tol.check_bf16(host(y), y_o, orc, _lab(name, "fused y bf16"), strict=True)
+        tol.check_rstd(host(rstd), r_o, _lab(name, "fused rstd"))
+        return
+    if op == "ln":
+        check_ln_fwd(orc, arr, "bf16", w.eps, tag=name)
+    else:
+        check_rms_fwd(orc, arr, "bf16", w.eps, tag=name)
+    check_bwd(orc, arr, "bf16", w.eps, layernorm=(op == "ln"), tag=name)
+
+
 # ------------------------------------------------------------ edge cases --
 # The LayerNorm page's validation list (64 ... 2049) plus tiny rows, ragged
 # tails, element-wise-path shapes and the largest rows.
@@ -810,31 +842,44 @@ def test_unsupported_sizes():
     assert ei.value.status == -6
 
 
-# Rows past the register plans (16-byte path above 16384 elements, the
-# element-wise path above 8192): one workgroup per row walks it in segments,
-# caching it in LDS between the passes where it fits (160 KiB on MI355X),
-# reading it again otherwise; the backward writes partial rows for rows of up
-# to 32768 elements when N makes them pay, else column sums.  Cases:
-#   (600, 20480, bf16)     16-byte path, LDS cache, partial rows
-#   (37, 32768, bf16)      cache (x and dy: 128 KiB), column sums (few rows)
-#   (300, 32768, bf16/f32) float32 parameters; RMS partial rows, LN column sums
-#   (3, 49152, bf16)       forward cached, backward read twice, column sums
-#   (5, 98304, bf16)       nothing cached (192 KiB rows), column sums
-#   (600, 24576, f32)      float32 rows: forward cached, backward read twice
-#                          with partial rows
-#   (50, 40000, f32)       LN/RMS forward cached (156 KiB), fused not
-#   (300, 8193, bf16)      element-wise path (odd H), cache, RMS partial rows
-#   (600, 12002, f16)      element-wise path (rows not 16-byte multiples),
+# Rows past the register plans (forward: 2-byte rows with 2-byte parameters
+# above 32768 elements, other 16-byte rows above 16384, the element-wise
+# path above 8192; backward: 16-byte rows above 16384, element-wise above
+# 8192).  The forward holds such a row on chip where it fits (its first
+# segments in registers, the next ones in LDS) and reads it twice
+# otherwise; the backward walks it in segments, caching x and dy in LDS
+# where they fit, and writes partial rows for rows of up to 32768 elements
+# when N makes them pay, else column sums.  Cases (forward; backward):
+#   (600, 20480, bf16)     32768-element register plan, masked tail; LDS
+#                          cache, partial rows
+#   (37, 32768, bf16)      register plan, full; cache (x and dy: 128 KiB),
+#                          column sums (few rows)
+#   (300, 32768, bf16/f32) float32 parameters: on chip in registers (two
+#                          workgroups per CU); RMS partial rows, LN column sums
+#   (3, 49152, bf16)       registers (6 segments; fused: 4 + 2 in LDS); read
+#                          twice, column sums
+#   (5, 98304, bf16)       registers + 4 LDS segments (fused: read twice);
+#                          nothing cached (192 KiB rows), column sums
+#   (30, 98304, bf16/f32)  the same with float32 parameters
+#   (600, 24576, f32)      float32 rows in registers; read twice, partial rows
+#   (50, 40000, f32)       registers + LDS for LN/RMS (fused: read twice)
+#   (300, 8193, bf16)      element-wise path (odd H), registers, two
+#                          workgroups per CU; cache, RMS partial rows
+#   (600, 12002, f16)      element-wise (rows not 16-byte multiples);
 #                          partial rows with 12 segments of accumulators
-#   (1, 16392, bf16), (2, 8201, f32)  one or two rows just past the register
-#                          plans (16-byte and element-wise paths)
+#   (20, 24577, f16)       element-wise, the 32-segment register kernel
+#   (40, 40001, bf16)      element-wise, registers + LDS
+#   (1, 16392, bf16), (2, 8201, f32)  one or two rows just past the
+#                          register plans (16-byte and element-wise paths)
 #   (2, 2^22, bf16), (1, 2^22, f32), (2, 2^22 - 1, f16/f32)  the longest rows
-#                          the library takes, on both paths: 4096 values per
-#                          lane in each fp32 sum, column sums over 2^22 columns
+#                          the library takes, on both paths (read twice): 4096
+#                          values per lane in each fp32 sum, column sums over
+#                          2^22 columns
 MAXH = 1 << 22
 LONG = [(600, 20480, "bf16"), (37, 32768, "bf16"), (300, 32768, "bf16/f32"),
-        (3, 49152, "bf16"), (5, 98304, "bf16"), (600, 24576, "f32"),
-        (50, 40000, "f32"), (300, 8193, "bf16"), (600, 12002, "f16"),
+        (3, 49152, "bf16"), (5, 98304, "bf16"), (30, 98304, "bf16/f32"),
+        (600, 24576, "f32"), (50, 40000, "f32"), (300, 8193, "bf16"),
+        (600, 12002, "f16"), (20, 24577, "f16"), (40, 40001, "bf16"),
         (1, 16392, "bf16"), (2, 8201, "f32"),
         (2, MAXH, "bf16"), (1, MAXH, "f32"), (2, MAXH - 1, "f16/f32")]
 
