@@ -137,6 +137,9 @@ template <> struct RawChunk<bf16_bits, 8> {
     template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
         v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
     }
+    __device__ __forceinline__ void gload_nt(const bf16_bits *p) {
+        v = __builtin_nontemporal_load((const u32x4 *)p);
+    }
     __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int k) const {
         return (k & 1) ? bf16_hi(v[k >> 1]) : bf16_lo(v[k >> 1]);
@@ -147,6 +150,9 @@ template <> struct RawChunk<bf16_bits, 1> {
     template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
         v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
     }
+    __device__ __forceinline__ void gload_nt(const bf16_bits *p) {
+        v = __builtin_nontemporal_load(p);
+    }
     __device__ __forceinline__ void zero() { v = 0u; }
     __device__ __forceinline__ float get(int) const { return __uint_as_float(v << 16); }
 };
@@ -154,6 +160,9 @@ template <> struct RawChunk<f16_t, 8> {
     u32x4 v;
     template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
         v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    }
+    __device__ __forceinline__ void gload_nt(const f16_t *p) {
+        v = __builtin_nontemporal_load((const u32x4 *)p);
     }
     __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int k) const {
@@ -164,6 +173,9 @@ template <> struct RawChunk<f16_t, 1> {
     unsigned v;
     template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
         v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+    }
+    __device__ __forceinline__ void gload_nt(const f16_t *p) {
+        v = __builtin_nontemporal_load((const uint16_t *)p);
     }
     __device__ __forceinline__ void zero() { v = 0u; }
     __device__ __forceinline__ float get(int) const { return f16_lo(v); }
@@ -185,6 +197,9 @@ template <> struct RawChunk<float, 4> {
     template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
         v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
     }
+    __device__ __forceinline__ void gload_nt(const float *p) {
+        v = __builtin_nontemporal_load((const f32x4 *)p);
+    }
     __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ float get(int k) const { return v[k]; }
 };
@@ -193,6 +208,7 @@ template <> struct RawChunk<float, 1> {
     template <int AUX> __device__ __forceinline__ void bload(rsrc_t r, int off) {
         v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX));
     }
+    __device__ __forceinline__ void gload_nt(const float *p) { v = __builtin_nontemporal_load(p); }
     __device__ __forceinline__ void zero() { v = 0.f; }
     __device__ __forceinline__ float get(int) const { return v; }
 };

@@ -523,6 +523,15 @@ __device__ __forceinline__ int64_t partial_index(int b, int P, int H, int col) {
 #ifndef RN_BWD_FOLD
 #define RN_BWD_FOLD 1
 #endif
+// 1: the register plans' dx kernel takes the column tiles after its rows;
+// 0: they run as a second kernel.
+#ifndef RN_COLSUM_FUSED
+#define RN_COLSUM_FUSED 1
+#endif
+// Minimum waves per SIMD asked of the dx-only kernel of 16-wave teams.
+#ifndef RN_BWD_DX_MINW
+#define RN_BWD_DX_MINW 1
+#endif
 // Largest one-per-CU workgroup (in waves) whose teams keep float32 copies.
 #ifndef RN_BWD_KEEP_MAXW
 #define RN_BWD_KEEP_MAXW 8
@@ -552,7 +561,8 @@ __host__ __device__ constexpr int bwd1_lds_floats(int RT, int H, bool ln) {
 // kernel 2 would produce from the single partial row).
 template <class T, class W, int VEC, int CPL, int TW, int RT, bool LN, bool PF, bool ACC,
           bool ADD = false, bool KEEP = false, bool FINAL = false>
-__global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(64 * TW * RT, (!ACC && TW * RT == 16) ? RN_BWD_DX_MINW : 1)
+void bwd1_kernel(const BwdArgs a) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     using Lay = Layout<VEC, CPL, TW>;
     using Raw = RawChunk<T, VEC>;
@@ -821,7 +831,8 @@ __global__ __launch_bounds__(64 * TW * RT) void bwd1_kernel(const BwdArgs a) {
     // several teams, each team parks its accumulators in LDS and every
     // thread then adds a column over the teams in team order.
     if constexpr (!ACC) {
-        return;
+        // the column-sum strategy: dgamma/dbeta from x and dy, tile by tile
+        if constexpr (RN_COLSUM_FUSED) colsum_tiles<T, W, VEC, LN, 64 * TW * RT>(a);
     } else if constexpr (RT == 1 && FINAL) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
@@ -1017,21 +1028,34 @@ hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void 
 // Column sums straight from the rows: dgamma_j = sum_r dy_rj (x_rj - mean_r)
 // rstd_r and dbeta_j = sum_r dy_rj.  Used instead of partial rows when the
 // rows are so few that P partial rows would outweigh reading x and dy again
-// (see bwd_use_colsum).  A 1024-thread workgroup owns COLS = 8*VEC columns:
-// 8 lanes across the columns (one chunk each) times 128 row slots; slot j
-// adds rows j, j+128, ... in increasing order, and the slots are then added
-// in a fixed two-level order through LDS.
-template <class T, class W, int VEC, bool LN>
-__global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, W *dgamma,
-                                                         W *dbeta) {
-    constexpr int CL = 8, SL = 1024 / CL, COLS = CL * VEC;
-    constexpr int NG = 1024 / COLS;      // second-level groups of slots
-    constexpr int SPG = SL / NG;         // slots per group
-    __shared__ float red[SL * COLS];
-    __shared__ float red2[NG * COLS];
+// (see bwd_use_colsum).  They use the saved statistics only, not dx, so the
+// kernels that write dx take these tiles too, after their rows: the tiles
+// then fill the tail of the dx work instead of following it as a second
+// launch.  A workgroup of THREADS threads owns a tile of COLS = 8*VEC
+// columns: 8 lanes across the columns (one chunk each) times THREADS/8 row
+// slots; slot j adds rows j, j + THREADS/8, ... in increasing order, and the
+// slots are then added in a fixed two-level order through LDS.
+// Row iterations of a column tile whose loads are issued together.
+#ifndef RN_COLSUM_UNROLL
+#define RN_COLSUM_UNROLL 2
+#endif
+template <class T, int VEC, int THREADS>
+struct ColsumTile {
+    static constexpr int CL = 8, SL = THREADS / CL, COLS = CL * VEC;
+    static constexpr int NG = THREADS / COLS;   // second-level groups of slots
+    static constexpr int SPG = SL / NG;         // slots per group
+    static_assert(NG * COLS == THREADS && SPG * NG == SL, "tile shape");
+    static constexpr int LDS_FLOATS = SL * COLS + NG * COLS;
+};
+
+template <class T, class W, int VEC, bool LN, int THREADS>
+__device__ void colsum_tile(const BwdArgs &a, int tile, float *red) {
+    using C = ColsumTile<T, VEC, THREADS>;
+    constexpr int CL = C::CL, SL = C::SL, COLS = C::COLS, NG = C::NG, SPG = C::SPG;
+    float *red2 = red + SL * COLS;
     const int lc = threadIdx.x % CL;
     const int slot = threadIdx.x / CL;
-    const int c0 = blockIdx.x * COLS + lc * VEC;
+    const int c0 = tile * COLS + lc * VEC;
     const int H = a.H;
     const int64_t N = a.N;
     float ag[VEC], ab[VEC];
@@ -1040,17 +1064,19 @@ __global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, W *dg
     if (c0 < H) {
         const T *xb = (const T *)a.x + c0;
         const T *dyb = (const T *)a.dy + c0;
-#pragma unroll 4
+#pragma unroll RN_COLSUM_UNROLL
         for (int64_t r = slot; r < N; r += SL) {
-            float xv[VEC], dv[VEC];
-            load_chunk<VEC, true>(xb + r * a.ldx, xv);
-            load_chunk<VEC, true>(dyb + r * a.lddy, dv);
+            // packed until used
+            RawChunk<T, VEC> cx, cd;
+            cx.gload_nt(xb + r * a.ldx);
+            cd.gload_nt(dyb + r * a.lddy);
             const float mu = LN ? a.mean[r] : 0.0f;
             const float s = a.rstd[r];
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
-                ag[k] = __builtin_fmaf(dv[k], (xv[k] - mu) * s, ag[k]);
-                if constexpr (LN) ab[k] += dv[k];
+                const float dv = cd.get(k);
+                ag[k] = __builtin_fmaf(dv, (cx.get(k) - mu) * s, ag[k]);
+                if constexpr (LN) ab[k] += dv;
             }
         }
     }
@@ -1067,15 +1093,40 @@ __global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a, W *dg
         red2[grp * COLS + cc] = t;
         __syncthreads();
         if (threadIdx.x < COLS) {
-            const int col = blockIdx.x * COLS + threadIdx.x;
+            const int col = tile * COLS + threadIdx.x;
             if (col < H) {
                 float u = 0.0f;
                 for (int g = 0; g < NG; ++g) u += red2[g * COLS + threadIdx.x];
-                store_one(p == 0 ? dgamma + col : dbeta + col, u);
+                store_one((p == 0 ? (W *)a.dgamma : (W *)a.dbeta) + col, u);
             }
         }
         __syncthreads();
     }
+}
+
+// Every column tile of the row, taken by the workgroups in turn.
+template <class T, class W, int VEC, bool LN, int THREADS>
+__device__ void colsum_tiles(const BwdArgs &a) {
+    using C = ColsumTile<T, VEC, THREADS>;
+    __shared__ float red[C::LDS_FLOATS];
+    const int ntiles = (a.H + C::COLS - 1) / C::COLS;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x)
+        colsum_tile<T, W, VEC, LN, THREADS>(a, t, red);
+}
+
+// The column tiles as a kernel of their own (RN_COLSUM_FUSED = 0).
+template <class T, class W, int VEC, bool LN>
+__global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a) {
+    colsum_tiles<T, W, VEC, LN, 1024>(a);
+}
+
+// Workgroups the dx kernel with trailing column tiles needs: its row groups,
+// or one per tile if there are more tiles.
+template <int VEC>
+inline int64_t colsum_grid(int64_t row_groups, int H) {
+    const int64_t ntiles = (H + 8 * VEC - 1) / (8 * VEC);
+    const int64_t g = row_groups > ntiles ? row_groups : ntiles;
+    return g < (1 << 20) ? g : (1 << 20);
 }
 
 // ------------------------------------------------------------------ plans --
@@ -1209,18 +1260,22 @@ hipError_t launch_bwd_ln(const BwdArgs &a, int P_, bool colsum, int cus, void *d
         }
         return launch_bwd2<W>(a.part, P_, a.H, LN, dg, db, s);
     }
-    // column sums: kernel 1 writes dx only (forward-style grid), then the
-    // column-sum kernel reads x and dy again
+    // column sums: kernel 1 writes dx (forward-style grid) and then forms
+    // dgamma/dbeta tile by tile from x and dy (a.dgamma, a.dbeta)
     constexpr auto k = bwd1_kernel<T, W, P::VEC, P::CPL, P::TW, P::RT, LN, P::PF, false, ADD>;
     const int resident = resident_per_cu<k>(P::THREADS, 0);
-    const int grid = persistent_grid<P>(a.N, cus, resident >= 2 ? (1 << 20) : resident, 1);
-    hipLaunchKernelGGL(k, dim3(grid), dim3(P::THREADS), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    constexpr int VEC = P::VEC;
-    constexpr int COLS = 8 * VEC;
-    hipLaunchKernelGGL((bwd_colsum_kernel<T, W, VEC, LN>), dim3((a.H + COLS - 1) / COLS),
-                       dim3(1024), 0, s, a, (W *)dg, (W *)db);
+    const int rows = persistent_grid<P>(a.N, cus, resident >= 2 ? (1 << 20) : resident, 1);
+    if constexpr (RN_COLSUM_FUSED) {
+        const int64_t grid = colsum_grid<P::VEC>(rows, a.H);
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(P::THREADS), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(k, dim3(rows), dim3(P::THREADS), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        constexpr int COLS = 8 * P::VEC;
+        hipLaunchKernelGGL((bwd_colsum_kernel<T, W, P::VEC, LN>),
+                           dim3((a.H + COLS - 1) / COLS), dim3(1024), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -29,10 +29,12 @@
 // denominator is always H.
 //
 // Backward: the first pass forms x_hat, g = dy*gamma and the row sums of g
-// and g*x_hat (and, for rows of up to 32 elements per lane, adds dy*x_hat and
-// dy into per-lane accumulators that become the workgroup's partial row);
-// the second pass forms dx.  Wider rows leave dgamma/dbeta to the column-sum
-// kernel.
+// and g*x_hat, the second pass forms dx.  With partial rows (rows of up to
+// 32 elements per lane, when N makes them pay) a persistent workgroup also
+// adds dy*x_hat and dy into per-lane accumulators that become its partial
+// row, and caches x and dy in LDS when they fit.  Otherwise the kernel
+// writes dx only, one row per workgroup held on chip as far as registers
+// and LDS go, and the column-sum kernel forms dgamma/dbeta.
 #pragma once
 
 #include "rn_kernels.h"
@@ -448,25 +450,208 @@ __global__ __launch_bounds__(kLongThreads) void fwd_long_kernel(const FwdArgs a)
     }
 }
 
-// Backward.  ACC: persistent grid, per-lane dgamma (and dbeta) accumulators
-// over all the workgroup's rows, written at the end as the workgroup's
-// float32 partial row (row-major: part[b*H + j], dbeta rows after
-// partial_stride(P)*H floats); rows of at most kLongAccMaxH elements.
-// Without ACC only dx is written and the column-sum kernel forms the
-// parameter gradients.  ADD: the fused add+RMSNorm backward (a.add, if set,
-// is added to dx; a.dx2, if set, receives dx as well).  `cache`: x and dy of
-// the row (two rows of long_row_pad bytes) wait in LDS between the passes.
-template <class T, class W, int VEC, bool LN, bool ADD, bool ACC>
-__global__ __launch_bounds__(kLongThreads) void bwd_long_kernel(const BwdArgs a, int cache) {
+// dx of one chunk of the backward (and, for the fused op, dh_in added and
+// the second copy stored).  LayerNorm: dx = rstd*g + (x_hat*k2 + k1) with
+// k2 = -c2*rstd, k1 = -c1*rstd; RMSNorm: dx = (g - x_hat*c2)*rstd.
+template <class T, class W, int VEC, bool LN, bool ADD>
+__device__ __forceinline__ void bwd_long_dx(const RawChunk<T, VEC> &cx,
+                                            const RawChunk<T, VEC> &cd,
+                                            const RawChunk<W, VEC> &cg,
+                                            const RawChunk<T, VEC> &ca, bool has_add,
+                                            float mu, float s, float c2, float k1, float k2,
+                                            rsrc_t rdx, rsrc_t rdx2, uint32_t off) {
+    float dx[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        const float xhat = (cx.get(k) - mu) * s;
+        const float t = cd.get(k) * cg.get(k);
+        if constexpr (LN) dx[k] = __builtin_fmaf(t, s, __builtin_fmaf(xhat, k2, k1));
+        else dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
+        if constexpr (ADD) {
+            if (has_add) dx[k] += ca.get(k);
+        }
+    }
+    bstore_chunk<VEC>((T *)nullptr, rdx, off, dx);
+    if constexpr (ADD) bstore_chunk<VEC>((T *)nullptr, rdx2, off, dx);
+}
+
+// Raw chunks of x and of dy that the backward without accumulators keeps in
+// registers: 32 registers' worth of each (24 beside float32 parameters).
+template <class T, class W, int VEC>
+constexpr int bwd_reg_segs() {
+    return (sizeof(W) > sizeof(T) ? 24 : 32) / ((VEC * (int)sizeof(T) + 3) / 4);
+}
+
+// Backward without accumulators: dx, one row per workgroup, held on chip as
+// far as it fits (segments [0, R) of x and dy in registers, the next `nlds`
+// in LDS; the rest are read again by the dx pass), then dgamma/dbeta by
+// column tiles (colsum_tiles).  ADD: the fused add+RMSNorm backward (a.add,
+// if set, is added to dx; a.dx2, if set, receives dx too).
+template <class T, class W, int VEC, bool LN, bool ADD>
+__global__ __launch_bounds__(kLongThreads) void bwd_onchip_kernel(const BwdArgs a, int nlds) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     using Raw = RawChunk<T, VEC>;
     using RawW = RawChunk<W, VEC>;
-    // with accumulators, two segments in flight (registers)
-    constexpr int U = ACC ? 2 : RN_LONG_UNROLL;
+    constexpr int R = bwd_reg_segs<T, W, VEC>();
+    // segments per group past the registers, and register segments whose
+    // parameters come together (one with float32 parameters beside 16-bit
+    // rows: twice the registers)
+    constexpr int U = sizeof(W) > sizeof(T) ? 1 : 2;
+    constexpr int G = U;
+    static_assert(R % G == 0, "whole parameter groups");
     constexpr int SPAN = kLongThreads * VEC;
-    constexpr int MAXSEG = ACC ? kLongAccMaxH / SPAN : 1;
-    static_assert(!ACC || MAXSEG % U == 0, "whole segment groups");
-    constexpr int EA = ACC ? MAXSEG * VEC : 1;
+    constexpr int ES = (int)sizeof(T);
+    extern __shared__ f32x4 lds_cache[];
+    __shared__ float red[2 * 16];
+    unsigned char *lds = (unsigned char *)lds_cache;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int nseg = (H + SPAN - 1) / SPAN;
+    const int lend = R + nlds;   // segments from here on are read twice
+    const uint32_t nb = (uint32_t)H * (uint32_t)ES;
+    const uint32_t lin = (uint32_t)nlds * (uint32_t)(SPAN * ES);   // LDS bytes of x; dy follows
+    const rsrc_t rg = make_rsrc(a.gamma, (uint32_t)H * (uint32_t)sizeof(W));
+    const T *addb = (const T *)a.add;
+    const bool has_add = ADD && addb != nullptr;
+    auto el = [&](int sgm) { return sgm * SPAN + tid * VEC; };
+    auto lslot = [&](int sgm) { return (uint32_t)(((sgm - R) * SPAN + tid * VEC) * ES); };
+    auto woff = [&](int sgm) { return el(sgm) * (int)sizeof(W); };
+    int parity = 0;
+
+    for (int64_t row = blockIdx.x; row < a.N; row += gridDim.x) {
+        const rsrc_t rx = make_rsrc((const T *)a.x + row * a.ldx, nb);
+        const rsrc_t rdy = make_rsrc((const T *)a.dy + row * a.lddy, nb);
+        const float mu = LN ? a.mean[row] : 0.0f;
+        const float s = a.rstd[row];
+        float sg = 0.0f, sgx = 0.0f;
+        auto add1 = [&](const Raw &cx, const Raw &cd, const RawW &cg) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const float xhat = (cx.get(k) - mu) * s;
+                const float gv = cd.get(k) * cg.get(k);
+                sg += gv;
+                sgx = __builtin_fmaf(gv, xhat, sgx);
+            }
+        };
+        // ---- pass 1: the row sums (and the LDS copies)
+        Raw rgx[R], rgd[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            rgx[u].template bload<RN_LOAD_AUX>(rx, el(u) * ES);
+            rgd[u].template bload<RN_LOAD_AUX>(rdy, el(u) * ES);
+        }
+        for (int s0 = R; s0 < nseg; s0 += U) {
+            Raw cx[U], cd[U];
+            RawW cg[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                cx[u].template bload<RN_LOAD_AUX>(rx, el(s0 + u) * ES);
+                cd[u].template bload<RN_LOAD_AUX>(rdy, el(s0 + u) * ES);
+                cg[u].template bload<0>(rg, woff(s0 + u));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (el(s0 + u) < H) {
+                    if (s0 + u < lend) {
+                        lds_put<T, VEC>(lds + lslot(s0 + u), cx[u]);
+                        lds_put<T, VEC>(lds + lin + lslot(s0 + u), cd[u]);
+                    }
+                    add1(cx[u], cd[u], cg[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u0 = 0; u0 < R; u0 += G) {
+            if (u0 < nseg) {
+                RawW cg[G];
+#pragma unroll
+                for (int u = 0; u < G; ++u) cg[u].template bload<0>(rg, woff(u0 + u));
+#pragma unroll
+                for (int u = 0; u < G; ++u)
+                    if (el(u0 + u) < H) add1(rgx[u0 + u], rgd[u0 + u], cg[u]);
+            }
+        }
+        // keep the held chunks packed across the reductions
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            opaque(rgx[u].v);
+            opaque(rgd[u].v);
+        }
+        const float c1 = LN ? block_sum16(sg, red, parity) * a.inv_H : 0.0f;
+        const float c2 = block_sum16(sgx, red, parity) * a.inv_H;
+        const float k2 = -c2 * s, k1 = -c1 * s;
+        // ---- pass 2: dx
+        const rsrc_t rdx = make_rsrc((T *)a.dx + row * a.lddx, nb);
+        const rsrc_t rad = make_rsrc(has_add ? addb + row * a.ldadd : (const T *)a.x,
+                                     has_add ? nb : 0u);
+        const bool two = ADD && a.dx2 != nullptr;
+        const rsrc_t rdx2 = make_rsrc(two ? (T *)a.dx2 + row * a.lddx2 : (T *)a.dx,
+                                      two ? nb : 0u);
+#pragma unroll
+        for (int u0 = 0; u0 < R; u0 += G) {
+            if (u0 < nseg) {
+                RawW cg[G];
+                Raw ca[G];
+#pragma unroll
+                for (int u = 0; u < G; ++u) {
+                    cg[u].template bload<0>(rg, woff(u0 + u));
+                    if constexpr (ADD) ca[u].template bload<RN_LOAD_AUX>(rad, el(u0 + u) * ES);
+                }
+#pragma unroll
+                for (int u = 0; u < G; ++u)
+                    bwd_long_dx<T, W, VEC, LN, ADD>(rgx[u0 + u], rgd[u0 + u], cg[u], ca[u],
+                                                    has_add, mu, s, c2, k1, k2, rdx, rdx2,
+                                                    (uint32_t)(el(u0 + u) * ES));
+            }
+        }
+        for (int s0 = R; s0 < nseg; s0 += U) {
+            Raw cx[U], cd[U], ca[U];
+            RawW cg[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sgm = s0 + u;
+                if (sgm < lend) {
+                    if (el(sgm) < H) {
+                        lds_get<T, VEC>(lds + lslot(sgm), cx[u]);
+                        lds_get<T, VEC>(lds + lin + lslot(sgm), cd[u]);
+                    } else {
+                        cx[u].zero();
+                        cd[u].zero();
+                    }
+                } else {
+                    cx[u].template bload<RN_LOAD_AUX>(rx, el(sgm) * ES);
+                    cd[u].template bload<RN_LOAD_AUX>(rdy, el(sgm) * ES);
+                }
+                cg[u].template bload<0>(rg, woff(sgm));
+                if constexpr (ADD) ca[u].template bload<RN_LOAD_AUX>(rad, el(sgm) * ES);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                bwd_long_dx<T, W, VEC, LN, ADD>(cx[u], cd[u], cg[u], ca[u], has_add, mu, s, c2,
+                                                k1, k2, rdx, rdx2, (uint32_t)(el(s0 + u) * ES));
+        }
+    }
+    colsum_tiles<T, W, VEC, LN, kLongThreads>(a);
+}
+
+// Backward with partial rows: a persistent grid whose lanes keep dgamma
+// (and dbeta) accumulators for their columns over all the workgroup's rows,
+// written at the end as the workgroup's float32 partial row (row-major:
+// part[b*H + j], dbeta rows after partial_stride(P)*H floats); rows of at
+// most kLongAccMaxH elements.  ADD: as in bwd_onchip_kernel.  `cache`: x
+// and dy of the row (two rows of long_row_pad bytes) wait in LDS between
+// the passes.
+template <class T, class W, int VEC, bool LN, bool ADD>
+__global__ __launch_bounds__(kLongThreads) void bwd_long_acc_kernel(const BwdArgs a, int cache) {
+    static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
+    using Raw = RawChunk<T, VEC>;
+    using RawW = RawChunk<W, VEC>;
+    // beside the accumulators, two segments in flight (registers)
+    constexpr int U = 2;
+    constexpr int SPAN = kLongThreads * VEC;
+    constexpr int MAXSEG = kLongAccMaxH / SPAN;
+    static_assert(MAXSEG % U == 0, "whole segment groups");
+    constexpr int EA = MAXSEG * VEC;
     extern __shared__ f32x4 lds_cache[];
     __shared__ float red[2 * 16];
     unsigned char *lds = (unsigned char *)lds_cache;
@@ -480,11 +665,11 @@ __global__ __launch_bounds__(kLongThreads) void bwd_long_kernel(const BwdArgs a,
     const bool has_add = ADD && addb != nullptr;
     int parity = 0;
 
-    float adg[EA], adb[(ACC && LN) ? EA : 1];
+    float adg[EA], adb[LN ? EA : 1];
 #pragma unroll
     for (int e = 0; e < EA; ++e) adg[e] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < ((ACC && LN) ? EA : 1); ++e) adb[e] = 0.0f;
+    for (int e = 0; e < (LN ? EA : 1); ++e) adb[e] = 0.0f;
 
     for (int64_t row = blockIdx.x; row < a.N; row += gridDim.x) {
         const rsrc_t rx = make_rsrc((const T *)a.x + row * a.ldx, nb);
@@ -519,21 +704,15 @@ __global__ __launch_bounds__(kLongThreads) void bwd_long_kernel(const BwdArgs a,
                     const float gv = dyv * cg[u].get(k);
                     sg += gv;
                     sgx = __builtin_fmaf(gv, xhat, sgx);
-                    if constexpr (ACC) {
-                        const int e = (s0 + u) * VEC + k;   // constant: s0 is unrolled
-                        adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
-                        if constexpr (LN) adb[e] += dyv;
-                    }
+                    const int e = (s0 + u) * VEC + k;   // constant: s0 is unrolled
+                    adg[e] = __builtin_fmaf(dyv, xhat, adg[e]);
+                    if constexpr (LN) adb[e] += dyv;
                 }
             }
         };
-        if constexpr (ACC) {
 #pragma unroll
-            for (int s0 = 0; s0 < MAXSEG; s0 += U)
-                if (s0 < nseg) pass1(s0);
-        } else {
-            for (int s0 = 0; s0 < nseg; s0 += U) pass1(s0);
-        }
+        for (int s0 = 0; s0 < MAXSEG; s0 += U)
+            if (s0 < nseg) pass1(s0);
         const float c1 = LN ? block_sum16(sg, red, parity) * a.inv_H : 0.0f;
         const float c2 = block_sum16(sgx, red, parity) * a.inv_H;
         // LayerNorm: dx = rstd*g + (x_hat*(-c2*rstd) + (-c1*rstd))
@@ -568,27 +747,14 @@ __global__ __launch_bounds__(kLongThreads) void bwd_long_kernel(const BwdArgs a,
                 if constexpr (ADD) ca[u].template bload<RN_LOAD_AUX>(rad, off);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t off =
-                    (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T));
-                float dx[VEC];
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float xhat = (cx[u].get(k) - mu) * s;
-                    const float t = cd[u].get(k) * cg[u].get(k);
-                    if constexpr (LN) dx[k] = __builtin_fmaf(t, s, __builtin_fmaf(xhat, k2, k1));
-                    else dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
-                    if constexpr (ADD) {
-                        if (has_add) dx[k] += ca[u].get(k);
-                    }
-                }
-                bstore_chunk<VEC>((T *)nullptr, rdx, off, dx);
-                if constexpr (ADD) bstore_chunk<VEC>((T *)nullptr, rdx2, off, dx);
-            }
+            for (int u = 0; u < U; ++u)
+                bwd_long_dx<T, W, VEC, LN, ADD>(
+                    cx[u], cd[u], cg[u], ca[ADD ? u : 0], has_add, mu, s, c2, k1, k2, rdx, rdx2,
+                    (uint32_t)(((s0 + u) * SPAN + tid * VEC) * (int)sizeof(T)));
         }
     }
 
-    if constexpr (ACC) {
+    {
         float *pg = a.part + (int64_t)blockIdx.x * H;
         float *pb = a.part + (int64_t)partial_stride(gridDim.x) * H + (int64_t)blockIdx.x * H;
 #pragma unroll
@@ -672,7 +838,7 @@ hipError_t launch_bwd_long_t(const BwdArgs &a, int P, bool colsum, void *dg, voi
                              hipStream_t s) {
     const int lds = long_cache_bytes(a.H, (int)sizeof(T), 2, long_lds_budget());
     if (!colsum) {
-        constexpr auto k = bwd_long_kernel<T, W, VEC, LN, ADD, true>;
+        constexpr auto k = bwd_long_acc_kernel<T, W, VEC, LN, ADD>;
         allow_lds<k>(lds);
         if (P > 0) {
             hipLaunchKernelGGL(k, dim3(P), dim3(kLongThreads), lds, s, a, lds > 0 ? 1 : 0);
@@ -681,18 +847,21 @@ hipError_t launch_bwd_long_t(const BwdArgs &a, int P, bool colsum, void *dg, voi
         }
         return launch_bwd2<W>(a.part, P, a.H, LN, dg, db, s);
     }
-    constexpr auto k = bwd_long_kernel<T, W, VEC, LN, ADD, false>;
-    allow_lds<k>(lds);
-    const int64_t grid = a.N < (1 << 20) ? a.N : (1 << 20);
-    if (grid > 0) {
-        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kLongThreads), lds, s, a,
-                           lds > 0 ? 1 : 0);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    constexpr int COLS = 8 * VEC;
-    hipLaunchKernelGGL((bwd_colsum_kernel<T, W, VEC, LN>), dim3((a.H + COLS - 1) / COLS),
-                       dim3(1024), 0, s, a, (W *)dg, (W *)db);
+    // dx, the row held on chip as far as registers and LDS go (LDS less the
+    // column tiles' static share), then the column tiles
+    constexpr int R = bwd_reg_segs<T, W, VEC>();
+    constexpr int SPAN = kLongThreads * VEC;
+    const int nseg = (a.H + SPAN - 1) / SPAN;
+    const int pair = 2 * SPAN * (int)sizeof(T);   // LDS bytes of one segment of x and dy
+    constexpr int tile_lds = ColsumTile<T, VEC, kLongThreads>::LDS_FLOATS * (int)sizeof(float);
+    const int budget = long_lds_budget() - tile_lds;
+    const int fit = budget > 0 ? budget / pair : 0;
+    const int nlds = nseg > R ? (nseg - R < fit ? nseg - R : fit) : 0;
+    constexpr auto k = bwd_onchip_kernel<T, W, VEC, LN, ADD>;
+    allow_lds<k>(nlds * pair);
+    const int64_t rows = a.N < (1 << 20) ? a.N : (1 << 20);
+    hipLaunchKernelGGL(k, dim3((unsigned)colsum_grid<VEC>(rows, a.H)), dim3(kLongThreads),
+                       (unsigned)(nlds * pair), s, a, nlds);
     return hipGetLastError();
 }
 
