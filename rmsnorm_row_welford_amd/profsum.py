@@ -63,13 +63,15 @@ def kernel_table(db: str):
 def _role(name: str, op: str) -> str:
     """What a kernel is to `op` in a one-op trace."""
     bwd = op.endswith("_bwd")
-    if "bwd1_kernel" in name or "bwd1_seg_kernel" in name:
+    if any(k in name for k in ("bwd1_kernel", "bwd1_seg_kernel", "bwd_onchip_kernel",
+                               "bwd_long_acc_kernel")):
         return "kernel 1" if bwd else "other"
     if "bwd2_" in name:
         return "kernel 2" if bwd else "other"
     if "bwd_colsum_kernel" in name:
         return "kernel 2 (column sums)" if bwd else "other"
-    if "fwd_kernel" in name or "fwd_seg_kernel" in name:
+    if any(k in name for k in ("fwd_kernel", "fwd_seg_kernel", "fwd_onchip_kernel",
+                               "fwd_long_kernel")):
         return "set-up forward" if bwd else "forward"
     return "other"
 
