@@ -211,14 +211,15 @@ int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype, int is_layernorm,
 /* Longest row (H) supported for `dtype`: 4194304 elements on both the 16-byte
  * path (rows whose size, stride and base addresses are multiples of 16
  * bytes) and the element-wise path (`vectorizable` = 0).  Rows of up to
- * 16384 (16-byte path) or 8192 (element-wise) elements are held in
- * registers and cross HBM once; longer rows are walked in segments by one
- * 1024-thread workgroup, cached in LDS between the statistics and the
- * output pass where they fit (160 KiB on MI355X: x for the LayerNorm and
- * RMSNorm forward, x and the residual for the fused forward, x and dy for
- * the backward) and read twice otherwise ("Write Triton Layernorm Kernel",
- * Required reasoning process, large-H loop over column blocks).  Returns 0
- * for an unknown dtype. */
+ * 16384 (16-byte path; 32768 in the forward of 2-byte rows with 2-byte
+ * parameters) or 8192 (element-wise) elements are held in the registers of
+ * the register plans; longer rows are walked in segments by one
+ * 1024-thread workgroup that keeps as much of the row as fits on chip
+ * (first in registers, then in LDS: 160 KiB on MI355X) between the
+ * statistics and the output pass and reads the rest twice ("Write Triton
+ * Layernorm Kernel", Required reasoning process, large-H loop over column
+ * blocks).  The forward holds LayerNorm/RMSNorm bf16 rows of up to 139264
+ * elements, fused rows of up to 65536.  Returns 0 for an unknown dtype. */
 int64_t rn_max_hidden(int dtype, int vectorizable);
 
 /* Text for a status code.  The argument checks behind the codes follow the

@@ -43,7 +43,8 @@ int current_cus(int *cus) {
 }  // namespace
 
 // Dynamic LDS a long-row workgroup may use: the device's per-workgroup
-// limit, less 1 KiB for the kernels' static LDS; cached per device.
+// limit, less 1 KiB for the kernels' small static LDS (the launches that
+// also take column tiles subtract those tiles' share); cached per device.
 int rn::long_lds_budget() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
