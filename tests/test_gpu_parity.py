@@ -920,12 +920,16 @@ def test_long_rows(orc, N, H, storage):
         assert torch.equal(a_, b_), "not reproducible run to run"
 
 
-@pytest.mark.parametrize("H,pad", [(20480, 24), (20480, 3), (40960, 8)])
+@pytest.mark.parametrize("H,pad", [(20480, 24), (20480, 3), (40960, 8), (98304, 8)])
 def test_long_rows_strided_in_place(orc, H, pad):
     """Long rows at a row stride of H + pad (pad 3: the element-wise path):
     the padding and a guard row stay untouched; the fused forward writes h
-    over x (at 40960 the fused rows do not fit in LDS, so x is read twice and
-    h may only be written in the second pass)."""
+    over x.  Forward paths: 20480 the 32768-element register plan (pad 3:
+    the element-wise on-chip kernel); 40960 on chip (LN: registers; fused:
+    registers and LDS); 98304 LN on chip with LDS, the fused op read twice
+    (h may only be written in the second pass, from values the same lane
+    read there).  The backward at 98304 holds part of x and dy on chip and
+    reads the rest twice."""
     N = 7
     arr = synth.custom(21, N, H, "bf16")
     SENT = -7.0
