@@ -71,7 +71,8 @@ EXTRA_OPS = ("fused_add_rms_bwd", "fused_add_rms_fwd_inplace", "unfused_add_rms"
 # gradients) and short rows (2^20 rows of 128: a normalization over a head
 # dimension), each for every op they have a workload for, and rows past the
 # register-resident plans (32768 elements: cached in LDS between the two
-# passes; 131072: read twice).
+# passes; 131072: read twice), and the other shapes of the backward page's
+# timing table (8192x1024 ... 1024x8192).
 NORM_OPS = ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd")
 ALL_OPS = NORM_OPS + ("fused_add_rms_fwd", "fused_add_rms_bwd")
 SHAPES = (
@@ -85,7 +86,9 @@ SHAPES = (
     ("rows_bf16_1048576x128", NORM_OPS),
     ("long_bf16_2048x32768", NORM_OPS + ("fused_add_rms_fwd",)),
     ("long_bf16_256x131072", NORM_OPS),
-)
+) + tuple((f"bwdtab_bf16_{n}x{h}", NORM_OPS)
+          for n, h in ((8192, 1024), (16384, 1024), (2048, 4096), (4096, 4096), (8192, 4096),
+                       (1024, 8192)))
 
 
 def log(*a):

@@ -107,6 +107,12 @@ WORKLOADS: Dict[str, Workload] = {
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
         Workload("bwd_bf16_2048x16384", 1005, 2048, 16384, "bf16", 1e-5,
                  x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1)),
+        # the other shapes of the backward page's timing table (tall, square
+        # and wide), bf16, both norms
+        *[Workload(f"bwdtab_bf16_{n}x{h}", 1012 + i, n, h, "bf16", 1e-5,
+                   x=(0.0, 1.0), gamma=(1.0, 0.1), beta=(0.0, 0.1))
+          for i, (n, h) in enumerate([(8192, 1024), (16384, 1024), (2048, 4096),
+                                      (4096, 4096), (8192, 4096), (1024, 8192)])],
         # rows past the register-resident plans: one that the LDS row cache
         # holds (x and dy of a 32768-element bf16 row: 128 KiB), one that no
         # cache holds (256 KiB rows, read twice)

@@ -258,8 +258,12 @@ def test_step_workload(orc):
     check_bwd(orc, arr, "bf16", w.eps, layernorm=False, tag=w.name)
 
 
+# the named backward workloads, then the other shapes of the backward
+# page's timing table (timed by the benchmark beside them)
 BWD = ["bwd_bf16_32768x1024", "bwd_bf16_16384x2048", "bwd_bf16_512x16384",
-       "bwd_bf16_2048x16384"]
+       "bwd_bf16_2048x16384", "bwdtab_bf16_8192x1024", "bwdtab_bf16_16384x1024",
+       "bwdtab_bf16_2048x4096", "bwdtab_bf16_4096x4096", "bwdtab_bf16_8192x4096",
+       "bwdtab_bf16_1024x8192"]
 
 
 @pytest.mark.parametrize("name", BWD)
