@@ -191,6 +191,12 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 #ifndef RN_BWD_BF16_2048
 #define RN_BWD_BF16_2048 Plan<8, 2, 2, 4, true, 1>
 #endif
+#ifndef RN_BWD_BF16_4096
+#define RN_BWD_BF16_4096 Plan<8, 2, 4, 2, true, 1>
+#endif
+#ifndef RN_BWD_BF16_8192
+#define RN_BWD_BF16_8192 Plan<8, 2, 8, 1, true, 1>
+#endif
 #ifndef RN_BWD_BF16_16384
 #define RN_BWD_BF16_16384 Plan<8, 2, 16, 1>
 #endif
@@ -244,8 +250,8 @@ using BwdPlans2B = PlanList<SegPlan<8, 8, 4, 1>,    //    64
                             Plan<8, 1, 1, 8>,       //   512
                               RN_BWD_BF16_1024,     //  1024
                               RN_BWD_BF16_2048,     //  2048
-                              Plan<8, 2, 4, 2, true, 1>,   //  4096
-                              Plan<8, 2, 8, 1, true, 1>,   //  8192
+                              RN_BWD_BF16_4096,     //  4096
+                              RN_BWD_BF16_8192,     //  8192
                               RN_BWD_BF16_16384>;   // 16384
 // float32 rows of 16 elements per lane are too wide to double-buffer.
 using BwdPlansF32 = PlanList<SegPlan<4, 8, 4, 1>,          //    32
