@@ -2,5 +2,5 @@
 #include "rn_plans.h"
 
 namespace rn {
-RN_DEFINE_FWD(bf16, bf16_bits, bf16_bits, FwdPlans2B, FusedPlans2B)
+RN_DEFINE_FWD(bf16, bf16_bits, bf16_bits, FwdPlans2B, RowPlans2B)
 }  // namespace rn

@@ -2,5 +2,5 @@
 #include "rn_plans.h"
 
 namespace rn {
-RN_DEFINE_FWD(bf16_f32w, bf16_bits, float, FwdPlans2BW, FusedPlans2BW)
+RN_DEFINE_FWD(bf16_f32w, bf16_bits, float, FwdPlans2BW, RowPlans2BW)
 }  // namespace rn

@@ -162,20 +162,23 @@ int pick_plan_int(PlanList<P, Ps...>, int H, F &&f) {
 // Rows of 4096 and 8192: LayerNorm and RMSNorm run one 1024-thread
 // workgroup per CU (teams of 4 or 8 waves) prefetching their next rows,
 // which holds the parameters in registers for all the rows; the fused op
-// (twice the row registers) runs one small workgroup per row instead.
-// Measured at 2048-8192 x 4096: 1-2 us faster for LN/RMS, 4.5 us slower for
-// the fused op at 32768 x 4096.
+// (twice the row registers) and inputs of fewer than 4 rows per CU (the
+// few-row, latency-bound regime) run one small workgroup per row group
+// instead (the RowPlans lists).  Measured: at 2048-8192 x 4096 the
+// persistent plans are 1-2 us faster for LN/RMS and 4.5 us slower for the
+// fused op at 32768 x 4096; at 1-64 rows of 4096 they take 3.3-4.3 us per
+// call against 2.0-2.8.
 #ifndef RN_FWD_BF16_4096
 #define RN_FWD_BF16_4096 Plan<8, 2, 4, 4>
 #endif
 #ifndef RN_FWD_BF16_8192
 #define RN_FWD_BF16_8192 Plan<8, 2, 8, 2>
 #endif
-#ifndef RN_FUSED_BF16_4096
-#define RN_FUSED_BF16_4096 Plan<8, 2, 4, 1, false>
+#ifndef RN_ROW_BF16_4096
+#define RN_ROW_BF16_4096 Plan<8, 2, 4, 1, false>
 #endif
-#ifndef RN_FUSED_BF16_8192
-#define RN_FUSED_BF16_8192 Plan<8, 2, 8, 1, false>
+#ifndef RN_ROW_BF16_8192
+#define RN_ROW_BF16_8192 Plan<8, 2, 8, 1, false>
 #endif
 #ifndef RN_FWD_BF16_16384
 #define RN_FWD_BF16_16384 Plan<8, 2, 16, 1>
@@ -212,18 +215,18 @@ using FwdPlans2B = PlanList<SegPlan<8, 8, 4, 2>,          //    64
                             RN_FWD_BF16_8192,             //  8192
                             RN_FWD_BF16_16384,            // 16384
                             RN_FWD_BF16_32768>;           // 32768
-using FusedPlans2B = PlanList<SegPlan<8, 8, 4, 2>, SegPlan<8, 16, 4, 2>, SegPlan<8, 32, 4, 2>,
+using RowPlans2B = PlanList<SegPlan<8, 8, 4, 2>, SegPlan<8, 16, 4, 2>, SegPlan<8, 32, 4, 2>,
                               RN_FWD_BF16_512, RN_FWD_BF16_1024, RN_FWD_BF16_2048,
-                              RN_FUSED_BF16_4096, RN_FUSED_BF16_8192, RN_FWD_BF16_16384,
+                              RN_ROW_BF16_4096, RN_ROW_BF16_8192, RN_FWD_BF16_16384,
                               RN_FWD_BF16_32768>;
 // float32 parameters take twice the registers: no 32768 plan (those rows
 // take the long-row kernels).
 using FwdPlans2BW = PlanList<SegPlan<8, 8, 4, 2>, SegPlan<8, 16, 4, 2>, SegPlan<8, 32, 4, 2>,
                              RN_FWD_BF16_512, RN_FWD_BF16_1024, RN_FWD_BF16_2048,
                              RN_FWD_BF16_4096, RN_FWD_BF16_8192, RN_FWD_BF16_16384>;
-using FusedPlans2BW = PlanList<SegPlan<8, 8, 4, 2>, SegPlan<8, 16, 4, 2>, SegPlan<8, 32, 4, 2>,
+using RowPlans2BW = PlanList<SegPlan<8, 8, 4, 2>, SegPlan<8, 16, 4, 2>, SegPlan<8, 32, 4, 2>,
                                RN_FWD_BF16_512, RN_FWD_BF16_1024, RN_FWD_BF16_2048,
-                               RN_FUSED_BF16_4096, RN_FUSED_BF16_8192, RN_FWD_BF16_16384>;
+                               RN_ROW_BF16_4096, RN_ROW_BF16_8192, RN_FWD_BF16_16384>;
 using FwdPlansF32 = PlanList<SegPlan<4, 8, 4, 2>,         //    32
                              SegPlan<4, 16, 4, 2>,        //    64
                              SegPlan<4, 32, 4, 2>,        //   128
@@ -282,16 +285,21 @@ constexpr int max_span(PlanList<Ps...>) {
     return m;
 }
 
-template <class T, class W, class VecPlans, class FusedPlans = VecPlans>
+// VecPlans: the 16-byte path's plans; RowPlans: the same row lengths with
+// one workgroup per row group wherever VecPlans run persistent teams, for
+// the fused op and for inputs of fewer than 4 rows per CU.
+template <class T, class W, class VecPlans, class RowPlans = VecPlans>
 hipError_t launch_fwd_t(int op, const FwdArgs &a, bool vec, int cus,
                         hipStream_t s) {
-    static_assert(max_span(VecPlans{}) == max_span(FusedPlans{}), "one long-row limit");
+    static_assert(max_span(VecPlans{}) == max_span(RowPlans{}), "one long-row limit");
     if (a.H > (vec ? max_span(VecPlans{}) : kMaxHiddenRegScalar))
         return vec ? launch_fwd_long<T, W, Vec16<T>::N>(op, a, s)
                    : launch_fwd_long<T, W, 1>(op, a, s);
     auto f = [&]<class P>() { return launch_fwd_any<T, W, P>(op, a, cus, s); };
     if (!vec) return pick_plan(FwdPlansScalar{}, a.H, f);
-    return op == OP_FUSED ? pick_plan(FusedPlans{}, a.H, f) : pick_plan(VecPlans{}, a.H, f);
+    const bool few = a.N < 4 * (int64_t)cus;
+    return (op == OP_FUSED || few) ? pick_plan(RowPlans{}, a.H, f)
+                                   : pick_plan(VecPlans{}, a.H, f);
 }
 
 template <class T, class W, class VecPlans>
