@@ -111,12 +111,15 @@ RN_DECLARE_STORAGE(f16_f32w)
 // Which reduction the backward uses for dgamma/dbeta.  Partial rows cost
 // 2*P*H*4 bytes per parameter (written by kernel 1, read by kernel 2); the
 // column-sum strategy instead reads x and dy a second time, 2*N*H*e bytes,
-// typically from the Infinity Cache right after kernel 1 read them.  The
-// cheaper one in bytes wins (RN_BWD_COLSUM_PCT scales the comparison).
-// Measured on MI355X, the column sums pay off only with a 2x byte margin
-// and when the row is wide enough for one 8-chunk column tile per CU.
+// in column tiles that the dx kernel takes after its rows (no second
+// launch).  The cheaper one in bytes wins, ties to the column sums
+// (RN_BWD_COLSUM_PCT scales the comparison), when the row gives at least
+// a quarter of the CUs an 8-chunk column tile.  Measured on MI355X: at
+// equal bytes the column sums win by about the second launch (512 x 16384
+// RMSNorm: 17.9 -> 16.3 us); when the tiles followed as a kernel of their
+// own they paid only with a 2x byte margin.
 #ifndef RN_BWD_COLSUM_PCT
-#define RN_BWD_COLSUM_PCT 50
+#define RN_BWD_COLSUM_PCT 100
 #endif
 // Rows each team of a backward workgroup may take before the grid grows
 // past one workgroup: with a single workgroup its partial row is already
@@ -129,7 +132,7 @@ RN_DECLARE_STORAGE(f16_f32w)
 inline bool bwd_use_colsum(int64_t N, int H, int e, int P, bool ln, int cus) {
     if (N <= 0 || P <= 0) return false;
     const int cols_per_tile = 8 * (16 / e);
-    if (H / cols_per_tile < cus) return false;
+    if (H / cols_per_tile < cus / 4) return false;
     const int64_t partial = (int64_t)8 * P * (ln ? 2 : 1);
     const int64_t reread = (int64_t)2 * N * e;
     return reread * 100 <= partial * RN_BWD_COLSUM_PCT;

@@ -854,21 +854,22 @@ def test_unsupported_sizes():
 # where they fit, and writes partial rows for rows of up to 32768 elements
 # when N makes them pay, else column sums.  Cases (forward; backward):
 #   (600, 20480, bf16)     32768-element register plan, masked tail; LDS
-#                          cache, partial rows
-#   (37, 32768, bf16)      register plan, full; cache (x and dy: 128 KiB),
-#                          column sums (few rows)
+#                          cache, RMS partial rows, LN column sums
+#   (37, 32768, bf16)      register plan, full; x and dy on chip, column
+#                          sums (few rows)
 #   (300, 32768, bf16/f32) float32 parameters: on chip in registers (two
-#                          workgroups per CU); RMS partial rows, LN column sums
-#   (3, 49152, bf16)       registers (6 segments; fused: 4 + 2 in LDS); read
-#                          twice, column sums
+#                          workgroups per CU); column sums
+#   (3, 49152, bf16)       registers (6 segments; fused: 4 + 2 in LDS);
+#                          column sums (rows past 32768 always take them)
 #   (5, 98304, bf16)       registers + 4 LDS segments (fused: read twice);
-#                          nothing cached (192 KiB rows), column sums
+#                          x and dy partly on chip, the rest read twice
 #   (30, 98304, bf16/f32)  the same with float32 parameters
-#   (600, 24576, f32)      float32 rows in registers; read twice, partial rows
+#   (600, 24576, f32)      float32 rows in registers; read twice, partial
+#                          rows (LN and RMS)
 #   (50, 40000, f32)       registers + LDS for LN/RMS (fused: read twice)
 #   (300, 8193, bf16)      element-wise path (odd H), registers, two
-#                          workgroups per CU; cache, RMS partial rows
-#   (600, 12002, f16)      element-wise (rows not 16-byte multiples);
+#                          workgroups per CU; column sums
+#   (600, 12002, f16)      element-wise (rows not 16-byte multiples); RMS
 #                          partial rows with 12 segments of accumulators
 #   (20, 24577, f16)       element-wise, the 32-segment register kernel
 #   (40, 40001, bf16)      element-wise, registers + LDS

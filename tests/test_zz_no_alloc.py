@@ -83,13 +83,13 @@ def test_noalloc_matches_workspace_entry_point(orc, first, second):
 def test_noalloc_rejects_what_does_not_fit():
     """The array holds RN_NOALLOC_MAX_WORKSPACE_BYTES: every register-plan
     shape fits; a long-row shape whose LayerNorm partial rows need more
-    (600 x 32768: 256 partial rows of 32768 floats, twice) is refused with
+    (2048 x 32768: 256 partial rows of 32768 floats, twice) is refused with
     RN_EWORKSPACE, leaving the outputs untouched."""
     bf = torch.bfloat16
     cap = 32 << 20
     for H in (1024, 2048, 4096, 8192, 16384):
         assert rn.workspace_bytes(1 << 20, H, bf, True) <= cap
-    N, H = 600, 32768
+    N, H = 2048, 32768
     assert rn.workspace_bytes(N, H, bf, True) > cap
     x = torch.randn(N, H, device=DEV).to(bf)
     g = torch.ones(H, dtype=bf, device=DEV)
