@@ -1062,14 +1062,16 @@ __device__ void colsum_tile(const BwdArgs &a, int tile, float *red) {
 #pragma unroll
     for (int k = 0; k < VEC; ++k) ag[k] = ab[k] = 0.0f;
     if (c0 < H) {
-        const T *xb = (const T *)a.x + c0;
-        const T *dyb = (const T *)a.dy + c0;
+        // pointers stepped by SL rows (no per-row products)
+        const T *xp = (const T *)a.x + c0 + slot * a.ldx;
+        const T *dp = (const T *)a.dy + c0 + slot * a.lddy;
+        const int64_t xs = (int64_t)SL * a.ldx, ds = (int64_t)SL * a.lddy;
 #pragma unroll RN_COLSUM_UNROLL
-        for (int64_t r = slot; r < N; r += SL) {
+        for (int64_t r = slot; r < N; r += SL, xp += xs, dp += ds) {
             // packed until used
             RawChunk<T, VEC> cx, cd;
-            cx.gload_nt(xb + r * a.ldx);
-            cd.gload_nt(dyb + r * a.lddy);
+            cx.gload_nt(xp);
+            cd.gload_nt(dp);
             const float mu = LN ? a.mean[r] : 0.0f;
             const float s = a.rstd[r];
 #pragma unroll
