@@ -201,7 +201,10 @@ int fused_add_rms_bwd(const void *dy, int64_t lddy, const void *h, int64_t ldh,
  * the size grows with H and with N only up to that count ("Rewrite Triton
  * normalization backward kernel_1 (#499)", Summary: bounded partial rows,
  * program count tied to the CU count).  It depends on dtype because each
- * storage pair has its own team plans, and on the device's CU count.
+ * storage pair has its own team plans, and on the device's CU count.  It
+ * is 0 when no partial rows are needed: one workgroup holds every row, or
+ * the rows are so few for their width that the backward forms dgamma/dbeta
+ * from x and dy directly.
  * Returns RN_OK and sets *bytes (0 for N = 0, without touching any GPU), or
  * RN_EINVAL (bytes NULL, device < -1, bad N/H), RN_EDTYPE, RN_EUNSUPPORTED,
  * or RN_EHIP (the device cannot be queried). */

@@ -34,7 +34,10 @@
 // LayerNorm).  The grid
 // of kernel 1 is a small multiple of the CU count, so the partial buffer
 // does not grow with N.  Kernel 2 sums the partial rows column-wise in a
-// fixed order and rounds to the parameter type.
+// fixed order and rounds to the parameter type.  When the rows are so few
+// that the partial rows would cost more than reading x and dy again, kernel
+// 1 writes dx only and then forms dgamma/dbeta itself, column tile by
+// column tile (the column-sum strategy, one launch).
 #pragma once
 
 #include <atomic>
@@ -552,8 +555,8 @@ __host__ __device__ constexpr int bwd1_lds_floats(int RT, int H, bool ln) {
 }
 
 // ACC: accumulate dy*x_hat (and dy) and write partial rows; without it the
-// kernel only writes dx (the column-sum strategy computes the parameter
-// gradients separately).  ADD (RMSNorm only): the fused add+RMSNorm
+// kernel writes dx and then takes its share of the column tiles that form
+// dgamma/dbeta (the column-sum strategy).  ADD (RMSNorm only): the fused add+RMSNorm
 // backward, where x is the stored h, a.add (if set) is added to dx and
 // a.dx2 (if set) receives the same values as dx.
 // KEEP (plans that run one workgroup of at most 8 waves per CU, which
@@ -1042,6 +1045,7 @@ hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void 
 // columns: 8 lanes across the columns (one chunk each) times THREADS/8 row
 // slots; slot j adds rows j, j + THREADS/8, ... in increasing order, and the
 // slots are then added in a fixed two-level order through LDS.
+//
 // Row iterations of a column tile whose loads are issued together.
 #ifndef RN_COLSUM_UNROLL
 #define RN_COLSUM_UNROLL 2

@@ -33,8 +33,9 @@
 // 32 elements per lane, when N makes them pay) a persistent workgroup also
 // adds dy*x_hat and dy into per-lane accumulators that become its partial
 // row, and caches x and dy in LDS when they fit.  Otherwise the kernel
-// writes dx only, one row per workgroup held on chip as far as registers
-// and LDS go, and the column-sum kernel forms dgamma/dbeta.
+// writes dx, one row per workgroup held on chip as far as registers and LDS
+// go, and then takes its share of the column tiles that form dgamma/dbeta
+// from x and dy (colsum_tiles).
 #pragma once
 
 #include "rn_kernels.h"
