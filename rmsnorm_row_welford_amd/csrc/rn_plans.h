@@ -247,8 +247,11 @@ using FwdPlansScalar = PlanList<SegPlan<1, 8, 4, 2>,   //     8
                                 Plan<1, 8, 16, 1>>; //  8192
 
 // ------------------------------------------------------------ backward --
+#ifndef RN_BWD_BF16_128
+#define RN_BWD_BF16_128 SegPlan<8, 16, 4, 1>
+#endif
 using BwdPlans2B = PlanList<SegPlan<8, 8, 4, 1>,    //    64
-                            SegPlan<8, 16, 4, 1>,   //   128
+                              RN_BWD_BF16_128,      //   128
                             SegPlan<8, 32, 4, 1>,   //   256
                             Plan<8, 1, 1, 8>,       //   512
                               RN_BWD_BF16_1024,     //  1024

@@ -217,6 +217,12 @@ void fwd_seg_kernel(const FwdArgs a) {
     }
 }
 
+// The short-row backward requests a wave's next row group before it works on
+// the current one (1), or fetches each group when its turn comes (0).
+#ifndef RN_SEG_BWD_PF
+#define RN_SEG_BWD_PF 1
+#endif
+
 // Backward kernel 1.  Persistent: wave w of workgroup b takes row groups
 // b*WPG + w, += gridDim.x*WPG, each of 64/SEG rows; every lane accumulates
 // dy*x_hat (and dy) for its VEC columns over all its rows.  At the end the
@@ -251,31 +257,48 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
     const bool has_add = ADD && addb != nullptr;
 
     const int64_t gstep = (int64_t)gridDim.x * WPG;
-    for (int64_t gi = (int64_t)blockIdx.x * WPG + wave; gi * RPW < N; gi += gstep) {
-        const int64_t row0 = gi * RPW;
-        const int n = (int)(N - row0 < RPW ? N - row0 : RPW);
+    // A row group's chunks and statistics.  Every group issues the same
+    // loads through wave-uniform buffer resources: a group past N reads an
+    // empty range (0, nothing touched), and the statistics of row seg are
+    // the word at seg*4 of a range of n words.
+    struct Grp {
         Raw cx, cdy, cad;
-        cx.template bload<RN_LOAD_AUX>(group_rsrc<T>(a.x, row0, n, a.ldx, H),
-                                       seg_off<T, VEC>(seg, sl, a.ldx, valid));
-        cdy.template bload<RN_LOAD_AUX>(group_rsrc<T>(a.dy, row0, n, a.lddy, H),
-                                        seg_off<T, VEC>(seg, sl, a.lddy, valid));
-        if constexpr (ADD) {
-            if (has_add)
-                cad.template bload<RN_LOAD_AUX>(group_rsrc<T>(addb, row0, n, a.ldadd, H),
-                                                seg_off<T, VEC>(seg, sl, a.ldadd, valid));
-            else
-                cad.zero();
-        }
-        const bool live = seg < n;
-        const float mu = (LN && live) ? a.mean[row0 + seg] : 0.0f;
-        const float s = live ? a.rstd[row0 + seg] : 0.0f;
-
+        float mu, s;
+    };
+    auto rows_in = [&](int64_t gi) -> int {
+        const int64_t left = N - gi * RPW;
+        return left <= 0 ? 0 : (left < RPW ? (int)left : RPW);
+    };
+    auto fetch = [&](int64_t gi, Grp &b) {
+        const int n = rows_in(gi);
+        const int64_t r0 = n > 0 ? gi * RPW : 0;
+        b.cx.template bload<RN_LOAD_AUX>(group_rsrc<T>(a.x, r0, n, a.ldx, H),
+                                         seg_off<T, VEC>(seg, sl, a.ldx, valid));
+        b.cdy.template bload<RN_LOAD_AUX>(group_rsrc<T>(a.dy, r0, n, a.lddy, H),
+                                          seg_off<T, VEC>(seg, sl, a.lddy, valid));
+        if constexpr (ADD)
+            b.cad.template bload<RN_LOAD_AUX>(
+                group_rsrc<T>(has_add ? addb : (const T *)a.x, r0, has_add ? n : 0,
+                              has_add ? a.ldadd : a.ldx, H),
+                seg_off<T, VEC>(seg, sl, has_add ? a.ldadd : a.ldx, valid));
+        const uint32_t so = (uint32_t)seg * 4u;
+        b.mu = LN ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               make_rsrc(a.mean + r0, 4u * n), so, 0, 0))
+                  : 0.0f;
+        b.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            make_rsrc(a.rstd + r0, 4u * n), so, 0, 0));
+    };
+    // dx of row group gi (n > 0 rows) from its fetched chunks
+    auto work = [&](const Grp &b, int64_t gi) {
+        const int64_t row0 = gi * RPW;
+        const int n = rows_in(gi);
+        const float mu = b.mu, s = b.s;
         // Masked elements and rows past N have dy = 0 and add nothing.
         float sg = 0.0f, sgx = 0.0f;
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float dyv = cdy.get(k);
-            const float xhat = (cx.get(k) - mu) * s;
+            const float dyv = b.cdy.get(k);
+            const float xhat = (b.cx.get(k) - mu) * s;
             const float gv = dyv * g.get(k);
             adg[k] = __builtin_fmaf(dyv, xhat, adg[k]);
             if constexpr (LN) adb[k] += dyv;
@@ -290,22 +313,57 @@ __global__ __launch_bounds__(64 * WPG) void bwd1_seg_kernel(const BwdArgs a) {
         float dx[VEC];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float xhat = (cx.get(k) - mu) * s;
-            float t = cdy.get(k) * g.get(k);
+            const float xhat = (b.cx.get(k) - mu) * s;
+            float t = b.cdy.get(k) * g.get(k);
             if constexpr (LN && RN_BWD_FOLD) {
                 dx[k] = __builtin_fmaf(t, s, __builtin_fmaf(xhat, k2, k1));
             } else {
                 if constexpr (LN) t -= c1;
                 dx[k] = __builtin_fmaf(-xhat, c2, t) * s;
             }
-            if constexpr (ADD) dx[k] += cad.get(k);
+            if constexpr (ADD) dx[k] += b.cad.get(k);
         }
         bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.dx, row0, n, a.lddx, H),
                           seg_off<T, VEC>(seg, sl, a.lddx, valid), dx);
         if constexpr (ADD) {
-            if (a.dx2 != nullptr)
-                bstore_chunk<VEC>((T *)nullptr, group_rsrc<T>(a.dx2, row0, n, a.lddx2, H),
-                                  seg_off<T, VEC>(seg, sl, a.lddx2, valid), dx);
+            // no second copy: the same store into an empty range
+            const bool two = a.dx2 != nullptr;
+            bstore_chunk<VEC>((T *)nullptr,
+                              group_rsrc<T>(two ? a.dx2 : a.dx, row0, two ? n : 0,
+                                            two ? a.lddx2 : a.lddx, H),
+                              seg_off<T, VEC>(seg, sl, two ? a.lddx2 : a.lddx, valid), dx);
+        }
+    };
+    int64_t gi = (int64_t)blockIdx.x * WPG + wave;
+    if constexpr (RN_SEG_BWD_PF) {
+        // Two buffers in turn: a wave's next group is requested before it
+        // works on the current one (a copy between the buffers would make
+        // the wave wait for the request it has just made).
+        Grp ga, gb;
+        fetch(gi, ga);
+        // work's stores, into an empty range: the loop is entered with the
+        // memory operations in flight that its back edge has, so the wait
+        // for a group's loads need not also wait for the last store
+        {
+            float z[VEC] = {};
+            const rsrc_t none = group_rsrc<T>(a.dx, 0, 0, a.lddx, H);
+            bstore_chunk<VEC>((T *)nullptr, none, 0u, z);
+            if constexpr (ADD) bstore_chunk<VEC>((T *)nullptr, none, 0u, z);
+        }
+        while (gi * RPW < N) {
+            fetch(gi + gstep, gb);
+            work(ga, gi);
+            gi += gstep;
+            if (gi * RPW >= N) break;
+            fetch(gi + gstep, ga);
+            work(gb, gi);
+            gi += gstep;
+        }
+    } else {
+        for (; gi * RPW < N; gi += gstep) {
+            Grp cur;
+            fetch(gi, cur);
+            work(cur, gi);
         }
     }
 

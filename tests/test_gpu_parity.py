@@ -363,6 +363,19 @@ def test_short_rows(orc, storage, H):
     check_fused_bwd(orc, arr, dtype, 1e-6)
 
 
+# Short rows in numbers that make every wave of the persistent backward grid
+# take several row groups, ending on a ragged group: the row group after a
+# wave's last one is requested too, and must read nothing and change nothing.
+@pytest.mark.parametrize("storage,H", [("bf16", 24), ("bf16", 128), ("bf16", 200),
+                                       ("f32", 40), ("f16/f32", 7)])
+def test_short_rows_persistent_tail(orc, storage, H):
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(700 + H, 150001, H, dtype, wdtype=wdt or None)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
+    check_bwd(orc, arr, dtype, 1e-5, layernorm=False)
+    check_fused_bwd(orc, arr, dtype, 1e-6)
+
+
 def test_qk_norm_bf16_1048576x128(orc):
     """Head-dimension rows (a million rows of 128), every row."""
     w = synth.WORKLOADS["rows_bf16_1048576x128"]
