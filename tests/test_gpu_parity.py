@@ -323,12 +323,9 @@ SHAPES = [64, 128, 256, 512, 768, 1024, 2048, 2049, 1, 2, 3, 1000, 3000, 4095,
 STORAGE = ["bf16", "f32", "f16", "bf16/f32", "f16/f32"]
 
 
-@pytest.mark.parametrize("storage", STORAGE)
-@pytest.mark.parametrize("H", SHAPES)
-def test_shapes_all_ops(orc, storage, H):
-    N = 67 if H <= 4096 else 19
-    dtype, _, wdt = storage.partition("/")
-    arr = synth.custom(100 + H, N, H, dtype, wdtype=wdt or None)
+def check_all_ops(orc, arr, dtype):
+    """Every op on one input set: LN and RMS forward and backward, the fused
+    forward (h bit-exact) and the fused backward."""
     check_ln_fwd(orc, arr, dtype, 1e-5)
     check_rms_fwd(orc, arr, dtype, 1e-5)
     check_bwd(orc, arr, dtype, 1e-5, layernorm=True)
@@ -343,6 +340,41 @@ def test_shapes_all_ops(orc, storage, H):
     tol.check_out(host(y), y_o, dtype, orc, f"edge: fused y {dtype}", strict=True)
     tol.check_rstd(host(rstd), r_o, "edge: fused rstd")
     check_fused_bwd(orc, arr, dtype, 1e-6)
+
+
+@pytest.mark.parametrize("storage", STORAGE)
+@pytest.mark.parametrize("H", SHAPES)
+def test_shapes_all_ops(orc, storage, H):
+    N = 67 if H <= 4096 else 19
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(100 + H, N, H, dtype, wdtype=wdt or None)
+    check_all_ops(orc, arr, dtype)
+
+
+def _sweep_cases(n=120, seed=20261202):
+    """(N, H, storage) drawn log-uniformly: H in [1, 140000] (every plan, the
+    segment and long-row kernels, masked tails and the element-wise path),
+    N in [1, 4000] with N*H at most about 3 M elements (the persistent
+    grids' rounds, the few-row plans and the one-workgroup backward)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = max(1, int(np.exp(rng.uniform(0.0, np.log(140000.0)))))
+        N = max(1, int(np.exp(rng.uniform(0.0, np.log(4000.0)))))
+        N = min(N, max(1, (3 << 20) // H))
+        out.append((N, H, STORAGE[int(rng.integers(len(STORAGE)))]))
+    return out
+
+
+# A seeded sweep of shapes and storage pairs that no list above was written
+# for, every op against the oracle.
+@pytest.mark.parametrize("case", list(enumerate(_sweep_cases())),
+                         ids=lambda c: f"{c[0]}-{c[1][0]}x{c[1][1]}-{c[1][2]}")
+def test_shape_sweep(orc, case):
+    i, (N, H, storage) = case
+    dtype, _, wdt = storage.partition("/")
+    arr = synth.custom(5000 + i, N, H, dtype, wdtype=wdt or None)
+    check_all_ops(orc, arr, dtype)
 
 
 # Short rows, several per wave: every segment width (8, 16, 32 lanes) on the
