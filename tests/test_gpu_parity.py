@@ -446,17 +446,11 @@ STRIDED = [(H, pad) for H in (1024, 128, 40, 24, 4096) for pad in (24, 3)] + \
           [(8192, 24), (16384, 24), (16384, 40)]
 
 
-@pytest.mark.parametrize("H,pad", STRIDED)
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_strided_rows_and_canaries(orc, dtype, pad, H):
-    """Row strides > H (pad 24 or 40 keeps 16-byte rows, pad 3 forces the
-    element-wise path): the padding between rows and a guard row after the
-    last row stay untouched, and results match the oracle.  Short rows run
-    several rows per wave, addressed through one range per row group; 16384
-    runs the persistent plan, whose ring reads rows past N from empty
-    ranges."""
-    N = 33
-    arr = synth.custom(11, N, H, dtype)
+def check_strided(orc, dtype, pad, H, N=33, seed=11):
+    """Rows at stride H + pad: LN and RMS forward and backward and the fused
+    forward leave the padding between rows and a guard row after the last
+    row untouched, and match the oracle."""
+    arr = synth.custom(seed, N, H, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     SENT = -7.0
 
@@ -470,13 +464,16 @@ def test_strided_rows_and_canaries(orc, dtype, pad, H):
         return t.as_strided((N, H), (H + pad, 1))
 
     X, DY, R = buf(arr["x"]), buf(arr["dy"]), buf(arr["residual"])
-    Y, DX, HH, Y2 = buf(), buf(), buf(), buf()
+    Y, DX, HH, Y2, Y3, DX3 = buf(), buf(), buf(), buf(), buf(), buf()
     g, b = to_dev(arr["gamma"]), to_dev(arr["beta"])
     _, mean, rstd = rn.ln_fwd(view(X), g, b, 1e-5, y=view(Y))
     rn.ln_bwd(view(DY), view(X), g, mean, rstd, 1e-5, dx=view(DX))
     rn.fused_add_rms_fwd(view(X), view(R), g, 1e-6, y=view(Y2), h=view(HH))
+    _, rstd3 = rn.rms_fwd(view(X), g, 1e-5, y=view(Y3))
+    _, dg3 = rn.rms_bwd(view(DY), view(X), g, rstd3, 1e-5, dx=view(DX3))
     torch.cuda.synchronize()
-    for t, name in ((Y, "y"), (DX, "dx"), (HH, "h"), (Y2, "fused y")):
+    for t, name in ((Y, "y"), (DX, "dx"), (HH, "h"), (Y2, "fused y"), (Y3, "RMS y"),
+                    (DX3, "RMS dx")):
         hb = t.float().cpu().numpy()
         assert np.all(hb[:N, H:] == SENT), f"{name}: row padding written"
         assert np.all(hb[N, :] == SENT), f"{name}: guard row written"
@@ -491,6 +488,44 @@ def test_strided_rows_and_canaries(orc, dtype, pad, H):
                   term_scale=tol.dx_term_scale(dyd, gd, r_o))
     h_o = xd + orc.decode(arr["residual"], dtype)
     assert np.array_equal(host(HH[:N, :H].contiguous()), orc.encode(h_o, dtype))
+    y3_o, _ = orc.rms_fwd(xd, gd, e)
+    tol.check_out(host(Y3[:N, :H].contiguous()), y3_o, dtype, orc,
+                  f"edge: strided RMS y {dtype}", strict=True)
+    dx3_o, dg3_o, r3_o = orc.rms_bwd(dyd, xd, gd, e)
+    tol.check_out(host(DX3[:N, :H].contiguous()), dx3_o, dtype, orc,
+                  f"edge: strided RMS dx {dtype}", term_scale=tol.dx_term_scale(dyd, gd, r3_o))
+    tol.check_param(orc.decode(host(dg3), dtype), dg3_o, "edge: strided RMS dgamma")
+
+
+@pytest.mark.parametrize("H,pad", STRIDED)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_rows_and_canaries(orc, dtype, pad, H):
+    """Row strides > H (pad 24 or 40 keeps 16-byte rows, pad 3 forces the
+    element-wise path).  Short rows run several rows per wave, addressed
+    through one range per row group; 16384 runs the persistent plan, whose
+    ring reads rows past N from empty ranges."""
+    check_strided(orc, dtype, pad, H)
+
+
+def _strided_cases(n=40, seed=7702):
+    """(N, H, pad, dtype): H log-uniform in [1, 70000], pads that keep or
+    break 16-byte rows, N up to 600 (about 2 M elements at most)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = max(1, int(np.exp(rng.uniform(0.0, np.log(70000.0)))))
+        N = max(1, int(np.exp(rng.uniform(0.0, np.log(600.0)))))
+        N = min(N, max(1, (2 << 20) // H))
+        pad = int(rng.choice([1, 3, 8, 24, 40, 129]))
+        out.append((N, H, pad, ["bf16", "f32"][int(rng.integers(2))]))
+    return out
+
+
+@pytest.mark.parametrize("case", list(enumerate(_strided_cases())),
+                         ids=lambda c: f"{c[0]}-{c[1][0]}x{c[1][1]}+{c[1][2]}-{c[1][3]}")
+def test_strided_sweep(orc, case):
+    i, (N, H, pad, dtype) = case
+    check_strided(orc, dtype, pad, H, N=N, seed=6000 + i)
 
 
 @pytest.mark.parametrize("alias", ["x", "residual"])
