@@ -57,6 +57,9 @@
 
 #include <stddef.h>
 #include <stdint.h>
+/* hipStream_t.  hipcc defines __HIP_PLATFORM_AMD__ itself; a plain C or C++
+ * compiler needs -D__HIP_PLATFORM_AMD__ and the ROCm include directory, and
+ * links with -lrownorm. */
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus

@@ -265,3 +265,39 @@ def test_add_argument_errors(L):
     assert L.rn_add(X + 1, Y, H_, 8, BF16, S) == EINVAL
     assert L.rn_add(X, Y, X + 4, 8, BF16, S) == EOVERLAP
     assert L.rn_add(X, Y, Y + 4, 8, F32, S) == EOVERLAP
+
+
+def test_headers_serve_a_plain_c_caller(L, tmp_path):
+    """Both headers compile as C99 with gcc (not hipcc), and a C program that
+    takes the address of every declared function links against
+    librownorm.so and runs the device-free workspace query."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    rocm_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(rocm_inc):
+        pytest.skip("needs gcc and the ROCm headers")
+    names = sorted(declarations())
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include "rownorm.h"\n#include "rownorm_bench.h"\n#include <stdio.h>\n'
+        "int main(void) {\n"
+        "    void *fns[] = {" + ", ".join(f"(void *)&{n}" for n in names) + "};\n"
+        "    size_t bytes = 123;\n"
+        "    int st = rn_bwd_workspace_bytes(0, 1024, RN_BF16, 1, -1, &bytes);\n"
+        '    printf("%d %zu %d %s\\n", st, bytes, (int)(sizeof fns / sizeof fns[0]),\n'
+        "           rn_status_str(RN_EOVERLAP));\n"
+        "    return 0;\n}\n")
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(rn.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration",
+                        "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+                        "-I" + rocm_inc, str(src), "-L" + libdir, "-lrownorm",
+                        "-Wl,-rpath," + libdir, "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    st, nbytes, nfn, msg = out.stdout.split(" ", 3)
+    assert (int(st), int(nbytes), int(nfn)) == (OK, 0, len(names))
+    assert msg.strip() == L.rn_status_str(EOVERLAP).decode()
