@@ -180,6 +180,28 @@ def generate(w: Workload, N: Optional[int] = None, H: Optional[int] = None,
     return out
 
 
+def device_normal(seed: int, shape, mu: float, sigma: float, dtype: str, device,
+                  chunk_rows: int = 1 << 18):
+    """A seeded draw made on the GPU, for tensors too large to draw on the
+    host: ``mu + sigma * z`` with z from torch's generator for ``device``
+    seeded with ``seed`` (binary32 standard normals, drawn in blocks of
+    ``chunk_rows`` rows), rounded to the storage type by torch's cast
+    (round-to-nearest-even).  Returns a torch tensor of that type on
+    ``device``; the same seed and shape give the same bytes."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=tdt, device=device)
+    flat = out.view(-1, shape[-1]) if len(shape) > 1 else out.view(1, -1)
+    for r0 in range(0, flat.shape[0], chunk_rows):
+        r1 = min(r0 + chunk_rows, flat.shape[0])
+        z = torch.randn((r1 - r0, flat.shape[1]), generator=gen, device=device,
+                        dtype=torch.float32)
+        flat[r0:r1] = (mu + sigma * z).to(tdt)
+    return out
+
+
 def custom(seed: int, N: int, H: int, dtype: str, x=(0.0, 1.0),
            gamma=(1.0, 0.1), beta=(0.0, 0.1), residual=(0.0, 1.0),
            dy=(0.0, 1.0), half_shifted=None, dh=(0.0, 1.0), wdtype=None

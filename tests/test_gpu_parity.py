@@ -712,6 +712,87 @@ def test_wide_rows(orc, N, H, storage):
         assert torch.equal(a_, b_), "not reproducible run to run"
 
 
+def test_tensors_past_4gib(orc):
+    """Row tensors of more than 4 GiB: 2^21 + 5 rows of 1024 bf16, so the
+    byte offset of every row from 2^21 on is at or past 2^32.  Every op runs
+    once at that size (inputs drawn on the GPU, seeded: synth.device_normal).
+    y, h, mean, rstd and dx of rows on both sides of the 2^32-byte mark and
+    of the last rows are compared with the oracle (each row's outputs depend
+    on that row alone).  dbeta and dgamma, which sum every row, are checked
+    against their definitions evaluated in float64 over all rows: dbeta =
+    the column sums of dy, dgamma = the column sums of dy * (x - mean) * rstd
+    with the saved statistics (float32 parameters, so the sums come back
+    unrounded)."""
+    N, H = (1 << 21) + 5, 1024
+    assert (1 << 21) * H * 2 == 1 << 32
+    bf = torch.bfloat16
+    x = synth.device_normal(7001, (N, H), 0.0, 1.0, "bf16", DEV)
+    r = synth.device_normal(7002, (N, H), 0.0, 1.0, "bf16", DEV)
+    dy = synth.device_normal(7003, (N, H), 0.0, 1.0, "bf16", DEV)
+    g = synth.device_normal(7004, (H,), 1.0, 0.1, "f32", DEV)
+    b = synth.device_normal(7005, (H,), 0.0, 0.1, "f32", DEV)
+    rows = [0, 1, 1 << 20, (1 << 21) - 1, 1 << 21, (1 << 21) + 1, N - 2, N - 1]
+    e = oracle.eps_at_boundary(1e-5)
+    gd = host(g).astype(np.float64)
+    bd = host(b).astype(np.float64)
+
+    def rows_of(t):
+        return host(t[rows].contiguous())
+
+    xd = orc.decode(rows_of(x), "bf16")
+    rd = orc.decode(rows_of(r), "bf16")
+    dyd = orc.decode(rows_of(dy), "bf16")
+
+    y, mean, rstd = rn.ln_fwd(x, g, b, 1e-5)
+    torch.cuda.synchronize()
+    y_o, m_o, r_o = orc.ln_fwd(xd, gd, bd, e)
+    tol.check_out(rows_of(y), y_o, "bf16", orc, "edge: past 4 GiB LN y")
+    tol.check_mean(host(mean[rows]), m_o, 1.0 / (r_o * r_o) - e, e, "edge: past 4 GiB LN mean")
+    tol.check_rstd(host(rstd[rows]), r_o, "edge: past 4 GiB LN rstd")
+    dx, dg, db = rn.ln_bwd(dy, x, g, mean, rstd, 1e-5)
+    torch.cuda.synchronize()
+    dx_o, _, _, _, rs_o = orc.ln_bwd(dyd, xd, gd, e)
+    tol.check_out(rows_of(dx), dx_o, "bf16", orc, "edge: past 4 GiB LN dx",
+                  term_scale=tol.dx_term_scale(dyd, gd, rs_o))
+    # dgamma / dbeta against their definitions over all rows, in float64
+    want_dg = torch.zeros(H, dtype=torch.float64, device=DEV)
+    want_db = torch.zeros(H, dtype=torch.float64, device=DEV)
+    for r0 in range(0, N, 1 << 18):
+        sl = slice(r0, min(r0 + (1 << 18), N))
+        d64 = dy[sl].double()
+        xh = (x[sl].double() - mean[sl].double()[:, None]) * rstd[sl].double()[:, None]
+        want_dg += (d64 * xh).sum(0)
+        want_db += d64.sum(0)
+        del d64, xh
+    tol.check_param(host(dg).astype(np.float64), host(want_dg), "edge: past 4 GiB dgamma")
+    tol.check_param(host(db).astype(np.float64), host(want_db), "edge: past 4 GiB dbeta")
+    del dx, y
+
+    y2, rs2 = rn.rms_fwd(x, g, 1e-5)
+    torch.cuda.synchronize()
+    y_o, r_o = orc.rms_fwd(xd, gd, e)
+    tol.check_out(rows_of(y2), y_o, "bf16", orc, "edge: past 4 GiB RMS y", strict=True)
+    tol.check_rstd(host(rs2[rows]), r_o, "edge: past 4 GiB RMS rstd")
+    dx2, dg2 = rn.rms_bwd(dy, x, g, rs2, 1e-5)
+    torch.cuda.synchronize()
+    dx_o, _, rs_o = orc.rms_bwd(dyd, xd, gd, e)
+    tol.check_out(rows_of(dx2), dx_o, "bf16", orc, "edge: past 4 GiB RMS dx",
+                  term_scale=tol.dx_term_scale(dyd, gd, rs_o))
+    want_dg.zero_()
+    for r0 in range(0, N, 1 << 18):
+        sl = slice(r0, min(r0 + (1 << 18), N))
+        want_dg += (dy[sl].double() * (x[sl].double() * rs2[sl].double()[:, None])).sum(0)
+    tol.check_param(host(dg2).astype(np.float64), host(want_dg), "edge: past 4 GiB RMS dgamma")
+    del dx2, y2
+
+    y3, h3, rs3 = rn.fused_add_rms_fwd(x, r, g, 1e-5)
+    torch.cuda.synchronize()
+    y_o, h_o, r_o = orc.fused_add_rms_fwd(xd, rd, gd, e)
+    assert np.array_equal(rows_of(h3), orc.encode(h_o, "bf16")), "h not RNE(x + r)"
+    tol.check_out(rows_of(y3), y_o, "bf16", orc, "edge: past 4 GiB fused y", strict=True)
+    tol.check_rstd(host(rs3[rows]), r_o, "edge: past 4 GiB fused rstd")
+
+
 @pytest.mark.parametrize("N", [0, 1, 2, 7, 255, 513])
 def test_row_counts(orc, N):
     """N = 0 (no rows: dgamma = dbeta = 0), N below the partial-row count,
