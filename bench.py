@@ -365,6 +365,33 @@ def time_shapes(rn, dev, names=None, cold_bytes=1 << 30, K=24, only_ops=None):
     return out
 
 
+def bwd_plan(rn, N, H, dtype, wdtype, op, cus):
+    """The backward's dgamma/dbeta reduction at (N, H) as the library sizes
+    it: the partial rows its workspace holds (P_eff; 0 when none are needed:
+    the column sums of the rows, or one workgroup writing dgamma/dbeta
+    itself) and P_eff per CU (k)."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    p = rn.bwd_partial_rows(N, H, tdt[dtype], op == "ln_bwd",
+                            param_dtype=tdt[wdtype or dtype])
+    return {"partial_rows": p, "per_cu": round(p / cus, 3),
+            "reduction": "partial rows + kernel 2" if p else
+                         "column sums or one workgroup (no partial rows)"}
+
+
+def annotate(rn, dev, table, N, H, dtype, wdtype, copy_gbs):
+    """Adds to each op's entry its share of the copy ceiling measured in
+    the same run and, for the backward ops, the reduction's plan."""
+    import torch
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for k, v in table.items():
+        if not isinstance(v, dict) or "GBps" not in v:
+            continue
+        v["pct_copy_ceiling"] = round(100 * v["GBps"] / copy_gbs, 1)
+        if k in ("ln_bwd", "rms_bwd", "fused_add_rms_bwd"):
+            v.update(bwd_plan(rn, N, H, dtype, wdtype, k, cus))
+
+
 def decode_latency(rn, dev, H=4096, Ns=(1, 16, 64), K=50, reps=5):
     """us per call of every op at decode-size N, from graph replays (data in
     cache, so this is the launch-bound regime: kernels plus the gaps between
@@ -653,6 +680,10 @@ def main():
         shapes = time_shapes(rn, dev)
     ceil = stream_ceilings(rn, dev)
     copy_gbs = ceil["copy"]["GBps"]
+    annotate(rn, dev, per_op, N, H, w.dtype, w.wdtype, copy_gbs)
+    for name, row in (shapes or {}).items():
+        annotate(rn, dev, row, row["N"], row["H"], row["dtype"], row["param_dtype"],
+                 copy_gbs)
     for k, v in ceil.items():
         log(f"{k} stream ceiling {v['GBps']:.0f} GB/s ({100 * v['GBps'] / PEAK_GBS:.1f}% of peak)")
 

@@ -35,6 +35,16 @@ int rn_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 int rn_add(const void *a, const void *b, void *out, int64_t n, int dtype,
            hipStream_t stream);
 
+/* How the backward at (N, H) on the current device reduces dgamma/dbeta on
+ * the 16-byte vector path (vectorizable != 0) or the element-wise path:
+ * *rows receives the number of float32 partial rows kernel 1 writes per
+ * parameter (the persistent grid P, which does not grow with N), or 0 when
+ * it writes none (the column sums of the rows, or a single workgroup that
+ * writes dgamma/dbeta itself).  For reports: bench.py prints it beside each
+ * backward's time.  Status codes as for the backward entry points. */
+int rn_bwd_partial_rows(int64_t N, int64_t H, int dtype, int is_layernorm,
+                        int vectorizable, int *rows);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "RN_OK", -1: "RN_EINVAL", -2: "RN_EDTYPE",
                 -6: "RN_EUNSUPPORTED"}
 
 # name -> (argtypes, restype); mirrors include/rownorm.h and (the benchmark
-# helpers rn_copy, rn_add) include/rownorm_bench.h
+# helpers rn_copy, rn_add, rn_bwd_partial_rows) include/rownorm_bench.h
 _P, _I64, _I, _F, _SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                          ctypes.c_float, ctypes.c_size_t)
 SIGNATURES = {
@@ -47,6 +47,7 @@ SIGNATURES = {
     "rn_status_str": ([_I], ctypes.c_char_p),
     "rn_copy": ([_P, _P, _SZ, _P], _I),
     "rn_add": ([_P, _P, _P, _I64, _I, _P], _I),
+    "rn_bwd_partial_rows": ([_I64, _I64, _I, _I, _I, ctypes.POINTER(_I)], _I),
 }
 
 _lib = None
@@ -336,6 +337,18 @@ def fused_add_rms_bwd(dy, h, gamma, rstd, eps=1e-6, *, dh_in=None, dx=None,
 # ------------------------------------------------------------------ misc --
 def max_hidden(dtype_code: int, vectorizable: bool = True) -> int:
     return int(lib().rn_max_hidden(dtype_code, 1 if vectorizable else 0))
+
+
+def bwd_partial_rows(N, H, dtype, layernorm: bool, param_dtype=None,
+                     vectorizable: bool = True) -> int:
+    """The float32 partial rows per parameter the backward's kernel 1
+    writes at (N, H) on the current device (0: none, the column sums or one
+    workgroup); see rn_bwd_partial_rows."""
+    code = _code_of(dtype, dtype if param_dtype is None else param_dtype)
+    out = ctypes.c_int(0)
+    _check("rn_bwd_partial_rows", lib().rn_bwd_partial_rows(
+        N, H, code, 1 if layernorm else 0, 1 if vectorizable else 0, ctypes.byref(out)))
+    return int(out.value)
 
 
 def copy(src, dst, nbytes=None, stream=None):

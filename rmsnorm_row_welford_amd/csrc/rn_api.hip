@@ -295,6 +295,28 @@ static int workspace_bytes_here(int64_t N, int64_t H, int dtype, int is_layernor
     return RN_OK;
 }
 
+extern "C" int rn_bwd_partial_rows(int64_t N, int64_t H, int dtype, int is_layernorm,
+                                   int vectorizable, int *rows) {
+    if (!rows) return RN_EINVAL;
+    if (!dtype_ok(dtype)) return RN_EDTYPE;
+    RN_TRY(check_shape(N, H));
+    if (N == 0) {
+        *rows = 0;
+        return RN_OK;
+    }
+    int cus = 0;
+    RN_TRY(current_cus(&cus));
+    const bool vec = vectorizable != 0;
+    const int P = partial_rows(dtype, N, H, vec, cus);
+    if (P < 0) return RN_EUNSUPPORTED;
+    // the same choice as the backward entry points make
+    const bool colsum = bwd_force_colsum(H, vec) ||
+                        bwd_use_colsum(N, (int)H, (int)elem_size(dtype), P,
+                                       is_layernorm != 0, cus);
+    *rows = (colsum || (P == 1 && !is_long_row(H, vec))) ? 0 : P;
+    return RN_OK;
+}
+
 extern "C" int rn_bwd_workspace_bytes(int64_t N, int64_t H, int dtype,
                                       int is_layernorm, int device, size_t *bytes) {
     if (!bytes || device < -1) return RN_EINVAL;

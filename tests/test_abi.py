@@ -197,6 +197,17 @@ def test_workspace_query_without_device(L):
     assert L.rn_bwd_workspace_bytes(10, 1024, BF16, 1, -2, ctypes.byref(out)) == EINVAL
 
 
+def test_partial_rows_query_without_device(L):
+    # (N, H, dtype, is_layernorm, vectorizable, &rows)
+    out = ctypes.c_int(123)
+    assert L.rn_bwd_partial_rows(0, 1024, BF16, 1, 1, ctypes.byref(out)) == OK
+    assert out.value == 0                    # N = 0 touches no device
+    assert L.rn_bwd_partial_rows(10, 1024, 9, 1, 1, ctypes.byref(out)) == EDTYPE
+    assert L.rn_bwd_partial_rows(10, 0, BF16, 1, 1, ctypes.byref(out)) == EINVAL
+    assert L.rn_bwd_partial_rows(10, MAXH + 1, BF16, 1, 1, ctypes.byref(out)) == EUNSUP
+    assert L.rn_bwd_partial_rows(10, 1024, BF16, 1, 1, None) == EINVAL
+
+
 def test_copy_argument_errors(L):
     assert L.rn_copy(X, Y, 0, S) == OK
     assert L.rn_copy(None, Y, 16, S) == EINVAL

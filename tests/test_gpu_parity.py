@@ -793,6 +793,26 @@ def test_tensors_past_4gib(orc):
     tol.check_rstd(host(rs3[rows]), r_o, "edge: past 4 GiB fused rstd")
 
 
+def test_partial_rows_query():
+    """rn_bwd_partial_rows agrees with the workspace the backward asks for:
+    P partial rows per parameter fit in it (P rounded up to 8 slots), none
+    when the workspace is empty; the tall shapes use a bounded P that does
+    not grow with N, the 512 x 16384 LayerNorm the column sums."""
+    bf = torch.bfloat16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for N, H in [(32768, 1024), (16384, 2048), (2048, 16384), (512, 16384),
+                 (1048576, 128), (65536, 1024), (4, 4096), (600, 20480)]:
+        for ln in (True, False):
+            p = rn.bwd_partial_rows(N, H, bf, ln)
+            ws = rn.workspace_bytes(N, H, bf, ln)
+            need = ((p + 7) // 8 * 8) * H * 4 * (2 if ln else 1)
+            assert need <= ws, (N, H, ln, p, ws)
+            assert (p == 0) == (ws == 0) or p == 0, (N, H, ln, p, ws)
+            assert p <= 16 * cus, (N, H, ln, p)
+    assert rn.bwd_partial_rows(32768, 1024, bf, True) == rn.bwd_partial_rows(65536, 1024, bf, True)
+    assert rn.bwd_partial_rows(512, 16384, bf, True) == 0
+
+
 @pytest.mark.parametrize("N", [0, 1, 2, 7, 255, 513])
 def test_row_counts(orc, N):
     """N = 0 (no rows: dgamma = dbeta = 0), N below the partial-row count,
