@@ -14,7 +14,8 @@
   python -m rmsnorm_row_welford_amd.profsum traffic <fetch.db> <write.db>
          <kernel-substring>[|<kernel-substring>...] <out.json> [calib-substring calib-bytes]
       HBM bytes per launch of each listed kernel (and their sum: the op's
-      traffic per call) from a FETCH_SIZE run and a
+      traffic per call; a pattern '=label' matches one kernel label exactly)
+      from a FETCH_SIZE run and a
       WRITE_SIZE run (both KiB per dispatch), each scaled by what the same
       counter reads for the streaming copy kernel of known size
       (rn::copy16_kernel moving `calib-bytes` each way, 64 MiB by default:
@@ -127,8 +128,16 @@ def pmc_table(db: str):
 
 
 def _counter(db, counter, substr):
-    vals = [(n, nd, v) for n, cn, nd, v in _pmc_rows(db)
-            if cn == counter and substr in n]
+    """Average per dispatch over the kernels whose label contains `substr`,
+    or, for a pattern starting with '=', whose label is exactly the rest
+    (LayerNorm's and RMSNorm's kernel 2 share a name and differ only by the
+    grid suffix of the label)."""
+    if substr.startswith("="):
+        vals = [(n, nd, v) for n, cn, nd, v in _pmc_rows(db)
+                if cn == counter and n == substr[1:]]
+    else:
+        vals = [(n, nd, v) for n, cn, nd, v in _pmc_rows(db)
+                if cn == counter and substr in n]
     if not vals:
         raise SystemExit(f"no {counter} rows for kernels matching {substr!r} in {db}")
     tot_d = sum(nd for _, nd, _ in vals)
