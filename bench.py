@@ -38,7 +38,10 @@ bias; the fused forward at 32768x4096), the other storage pairs at
 32768x1024 (binary16 throughout; bf16 with float32 parameters: all six
 ops) and short rows (1048576x128 forward and backward), each with enough
 rotating copies that its data comes from HBM.  --shapes-only NAME[,NAME]
-(or all) times just those and prints their table.
+(or all) times just those and prints their table.  Each shape row also
+carries the library copy's GB/s at that shape's own tensor size
+(copy_same_size_GBps: launch and ramp weigh more on small tensors) and
+each op's share of it (pct_copy_same_size).
 
 decode (not in the step): the latency regime of a few rows (N = 1, 16, 64
 at H = 4096, bf16, data in cache), every op, forward and backward: 50
@@ -447,7 +450,8 @@ def decode_latency(rn, dev, H=4096, Ns=(1, 16, 64), K=50, reps=5):
     return out
 
 
-def stream_ceilings(rn, dev, nbytes=64 << 20, cold_bytes=1 << 30, K=24, reps=5):
+def stream_ceilings(rn, dev, nbytes=64 << 20, cold_bytes=1 << 30, K=24, reps=5,
+                    kinds=("copy", "add")):
     """Plain streams measured like the ops: K launches over rotating buffers
     of `nbytes` (the step's tensor size) captured in a HIP graph, each replay
     timed between events on the launch stream, the median of `reps`.
@@ -469,6 +473,8 @@ def stream_ceilings(rn, dev, nbytes=64 << 20, cold_bytes=1 << 30, K=24, reps=5):
     out = {}
     stream = torch.cuda.current_stream()
     for kind, moved in (("copy", 2 * nbytes), ("add", 3 * nbytes)):
+        if kind not in kinds:
+            continue
         for i in range(M):
             run(kind, i)
         torch.cuda.synchronize()
@@ -493,6 +499,25 @@ def stream_ceilings(rn, dev, nbytes=64 << 20, cold_bytes=1 << 30, K=24, reps=5):
                      "GBps": round(moved / (t * 1e-6) / 1e9, 1)}
     del bufs, bf
     return out
+
+
+def same_size_ceilings(rn, dev, shapes):
+    """For each shape row: the library copy's GB/s at that shape's own
+    tensor size (one read and one write stream of N*H*e bytes, same cold
+    protocol), and each op's share of it.  Small tensors pay the launch and
+    the ramp of the memory system on fewer bytes: this is what a plain
+    one-pass stream of that size reaches, context rather than a bound (a
+    persistent kernel can do better there)."""
+    cache = {}
+    for name, row in (shapes or {}).items():
+        nb = row["N"] * row["H"] * _ESIZE[row["dtype"]]
+        if nb not in cache:
+            cache[nb] = stream_ceilings(rn, dev, nbytes=nb, kinds=("copy",))["copy"]["GBps"]
+            log(f"copy at {nb >> 20} MiB per tensor: {cache[nb]:.0f} GB/s")
+        row["copy_same_size_GBps"] = cache[nb]
+        for v in row.values():
+            if isinstance(v, dict) and "GBps" in v:
+                v["pct_copy_same_size"] = round(100 * v["GBps"] / cache[nb], 1)
 
 
 def cpu_model():
@@ -593,6 +618,9 @@ def main():
                     help="with --shapes-only: comma list of the ops to time")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode-size table and print it")
+    ap.add_argument("--same-size-copy", action="store_true",
+                    help="with --shapes-only: also time the copy at each "
+                         "shape's tensor size (on by default in the full run)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="with --shapes-only: also run one 64 MiB rn_copy (the "
                          "known-size kernel that calibrates byte counters)")
@@ -625,8 +653,10 @@ def main():
             rn.copy(a, b)
             torch.cuda.synchronize()
             del a, b
-        print(json.dumps({"shapes": time_shapes(rn, dev, names, only_ops=only)}),
-              flush=True)
+        shapes = time_shapes(rn, dev, names, only_ops=only)
+        if args.same_size_copy:
+            same_size_ceilings(rn, dev, shapes)
+        print(json.dumps({"shapes": shapes}), flush=True)
         return
     w = synth.WORKLOADS[WORKLOAD]
     N, H = w.N, w.H
@@ -684,6 +714,7 @@ def main():
     for name, row in (shapes or {}).items():
         annotate(rn, dev, row, row["N"], row["H"], row["dtype"], row["param_dtype"],
                  copy_gbs)
+    same_size_ceilings(rn, dev, shapes)
     for k, v in ceil.items():
         log(f"{k} stream ceiling {v['GBps']:.0f} GB/s ({100 * v['GBps'] / PEAK_GBS:.1f}% of peak)")
 

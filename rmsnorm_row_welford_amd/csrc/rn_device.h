@@ -1,7 +1,7 @@
 // Device primitives for the gfx950 row-normalization kernels: vector
 // load/store of row chunks with float32 conversion, bfloat16 and binary16
-// rounding, and wave64 reductions built from DPP row permutations and
-// ds_swizzle.
+// rounding, and wave64 reductions built from DPP row permutations and row
+// broadcasts (ds_swizzle for 32-lane segments).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -278,6 +278,8 @@ enum : int {
     DPP_QUAD_XOR2 = 0x4E,   // quad_perm [2,3,0,1]
     DPP_ROW_HALF_MIRROR = 0x141,
     DPP_ROW_MIRROR = 0x140,
+    DPP_ROW_BCAST15 = 0x142,   // lane 15 of each row feeds the next row
+    DPP_ROW_BCAST31 = 0x143,   // lane 31 feeds rows 2 and 3
 };
 
 template <int CTRL>
@@ -285,6 +287,14 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                            0xF, 0xF, false));
+}
+
+// A DPP read in the rows that ROW_MASK enables; the other rows read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                           ROW_MASK, 0xF, false));
 }
 
 // Lane i reads lane i ^ 16 within each half of the wave (ds_swizzle
@@ -301,17 +311,19 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 
 // Sum over the 64 lanes of a wave; every lane gets the same bits.
 // Each step pairs lanes symmetrically (a+b and b+a round identically), so
-// after the four DPP steps all 16 lanes of a DPP row hold the row's sum,
-// after the swizzle all 32 lanes of a half hold the half's sum, and the two
-// halves are added once from scalar registers.  Must be called with all 64
-// lanes active.
+// after the four DPP steps all 16 lanes of DPP row k hold the row's sum
+// r_k.  Two row broadcasts then finish in the vector unit (no LDS round
+// trip): rows 1 and 3 add the row below (r1 + r0, r3 + r2), row 3 adds row
+// 1, and lane 63 holds (r3 + r2) + (r1 + r0), the same bits as
+// (r0 + r1) + (r2 + r3).  Must be called with all 64 lanes active.
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp<DPP_QUAD_XOR1>(v);
     v += dpp<DPP_QUAD_XOR2>(v);
     v += dpp<DPP_ROW_HALF_MIRROR>(v);
     v += dpp<DPP_ROW_MIRROR>(v);
-    v += swizzle_xor16(v);
-    return lane_value(v, 0) + lane_value(v, 32);
+    v += dpp_rows<DPP_ROW_BCAST15, 0xA>(v);
+    v += dpp_rows<DPP_ROW_BCAST31, 0xC>(v);
+    return lane_value(v, 63);
 }
 
 // Two independent sums, interleaved for latency.
@@ -324,10 +336,12 @@ __device__ __forceinline__ void wave_sum2(float &a, float &b) {
     b += dpp<DPP_ROW_HALF_MIRROR>(b);
     a += dpp<DPP_ROW_MIRROR>(a);
     b += dpp<DPP_ROW_MIRROR>(b);
-    a += swizzle_xor16(a);
-    b += swizzle_xor16(b);
-    a = lane_value(a, 0) + lane_value(a, 32);
-    b = lane_value(b, 0) + lane_value(b, 32);
+    a += dpp_rows<DPP_ROW_BCAST15, 0xA>(a);
+    b += dpp_rows<DPP_ROW_BCAST15, 0xA>(b);
+    a += dpp_rows<DPP_ROW_BCAST31, 0xC>(a);
+    b += dpp_rows<DPP_ROW_BCAST31, 0xC>(b);
+    a = lane_value(a, 63);
+    b = lane_value(b, 63);
 }
 
 // Sum over aligned groups of SEG lanes (8, 16 or 32): the first steps of

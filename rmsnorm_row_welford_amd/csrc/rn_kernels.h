@@ -18,7 +18,7 @@
 //  * LayerNorm works on x - pivot (pivot = the row's first element), so
 //    sums and deviations carry the row's spread rather than its mean.
 //  * TW == 1: two-pass over the register-resident row, each pass a wave64
-//    sum by DPP/ds_swizzle (mean first, then the centered sum of squares).
+//    sum by DPP (mean first, then the centered sum of squares).
 //  * TW > 1 (LayerNorm): each wave takes the two-pass mean and M2 of its own
 //    elements; the waves' (count, mean, M2) states meet in LDS (one barrier)
 //    and are combined with the parallel Welford merge, lane w of each wave
