@@ -1041,27 +1041,29 @@ hipError_t launch_bwd2(const float *part, int P, int H, bool ln, void *dg, void 
 // (see bwd_use_colsum).  They use the saved statistics only, not dx, so the
 // kernels that write dx take these tiles too, after their rows: the tiles
 // then fill the tail of the dx work instead of following it as a second
-// launch.  A workgroup of THREADS threads owns a tile of COLS = 8*VEC
-// columns: 8 lanes across the columns (one chunk each) times THREADS/8 row
-// slots; slot j adds rows j, j + THREADS/8, ... in increasing order, and the
-// slots are then added in a fixed two-level order through LDS.
+// launch.  A workgroup of THREADS threads owns a tile of COLS = CL*VEC
+// columns: CL lanes across the columns (one chunk each; 8 by default)
+// times SL = THREADS/CL row slots; slot j adds rows j, j + SL, ... in
+// increasing order, and the slots are then added in a fixed two-level order
+// through LDS.  Narrow tiles make many tiles; wide ones give each slot more
+// rows when the rows are few.
 //
 // Row iterations of a column tile whose loads are issued together.
 #ifndef RN_COLSUM_UNROLL
 #define RN_COLSUM_UNROLL 2
 #endif
-template <class T, int VEC, int THREADS>
+template <class T, int VEC, int THREADS, int CL_ = 8>
 struct ColsumTile {
-    static constexpr int CL = 8, SL = THREADS / CL, COLS = CL * VEC;
+    static constexpr int CL = CL_, SL = THREADS / CL, COLS = CL * VEC;
     static constexpr int NG = THREADS / COLS;   // second-level groups of slots
     static constexpr int SPG = SL / NG;         // slots per group
     static_assert(NG * COLS == THREADS && SPG * NG == SL, "tile shape");
     static constexpr int LDS_FLOATS = SL * COLS + NG * COLS;
 };
 
-template <class T, class W, int VEC, bool LN, int THREADS>
+template <class T, class W, int VEC, bool LN, int THREADS, int CL_ = 8>
 __device__ void colsum_tile(const BwdArgs &a, int tile, float *red) {
-    using C = ColsumTile<T, VEC, THREADS>;
+    using C = ColsumTile<T, VEC, THREADS, CL_>;
     constexpr int CL = C::CL, SL = C::SL, COLS = C::COLS, NG = C::NG, SPG = C::SPG;
     float *red2 = red + SL * COLS;
     const int lc = threadIdx.x % CL;
@@ -1118,13 +1120,13 @@ __device__ void colsum_tile(const BwdArgs &a, int tile, float *red) {
 }
 
 // Every column tile of the row, taken by the workgroups in turn.
-template <class T, class W, int VEC, bool LN, int THREADS>
+template <class T, class W, int VEC, bool LN, int THREADS, int CL = 8>
 __device__ void colsum_tiles(const BwdArgs &a) {
-    using C = ColsumTile<T, VEC, THREADS>;
+    using C = ColsumTile<T, VEC, THREADS, CL>;
     __shared__ float red[C::LDS_FLOATS];
     const int ntiles = (a.H + C::COLS - 1) / C::COLS;
     for (int t = blockIdx.x; t < ntiles; t += gridDim.x)
-        colsum_tile<T, W, VEC, LN, THREADS>(a, t, red);
+        colsum_tile<T, W, VEC, LN, THREADS, CL>(a, t, red);
 }
 
 // The column tiles as a kernel of their own (RN_COLSUM_FUSED = 0).
@@ -1134,10 +1136,10 @@ __global__ __launch_bounds__(1024) void bwd_colsum_kernel(const BwdArgs a) {
 }
 
 // Workgroups the dx kernel with trailing column tiles needs: its row groups,
-// or one per tile if there are more tiles.
+// or one per tile if there are more tiles (tiles of CL lanes across).
 template <int VEC>
-inline int64_t colsum_grid(int64_t row_groups, int H) {
-    const int64_t ntiles = (H + 8 * VEC - 1) / (8 * VEC);
+inline int64_t colsum_grid(int64_t row_groups, int H, int CL = 8) {
+    const int64_t ntiles = (H + CL * VEC - 1) / (CL * VEC);
     const int64_t g = row_groups > ntiles ? row_groups : ntiles;
     return g < (1 << 20) ? g : (1 << 20);
 }

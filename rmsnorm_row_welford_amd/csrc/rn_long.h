@@ -486,9 +486,10 @@ constexpr int bwd_reg_segs() {
 // Backward without accumulators: dx, one row per workgroup, held on chip as
 // far as it fits (segments [0, R) of x and dy in registers, the next `nlds`
 // in LDS; the rest are read again by the dx pass), then dgamma/dbeta by
-// column tiles (colsum_tiles).  ADD: the fused add+RMSNorm backward (a.add,
-// if set, is added to dx; a.dx2, if set, receives dx too).
-template <class T, class W, int VEC, bool LN, bool ADD>
+// column tiles (colsum_tiles, CL lanes across each tile).  ADD: the fused
+// add+RMSNorm backward (a.add, if set, is added to dx; a.dx2, if set,
+// receives dx too).
+template <class T, class W, int VEC, bool LN, bool ADD, int CL>
 __global__ __launch_bounds__(kLongThreads) void bwd_onchip_kernel(const BwdArgs a, int nlds) {
     static_assert(!(LN && ADD), "the residual variant is RMSNorm's");
     using Raw = RawChunk<T, VEC>;
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(kLongThreads) void bwd_onchip_kernel(const BwdArgs 
                                                 k1, k2, rdx, rdx2, (uint32_t)(el(s0 + u) * ES));
         }
     }
-    colsum_tiles<T, W, VEC, LN, kLongThreads>(a);
+    colsum_tiles<T, W, VEC, LN, kLongThreads, CL>(a);
 }
 
 // Backward with partial rows: a persistent grid whose lanes keep dgamma
@@ -834,6 +835,36 @@ inline int bwd_long_partials(int64_t N, int cus) {
     return (int)(N < cus ? N : cus);
 }
 
+// Rows below which the long-row backward's column tiles are 32 lanes wide
+// instead of 8: with 8 lanes across, each of the 128 row slots of a tile
+// adds only N/128 rows, too little work per workgroup for the loads to
+// stay in flight.  Measured at 256 x 131072 (bf16): LN 83 -> 71 us, RMS
+// 76 -> 68.5 us (64 lanes: 72.7 and 70 us).
+#ifndef RN_LONG_WIDE_TILE_ROWS
+#define RN_LONG_WIDE_TILE_ROWS 1024
+#endif
+
+// dx, the row held on chip as far as registers and LDS go (LDS less the
+// column tiles' static share), then the column tiles
+template <class T, class W, int VEC, bool LN, bool ADD, int CL>
+hipError_t launch_bwd_onchip(const BwdArgs &a, hipStream_t s) {
+    constexpr int R = bwd_reg_segs<T, W, VEC>();
+    constexpr int SPAN = kLongThreads * VEC;
+    const int nseg = (a.H + SPAN - 1) / SPAN;
+    const int pair = 2 * SPAN * (int)sizeof(T);   // LDS bytes of one segment of x and dy
+    constexpr int tile_lds =
+        ColsumTile<T, VEC, kLongThreads, CL>::LDS_FLOATS * (int)sizeof(float);
+    const int budget = long_lds_budget() - tile_lds;
+    const int fit = budget > 0 ? budget / pair : 0;
+    const int nlds = nseg > R ? (nseg - R < fit ? nseg - R : fit) : 0;
+    constexpr auto k = bwd_onchip_kernel<T, W, VEC, LN, ADD, CL>;
+    allow_lds<k>(nlds * pair);
+    const int64_t rows = a.N < (1 << 20) ? a.N : (1 << 20);
+    hipLaunchKernelGGL(k, dim3((unsigned)colsum_grid<VEC>(rows, a.H, CL)),
+                       dim3(kLongThreads), (unsigned)(nlds * pair), s, a, nlds);
+    return hipGetLastError();
+}
+
 template <class T, class W, int VEC, bool LN, bool ADD>
 hipError_t launch_bwd_long_t(const BwdArgs &a, int P, bool colsum, void *dg, void *db,
                              hipStream_t s) {
@@ -848,22 +879,9 @@ hipError_t launch_bwd_long_t(const BwdArgs &a, int P, bool colsum, void *dg, voi
         }
         return launch_bwd2<W>(a.part, P, a.H, LN, dg, db, s);
     }
-    // dx, the row held on chip as far as registers and LDS go (LDS less the
-    // column tiles' static share), then the column tiles
-    constexpr int R = bwd_reg_segs<T, W, VEC>();
-    constexpr int SPAN = kLongThreads * VEC;
-    const int nseg = (a.H + SPAN - 1) / SPAN;
-    const int pair = 2 * SPAN * (int)sizeof(T);   // LDS bytes of one segment of x and dy
-    constexpr int tile_lds = ColsumTile<T, VEC, kLongThreads>::LDS_FLOATS * (int)sizeof(float);
-    const int budget = long_lds_budget() - tile_lds;
-    const int fit = budget > 0 ? budget / pair : 0;
-    const int nlds = nseg > R ? (nseg - R < fit ? nseg - R : fit) : 0;
-    constexpr auto k = bwd_onchip_kernel<T, W, VEC, LN, ADD>;
-    allow_lds<k>(nlds * pair);
-    const int64_t rows = a.N < (1 << 20) ? a.N : (1 << 20);
-    hipLaunchKernelGGL(k, dim3((unsigned)colsum_grid<VEC>(rows, a.H)), dim3(kLongThreads),
-                       (unsigned)(nlds * pair), s, a, nlds);
-    return hipGetLastError();
+    if (a.N < RN_LONG_WIDE_TILE_ROWS)
+        return launch_bwd_onchip<T, W, VEC, LN, ADD, 32>(a, s);
+    return launch_bwd_onchip<T, W, VEC, LN, ADD, 8>(a, s);
 }
 
 template <class T, class W, int VEC>

@@ -1060,13 +1060,20 @@ def test_unsupported_sizes():
 #                          the library takes, on both paths (read twice): 4096
 #                          values per lane in each fp32 sum, column sums over
 #                          2^22 columns
+# Below 1024 rows the column sums past 32768 elements use tiles 32 lanes
+# wide (every case above); from 1024 rows on, 8 lanes wide:
+#   (1024, 33024, bf16)    16-byte path: x and dy in registers, column sums
+#                          over 8-lane tiles of 128 row slots
+#   (1030, 32777, f16)     element-wise path: x and dy in registers and LDS,
+#                          the same tiles
 MAXH = 1 << 22
 LONG = [(600, 20480, "bf16"), (37, 32768, "bf16"), (300, 32768, "bf16/f32"),
         (3, 49152, "bf16"), (5, 98304, "bf16"), (30, 98304, "bf16/f32"),
         (600, 24576, "f32"), (50, 40000, "f32"), (300, 8193, "bf16"),
         (600, 12002, "f16"), (20, 24577, "f16"), (40, 40001, "bf16"),
         (1, 16392, "bf16"), (2, 8201, "f32"),
-        (2, MAXH, "bf16"), (1, MAXH, "f32"), (2, MAXH - 1, "f16/f32")]
+        (2, MAXH, "bf16"), (1, MAXH, "f32"), (2, MAXH - 1, "f16/f32"),
+        (1024, 33024, "bf16"), (1030, 32777, "f16")]
 
 
 @pytest.mark.parametrize("N,H,storage", LONG)
