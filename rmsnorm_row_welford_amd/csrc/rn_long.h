@@ -16,17 +16,16 @@
 // same lane, so no lane reads what another wrote and no barrier is needed).
 // Otherwise the second pass reads it again from global memory.
 //
-// Forward statistics of a row held on chip: the exact two-pass over the
-// held values (LayerNorm: the mean of the values shifted by the row's first
-// element, as in the register plans, then the sum of squared deviations
-// from it; RMSNorm and the fused op: the sum of squares).  Of a row read
-// twice, in one read pass: each lane forms the exact mean and M2 of each of
-// its chunks and merges them into a running (count, mean, M2) with the
-// parallel merge ("Write Cuda Layernorm Kernel", Required reasoning
-// process, the Welford merge formula), and the 1024 lanes' states are
+// Forward statistics, in the read pass of the row (held on chip or read
+// twice): RMSNorm and the fused op sum the squares; LayerNorm shifts the
+// values by the row's first element, and each lane forms the exact mean and
+// M2 of each of its chunks and merges them into a running (count, mean, M2)
+// with the parallel merge ("Write Cuda Layernorm Kernel", Required
+// reasoning process, the Welford merge formula); the 1024 lanes' states are
 // combined by the multi-way form of the same merge:
 // mean = sum(n_l m_l)/H, M2 = sum(M2_l + n_l (m_l - mean)^2).  The
-// denominator is always H.
+// denominator is always H.  A row held on chip is therefore not walked a
+// second time for its M2: the statistics overlap the row's loads.
 //
 // Backward: the first pass forms x_hat, g = dy*gamma and the row sums of g
 // and g*x_hat, the second pass forms dx.  With partial rows (rows of up to
@@ -171,13 +170,35 @@ void fwd_onchip_kernel(const FwdArgs a, int nlds) {
             p0.template bload<0>(rx, 0);
             pivot = p0.get(0);
         }
-        // LayerNorm: sum of x - pivot; the others: sum of squares
+        // LayerNorm: the lane's running (count, mean, M2) about the pivot,
+        // each chunk's exact two-pass mean and M2 merged in as it arrives
+        // (the parallel merge); the others: the sum of squares
         float s1 = 0.0f;
+        float ln_n = 0.0f, ln_m = 0.0f, ln_q = 0.0f;
         auto add1 = [&](const float *v) {
+            if constexpr (OP == OP_LN) {
+                float uu[VEC], sm = 0.0f;
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                if constexpr (OP == OP_LN) s1 += v[k] - pivot;
-                else s1 = __builtin_fmaf(v[k], v[k], s1);
+                for (int k = 0; k < VEC; ++k) {
+                    uu[k] = v[k] - pivot;
+                    sm += uu[k];
+                }
+                const float mc = sm * (1.0f / (float)VEC);
+                float m2c = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float d = uu[k] - mc;
+                    m2c = __builtin_fmaf(d, d, m2c);
+                }
+                const float n1 = ln_n + (float)VEC;
+                const float f = (float)VEC / n1;
+                const float dl = mc - ln_m;
+                ln_m = __builtin_fmaf(dl, f, ln_m);
+                ln_q += m2c + dl * dl * (ln_n * f);
+                ln_n = n1;
+            } else {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) s1 = __builtin_fmaf(v[k], v[k], s1);
             }
         };
         auto widen = [&](const Raw &c0, const Raw &c1, float *v) {
@@ -240,31 +261,10 @@ void fwd_onchip_kernel(const FwdArgs a, int nlds) {
         repack();
         float ms = 0.0f, var;
         if constexpr (OP == OP_LN) {
-            // exact two-pass: the mean about the pivot, then the squared
-            // deviations from it over the held row
-            ms = block_sum16(s1, red, parity) * a.inv_H;
-            float q = 0.0f;
-            auto add2 = [&](const Raw &c) {
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float d = (c.get(k) - pivot) - ms;
-                    q = __builtin_fmaf(d, d, q);
-                }
-            };
-#pragma unroll
-            for (int u = 0; u < R; ++u)
-                if (el(u) < H) add2(reg[0][u]);
-            if constexpr (LSEG) {
-                for (int sg = R; sg < nseg; ++sg) {
-                    if (el(sg) < H) {
-                        Raw c;
-                        lds_get<T, VEC>(lds + lslot(sg), c);
-                        add2(c);
-                    }
-                }
-            }
-            repack();
-            var = block_sum16(q, red, parity) * a.inv_H;
+            // multi-way merge of the lanes' states (about the pivot)
+            ms = block_sum16(ln_n * ln_m, red, parity) * a.inv_H;
+            const float dm = ln_m - ms;
+            var = block_sum16(__builtin_fmaf(ln_n * dm, dm, ln_q), red, parity) * a.inv_H;
         } else {
             var = block_sum16(s1, red, parity) * a.inv_H;
         }
