@@ -944,21 +944,33 @@ __global__ __launch_bounds__(256) void bwd2_cols_kernel(const float *part, int P
     const int col0 = (blockIdx.x * 4 + wave_id_uniform()) * CPW;
     const float *base = part + (int64_t)blockIdx.y * Pp * H;
     T *dst = blockIdx.y == 0 ? dgamma : dbeta;
-    // all CPW columns' loads are issued before any is summed
+    // the loads of CPW columns and of U steps along them are issued before
+    // any is summed (one step at a time would wait a memory round trip per
+    // step); the sums still take each column's slots in increasing order
+    constexpr int U = 8;
     float s[CPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) s[i] = 0.0f;
-    for (int q = lane * 4; q < Pp; q += 256) {
-        f32x4 v[CPW];
+    for (int q0 = lane * 4; q0 < Pp; q0 += 256 * U) {
+        f32x4 v[U][CPW];
 #pragma unroll
-        for (int i = 0; i < CPW; ++i)
-            v[i] = col0 + i < H ? *(const f32x4 *)(base + (int64_t)(col0 + i) * Pp + q)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < CPW; ++i)
+            for (int i = 0; i < CPW; ++i) {
+                const int q = q0 + 256 * u;
+                v[u][i] = (q < Pp && col0 + i < H)
+                              ? *(const f32x4 *)(base + (int64_t)(col0 + i) * Pp + q)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (slot_used(q + k, P)) s[i] += v[i][k];
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + 256 * u;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (q < Pp && slot_used(q + k, P)) s[i] += v[u][i][k];
+        }
     }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
