@@ -233,7 +233,18 @@ void fwd_onchip_kernel(const FwdArgs a, int nlds) {
                     }
                 }
             };
-            if (R < nseg) request(ca, R);
+            // Segments past R always exist here.  The register segments are
+            // summed while the first LDS group is in flight rather than after
+            // the last one is parked, so their arithmetic overlaps the loads.
+            request(ca, R);
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                if (el(u) < H) {
+                    float v[VEC];
+                    widen(reg[0][u], reg[NIN - 1][u], v);
+                    add1(v);
+                }
+            }
             for (int s0 = R; s0 < nseg; s0 += 2 * U) {
                 if (s0 + U < nseg) request(cb, s0 + U);
                 park(ca, s0);
@@ -241,13 +252,14 @@ void fwd_onchip_kernel(const FwdArgs a, int nlds) {
                 if (s0 + 2 * U < nseg) request(ca, s0 + 2 * U);
                 park(cb, s0 + U);
             }
-        }
+        } else {
 #pragma unroll
-        for (int u = 0; u < R; ++u) {
-            if (el(u) < H) {
-                float v[VEC];
-                widen(reg[0][u], reg[NIN - 1][u], v);
-                add1(v);
+            for (int u = 0; u < R; ++u) {
+                if (el(u) < H) {
+                    float v[VEC];
+                    widen(reg[0][u], reg[NIN - 1][u], v);
+                    add1(v);
+                }
             }
         }
         // keep the held chunks packed across the reductions (widened again
